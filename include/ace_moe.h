@@ -1,0 +1,169 @@
+/*
+ * ace_moe.h -- C ABI of the MI355X (gfx950) library for one routed SwiGLU
+ * Mixture-of-Experts layer forward with ACE per-token expert-slot skipping.
+ *
+ * Method source: "ACE: Adaptive Calibration-Free Expert Skipping for
+ * MoE-based LLMs" (picx.dev summary page).  The layer input is x = x̄Γ
+ * (Theoretical Foundation), each expert is the SwiGLU map f of that section,
+ * each routed slot i of token t has gate g_{t,i}, and ACE skips a slot when
+ * both g·A^GSP(e) and g·A^RCR(e) fall below their thresholds (Methodology,
+ * sections 1-3), never skipping the top-1 slot.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers, row-major, owned by the caller.
+ *     The library never allocates, frees or synchronises; every call only
+ *     enqueues kernels on `stream` (a hipStream_t, NULL = default stream).
+ *   - Activations (x, h, act, y) and expert weights use desc->dtype
+ *     (ACE_F32: float, ACE_BF16: bf16 bit patterns, 2 bytes).  Router
+ *     weights, logits, gates, tables and slot outputs are float32.
+ *   - Expert weights follow the nn.Linear layout (out x in, K contiguous):
+ *     w_gate, w_up: [E, I, H]; w_down: [E, H, I].  The page's H x I matrix
+ *     W^gate is w_gate[e] transposed.
+ *   - Arguments are checked before anything is enqueued.  On error nothing
+ *     is launched, the status is returned and moe_last_error() (a
+ *     thread-local string, valid until the next call on that thread) names
+ *     the offending argument.  ACE_EHIP means a launch failed; the HIP error
+ *     text is in moe_last_error().  No C++ exception crosses this ABI.
+ *   - T = 0 is a valid empty batch: the call returns ACE_OK and launches
+ *     nothing.
+ *   - Limits: 1 <= k <= min(E, 16); 1 <= E <= 256; H and I multiples of 128;
+ *     T * k < 2^31.  Outside them: ACE_EUNSUPPORTED.
+ *   - Calls on one stream run in order; calls that share output or workspace
+ *     buffers must not run concurrently on different streams.
+ */
+#ifndef ACE_MOE_H
+#define ACE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ACE_MOE_ABI_VERSION 1
+
+typedef enum {
+  ACE_OK = 0,
+  ACE_EINVAL = 1,       /* null required pointer, negative size, bad enum */
+  ACE_EUNSUPPORTED = 2, /* valid request outside the limits above */
+  ACE_EWORKSPACE = 3,   /* workspace smaller than moe_workspace_bytes() */
+  ACE_EHIP = 4          /* a HIP launch or runtime call failed */
+} ace_status;
+
+typedef enum { ACE_F32 = 0, ACE_BF16 = 1 } ace_dtype;
+
+/* Expert-GEMM schedule.  GROUPED tiles 64 slot rows per weight tile (prefill);
+ * STREAM tiles 16 rows and splits weights finer, for small batches whose cost
+ * is reading the retained experts' weights (decode).  AUTO picks by T*k. */
+typedef enum { ACE_PATH_AUTO = 0, ACE_PATH_GROUPED = 1, ACE_PATH_STREAM = 2 } ace_path;
+
+/* How the two views are fused into the skip decision (Methodology section 3;
+ * the alternatives are the page's ablations, Tables 4 and 5).  With
+ * sG = g*A^GSP(e), sR = g*A^RCR(e) (float32 products), a non-top-1 slot is
+ * skipped when:
+ *   MAX   : sG < tau_gsp && sR < tau_rcr   (ACE: intersection of skip sets)
+ *   MIN   : sG < tau_gsp || sR < tau_rcr   (union)
+ *   MEAN  : (sG/tau_gsp + sR/tau_rcr)/2 < 1, in float64 (never if a tau is 0)
+ *   GSP   : sG < tau_gsp                   (single view)
+ *   RCR   : sR < tau_rcr                   (single view)
+ *   SCORE : g < tau_gsp                    (bare router gate)            */
+typedef enum {
+  ACE_FUSE_MAX = 0, ACE_FUSE_MIN = 1, ACE_FUSE_MEAN = 2,
+  ACE_FUSE_GSP = 3, ACE_FUSE_RCR = 4, ACE_FUSE_SCORE = 5
+} ace_fusion;
+
+typedef struct {
+  int32_t T;         /* tokens in the batch (rows of x) */
+  int32_t H;         /* hidden size */
+  int32_t E;         /* routed experts */
+  int32_t I;         /* expert intermediate size */
+  int32_t k;         /* routed slots per token (top-k) */
+  int32_t dtype;     /* ace_dtype */
+  int32_t norm_topk; /* 1: gates renormalised over the k selected experts */
+  int32_t fusion;    /* ace_fusion */
+  float rms_eps;     /* RMSNorm epsilon, added to the mean square */
+} ace_moe_desc;
+
+int moe_abi_version(void);
+const char* moe_last_error(void);
+
+/* Bytes of scratch that moe_dispatch needs (per-chunk counts, token masks).
+ * The same workspace may then be passed to moe_expert_forward, which needs
+ * none today.  Returns 0 for an invalid descriptor. */
+size_t moe_workspace_bytes(const ace_moe_desc* d);
+
+/*
+ * moe_route_skip -- RMSNorm, router, top-k gates and the ACE skip mask.
+ *   h[t]      = x[t] / sqrt(mean_j x[t,j]^2 + rms_eps) * gamma   (x = x̄Γ, Theoretical
+ *               Foundation), stored in dtype.
+ *   logits[t] = h[t] . w_router^T (+ router_bias), float32 accumulation.
+ *   topk_idx  = the k largest logits, descending, equal logits to the lower
+ *               expert index; slot 0 is the top-1 expert.
+ *   topk_gate = softmax of the logits in float64 (over all E, or over the k
+ *               selected when norm_topk), rounded to float32.
+ *   keep      = the fusion rule above with (tau_gsp, tau_rcr); keep[t,0] = 1.
+ * In:  x [T,H] dtype; gamma [H] f32; w_router [E,H] f32; router_bias [E] f32
+ *      or NULL; logits_in [T,E] f32 or NULL (when given, used instead of the
+ *      router product, which is then not computed); a_gsp, a_rcr [E] f32, > 0;
+ *      tau_gsp, tau_rcr >= 0.
+ * Out: h_out [T,H] dtype; logits_out [T,E] f32 or NULL; topk_idx [T,k] i32;
+ *      topk_gate [T,k] f32; keep [T,k] u8 (0/1).
+ * Logits must be finite; results for NaN logits are unspecified.
+ */
+ace_status moe_route_skip(const ace_moe_desc* d, const void* x, const float* gamma, const float* w_router,
+                          const float* router_bias, const float* logits_in, float* logits_out, const float* a_gsp,
+                          const float* a_rcr, float tau_gsp, float tau_rcr, void* h_out, int32_t* topk_idx,
+                          float* topk_gate, uint8_t* keep, void* stream);
+
+/*
+ * moe_dispatch -- group the kept slots by expert ("expert dispatch" on the
+ * article page about ACE).  Deterministic: within an expert, slots follow
+ * token order; no floating-point atomics are used.
+ * Out: expert_offsets [E+1] i32 (segment starts; [E] = n_kept);
+ *      sorted_token [T*k] i32 and sorted_gate [T*k] f32, first n_kept
+ *      entries valid; slot_pos [T*k] i32: the sorted row of slot (t,i), or
+ *      -1 when the slot is skipped.
+ * workspace: >= moe_workspace_bytes(d) bytes of device memory.
+ */
+ace_status moe_dispatch(const ace_moe_desc* d, const int32_t* topk_idx, const float* topk_gate, const uint8_t* keep,
+                        int32_t* expert_offsets, int32_t* sorted_token, float* sorted_gate, int32_t* slot_pos,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_expert_forward -- the SwiGLU experts over the dispatched slots (expert
+ * equation f, Theoretical Foundation), gate-weighted.  For sorted row p of
+ * expert e with token t = sorted_token[p]:
+ *   act[p]      = SiLU(h[t] . w_gate[e]^T) * (h[t] . w_up[e]^T)   (dtype)
+ *   slot_out[p] = sorted_gate[p] * (act[p] . w_down[e]^T)          (float32)
+ * Only rows p < expert_offsets[E] are written; only experts with at least
+ * one kept slot have their weights read.
+ * In:  h [T,H] dtype (from moe_route_skip); weights as above.
+ * Out: act [T*k, I] dtype (scratch rows); slot_out [T*k, H] f32.
+ */
+ace_status moe_expert_forward(const ace_moe_desc* d, int32_t path, const void* h, const void* w_gate,
+                              const void* w_up, const void* w_down, const int32_t* expert_offsets,
+                              const int32_t* sorted_token, const float* sorted_gate, void* act, float* slot_out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_combine -- y[t] = residual[t] + sum over kept slots i = 0..k-1 (in that
+ * order) of slot_out[slot_pos[t,i]], accumulated in float32, stored in dtype.
+ * Skipped slots contribute nothing and the kept gates are not renormalised.
+ * In:  slot_pos [T*k] i32; slot_out [T*k, H] f32; residual [T,H] dtype or NULL.
+ * Out: y [T,H] dtype.
+ */
+ace_status moe_combine(const ace_moe_desc* d, const int32_t* slot_pos, const float* slot_out, const void* residual,
+                       void* y, void* stream);
+
+/*
+ * moe_set_kernel_events -- for profiling callers: the next moe_expert_forward
+ * on this thread records `start` (a hipEvent_t) on its stream just before the
+ * gate/up kernel and `stop` just after it, then forgets both.  NULL clears.
+ */
+ace_status moe_set_kernel_events(void* start, void* stop);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ACE_MOE_H */

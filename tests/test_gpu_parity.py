@@ -1,0 +1,243 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer results (top-k indices, skip masks, dispatch order) must match bit for
+bit when both sides read the same float32 logits; gates too (both take them
+in float64 and round once).  Outputs must reach relative L2 <= 1e-5 (f32) and
+<= 1e-2 (bf16) against the float64 oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import token_adaptive_expert_amd as ace
+from gpu_util import (GpuLayer, check_dispatch, check_routing_shared_logits, oracle_thresholds, rel_l2, values)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+PATHS = [ace.ACE_PATH_GROUPED, ace.ACE_PATH_STREAM]
+
+
+def oracle_y(L, g, tau_g, tau_r, tokens=None, fusion="max", norm_topk=None):
+    S = L["shape"]
+    return oracle.moe_layer(L["x"], L["gamma"], L["w_router"], L["router_bias"], L["w_gate"], L["w_up"], L["w_down"],
+                            L["a_gsp"], L["a_rcr"], tau_g, tau_r, S.k,
+                            S.norm_topk if norm_topk is None else norm_topk, S.rms_eps, S.dtype,
+                            logits=g["logits"], tokens=tokens, fusion=fusion)
+
+
+def check_h_and_logits(L, g, logit_atol):
+    S = L["shape"]
+    h_ref = oracle.rmsnorm(L["x"], L["gamma"], S.rms_eps, S.dtype)
+    h_gpu = values(g["h"])
+    if S.dtype == "f32":
+        assert np.max(np.abs(h_gpu - h_ref)) <= 1e-6 * max(1.0, np.max(np.abs(h_ref)))
+    else:
+        # at most one bf16 step apart, and rarely
+        diff = np.abs(h_gpu - h_ref)
+        assert np.all(diff <= np.abs(h_ref) * 2.0 ** -7 + 1e-30)
+        assert np.mean(diff > 0) < 1e-3
+    lg_ref = oracle.router_logits(h_ref, L["w_router"], L["router_bias"]).astype(np.float64)
+    assert np.max(np.abs(g["logits"].astype(np.float64) - lg_ref)) <= logit_atol
+
+
+def check_slot_outputs(L, g, ref, tol):
+    """Per-slot gate-scaled expert outputs (down GEMM rows) against the oracle."""
+    S = L["shape"]
+    rows, refs = [], []
+    for (t, i), o in ref["slot_out"].items():
+        p = g["slot_pos"][t, i]
+        rows.append(g["slot_out"][p])
+        refs.append(o)
+    if rows:
+        assert rel_l2(np.stack(rows), np.stack(refs)) <= tol
+
+
+# ---------------------------------------------------------------- tiny fp32 layer
+@pytest.fixture(scope="module")
+def tiny():
+    S = workloads.CONFIGS["tiny"]
+    L = workloads.make_layer(S)
+    tg, tr = oracle_thresholds(L, 0.5)
+    return L, tg, tr
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_tiny_fp32_layer(tiny, dev, path):
+    L, tg, tr = tiny
+    S = L["shape"]
+    g = GpuLayer(L, dev).run(tg, tr, path)
+    check_h_and_logits(L, g, logit_atol=1e-5)
+    idx, gate, keep = check_routing_shared_logits(L, g, tg, tr)
+    check_dispatch(S, g)
+    n = math.floor(0.5 * S.T * S.k + 0.5)
+    assert abs(int((~keep).sum()) - n) <= 2
+    ref = oracle_y(L, g, tg, tr)
+    assert rel_l2(values(g["y"]), ref["y"]) <= TOL["f32"]
+    check_slot_outputs(L, g, ref, TOL["f32"])
+
+
+def test_oracle_logits_fed_to_gpu(tiny, dev):
+    """Reverse direction: the oracle's logits through logits_in."""
+    L, tg, tr = tiny
+    S = L["shape"]
+    h = oracle.rmsnorm(L["x"], L["gamma"], S.rms_eps, S.dtype)
+    lg = oracle.router_logits(h, L["w_router"], None)
+    g = GpuLayer(L, dev).run(tg, tr, logits_in=lg)
+    assert np.array_equal(g["logits"], lg)
+    idx = np.stack([oracle.topk_experts(lg[t], S.k) for t in range(S.T)])
+    gate = np.stack([oracle.topk_gates(lg[t], idx[t], True) for t in range(S.T)])
+    keep = oracle.skip_mask(idx, gate, L["a_gsp"], L["a_rcr"], tg, tr)
+    assert np.array_equal(g["topk_idx"], idx)
+    assert np.array_equal(g["topk_gate"], gate)
+    assert np.array_equal(g["keep"], keep)
+
+
+@pytest.mark.parametrize("fusion", ["max", "min", "mean", "gsp", "rcr", "score"])
+def test_fusion_rules(tiny, dev, fusion):
+    L, tg, tr = tiny
+    tau_g = 0.12 if fusion == "score" else tg
+    g = GpuLayer(L, dev, fusion=fusion).run(tau_g, tr)
+    check_routing_shared_logits(L, g, tau_g, tr, fusion=fusion)
+    check_dispatch(L["shape"], g)
+    ref = oracle_y(L, g, tau_g, tr, fusion=fusion)
+    assert rel_l2(values(g["y"]), ref["y"]) <= TOL["f32"]
+
+
+def test_threshold_extremes(tiny, dev):
+    L, _, _ = tiny
+    S = L["shape"]
+    gl = GpuLayer(L, dev)
+    g0 = gl.run(0.0, 0.0)
+    assert g0["keep"].all() and g0["offsets"][-1] == S.T * S.k     # plain top-k MoE
+    ref = oracle_y(L, g0, 0.0, 0.0)
+    assert rel_l2(values(g0["y"]), ref["y"]) <= TOL["f32"]
+    gi = gl.run(float("inf"), float("inf"))
+    assert gi["keep"][:, 0].all() and not gi["keep"][:, 1:].any()   # only the top-1 survives
+    ref = oracle_y(L, gi, np.inf, np.inf)
+    assert rel_l2(values(gi["y"]), ref["y"]) <= TOL["f32"]
+    # AND, not OR: one view alone never skips
+    ga = gl.run(float("inf"), 0.0)
+    assert ga["keep"].all()
+
+
+def test_gates_without_topk_renormalisation(tiny, dev):
+    L, tg, tr = tiny
+    g = GpuLayer(L, dev, norm_topk=0).run(tg, tr)
+    check_routing_shared_logits(L, g, tg, tr, norm_topk=0)
+    ref = oracle_y(L, g, tg, tr, norm_topk=0)
+    assert rel_l2(values(g["y"]), ref["y"]) <= TOL["f32"]
+
+
+def test_deterministic_and_residual(tiny, dev):
+    L, tg, tr = tiny
+    gl = GpuLayer(L, dev)
+    a = gl.run(tg, tr)
+    b = gl.run(tg, tr)
+    for n in ("y", "slot_out", "sorted_token", "slot_pos"):
+        m = a["offsets"][-1] if n in ("slot_out", "sorted_token") else None
+        assert np.array_equal(a[n][:m].view(np.uint8), b[n][:m].view(np.uint8)), n
+    c = gl.run(tg, tr, residual=gl.P["x"])
+    expect = values(a["y"]) + values(L["x"])
+    assert rel_l2(values(c["y"]), expect) <= 1e-6
+
+
+# ---------------------------------------------------------------- bf16, ragged and edge shapes
+def _bf16_case(T, H, E, I, k, rate, cfg_id, bias=None):
+    S = workloads.small_shape(T=T, H=H, E=E, I=I, k=k, dtype="bf16", cfg_id=cfg_id)
+    L = workloads.make_layer(S)
+    if bias is not None:
+        L["router_bias"] = bias
+    tg, tr = oracle_thresholds(L, rate)
+    return L, tg, tr
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("case", [
+    dict(T=100, H=256, E=24, I=256, k=5, rate=0.5, cfg_id=101),
+    dict(T=1, H=128, E=16, I=128, k=4, rate=0.0, cfg_id=102),
+    dict(T=33, H=128, E=256, I=128, k=16, rate=0.6, cfg_id=103),
+    dict(T=70, H=384, E=8, I=384, k=1, rate=0.0, cfg_id=104),
+    dict(T=130, H=512, E=40, I=640, k=8, rate=0.7, cfg_id=105),
+])
+def test_bf16_shapes(dev, path, case):
+    L, tg, tr = _bf16_case(**case)
+    S = L["shape"]
+    g = GpuLayer(L, dev).run(tg, tr, path)
+    check_h_and_logits(L, g, logit_atol=2e-3)
+    check_routing_shared_logits(L, g, tg, tr)
+    check_dispatch(S, g)
+    ref = oracle_y(L, g, tg, tr)
+    assert rel_l2(values(g["y"]), ref["y"]) <= TOL["bf16"]
+    check_slot_outputs(L, g, ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_one_expert_takes_every_token(dev, path):
+    """A strong router bias sends all 300 tokens to expert 3: its slot rows span
+    several m-tiles of both tilings."""
+    E = 16
+    bias = np.zeros(E, np.float32)
+    bias[3] = 20.0
+    L, tg, tr = _bf16_case(T=300, H=256, E=E, I=256, k=4, rate=0.4, cfg_id=106, bias=bias)
+    S = L["shape"]
+    g = GpuLayer(L, dev).run(tg, tr, path)
+    check_routing_shared_logits(L, g, tg, tr)
+    off, _, _, _ = check_dispatch(S, g)
+    assert off[4] - off[3] == S.T
+    ref = oracle_y(L, g, tg, tr)
+    assert rel_l2(values(g["y"]), ref["y"]) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------- full Qwen3-30B-A3B-shaped layer
+@pytest.fixture(scope="module")
+def qwen():
+    S = workloads.CONFIGS["qwen3_30b_a3b"]
+    L = workloads.make_layer(S)
+    tg, tr = oracle_thresholds(L, 0.6)
+    return L, tg, tr
+
+
+SAMPLE = [0, 1, 2, 63, 64, 65, 127, 128, 500, 777, 1022, 1023]
+
+
+def test_qwen3_prefill_full_size(qwen, dev):
+    L, tg, tr = qwen
+    S = L["shape"]
+    gl = GpuLayer(L, dev)
+    g = gl.run(tg, tr)   # AUTO: the grouped tiling at T*k = 8192
+    check_h_and_logits(L, g, logit_atol=2e-3)
+    check_routing_shared_logits(L, g, tg, tr)
+    check_dispatch(S, g)
+    skipped = int((~g["keep"]).sum())
+    assert abs(skipped / (S.T * S.k) - 0.6) < 0.01
+    ref = oracle_y(L, g, tg, tr, tokens=SAMPLE)
+    assert rel_l2(values(g["y"][SAMPLE]), ref["y"][SAMPLE]) <= TOL["bf16"]
+    # the other tiling gives the same layer output
+    g2 = gl.run(tg, tr, path=ace.ACE_PATH_STREAM)
+    assert rel_l2(values(g2["y"]), values(g["y"])) <= 1e-2
+
+
+@pytest.mark.parametrize("M", workloads.DECODE_M)
+def test_qwen3_decode_steps(qwen, dev, M):
+    """Decode batches of M fresh tokens, thresholds transferred from the
+    T=1024 calibration batch."""
+    L, tg, tr = qwen
+    S = workloads.CONFIGS["qwen3_30b_a3b_decode"].with_tokens(M)
+    x = workloads.make_tokens(S, seed=0, step=1)
+    Ld = dict(L)
+    Ld["x"] = x
+    Ld["shape"] = S
+    gl = GpuLayer(Ld, dev)
+    g = gl.run(tg, tr)
+    check_routing_shared_logits(Ld, g, tg, tr)
+    check_dispatch(S, g)
+    ref = oracle_y(Ld, g, tg, tr)
+    assert rel_l2(values(g["y"]), ref["y"]) <= TOL["bf16"]
+    for path in PATHS:
+        gp = gl.run(tg, tr, path=path)
+        assert rel_l2(values(gp["y"]), ref["y"]) <= TOL["bf16"]

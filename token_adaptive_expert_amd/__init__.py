@@ -1,0 +1,13 @@
+"""MI355X (gfx950) forward of a routed SwiGLU MoE layer with ACE per-token
+expert-slot skipping.  The arithmetic lives in the HIP library built from
+``csrc/``; this package holds its ctypes binding and a buffer-owning layer
+wrapper (torch supplies device memory and streams)."""
+from ._lib import (ACE_BF16, ACE_F32, ACE_PATH_AUTO, ACE_PATH_GROUPED, ACE_PATH_STREAM, AceMoeError, MoeDesc,
+                   load, make_desc, moe_abi_version, moe_combine, moe_dispatch, moe_expert_forward,
+                   moe_last_error, moe_route_skip, moe_set_kernel_events, moe_workspace_bytes)
+from .layer import AceMoeLayer, LayerBuffers
+
+__all__ = ["ACE_BF16", "ACE_F32", "ACE_PATH_AUTO", "ACE_PATH_GROUPED", "ACE_PATH_STREAM", "AceMoeError", "MoeDesc",
+           "load", "make_desc", "moe_abi_version", "moe_combine", "moe_dispatch", "moe_expert_forward",
+           "moe_last_error", "moe_route_skip", "moe_set_kernel_events", "moe_workspace_bytes", "AceMoeLayer",
+           "LayerBuffers"]

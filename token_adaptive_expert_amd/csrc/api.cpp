@@ -1,0 +1,281 @@
+// C ABI of the ACE MoE layer library: argument checks, path choice and
+// kernel launches.  Declarations and contracts: include/ace_moe.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/ace_moe.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+thread_local hipEvent_t g_ev_start = nullptr;
+thread_local hipEvent_t g_ev_stop = nullptr;
+
+ace_status fail(ace_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+ace_status ok() {
+  g_err.clear();
+  return ACE_OK;
+}
+
+ace_status hip_fail(const char* what, hipError_t e) {
+  return fail(ACE_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), int(e));
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_num_cu[kMaxDevices];
+
+// Compute units of the current device (cached per device).
+ace_status num_cu(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  if (dev < 0 || dev >= kMaxDevices) return fail(ACE_EUNSUPPORTED, "device index %d out of range", dev);
+  int n = g_num_cu[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail("hipDeviceGetAttribute", e);
+    g_num_cu[dev].store(n, std::memory_order_relaxed);
+  }
+  *out = n;
+  return ACE_OK;
+}
+
+ace_status check_desc(const ace_moe_desc* d) {
+  if (d == nullptr) return fail(ACE_EINVAL, "desc is NULL");
+  if (d->T < 0) return fail(ACE_EINVAL, "T=%d is negative", d->T);
+  if (d->H <= 0 || d->E <= 0 || d->I <= 0 || d->k <= 0)
+    return fail(ACE_EINVAL, "H=%d E=%d I=%d k=%d must be positive", d->H, d->E, d->I, d->k);
+  if (d->dtype != ACE_F32 && d->dtype != ACE_BF16) return fail(ACE_EINVAL, "dtype=%d is not an ace_dtype", d->dtype);
+  if (d->fusion < ACE_FUSE_MAX || d->fusion > ACE_FUSE_SCORE)
+    return fail(ACE_EINVAL, "fusion=%d is not an ace_fusion", d->fusion);
+  if (d->norm_topk != 0 && d->norm_topk != 1) return fail(ACE_EINVAL, "norm_topk=%d must be 0 or 1", d->norm_topk);
+  if (!(d->rms_eps >= 0.f)) return fail(ACE_EINVAL, "rms_eps must be >= 0");
+  if (d->E > 256) return fail(ACE_EUNSUPPORTED, "E=%d > 256", d->E);
+  if (d->k > 16 || d->k > d->E) return fail(ACE_EUNSUPPORTED, "k=%d must be <= min(E, 16)", d->k);
+  if (d->H % 128 != 0) return fail(ACE_EUNSUPPORTED, "H=%d is not a multiple of 128", d->H);
+  if (d->I % 128 != 0) return fail(ACE_EUNSUPPORTED, "I=%d is not a multiple of 128", d->I);
+  if (int64_t(d->T) * d->k >= (int64_t(1) << 31)) return fail(ACE_EUNSUPPORTED, "T*k >= 2^31");
+  if (int64_t(d->T) * d->H >= (int64_t(1) << 40)) return fail(ACE_EUNSUPPORTED, "T*H too large");
+  return ACE_OK;
+}
+
+#define REQUIRE(p) \
+  if ((p) == nullptr) return fail(ACE_EINVAL, "%s is NULL", #p)
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return ACE_MOE_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+size_t moe_workspace_bytes(const ace_moe_desc* d) {
+  if (check_desc(d) != ACE_OK) return 0;
+  return ace::dispatch_workspace_bytes(std::max(d->T, 1), d->E);
+}
+
+ace_status moe_route_skip(const ace_moe_desc* d, const void* x, const float* gamma, const float* w_router,
+                          const float* router_bias, const float* logits_in, float* logits_out, const float* a_gsp,
+                          const float* a_rcr, float tau_gsp, float tau_rcr, void* h_out, int32_t* topk_idx,
+                          float* topk_gate, uint8_t* keep, void* stream) {
+  try {
+    ace_status st = check_desc(d);
+    if (st != ACE_OK) return st;
+    REQUIRE(x);
+    REQUIRE(gamma);
+    if (logits_in == nullptr) REQUIRE(w_router);
+    REQUIRE(a_gsp);
+    REQUIRE(a_rcr);
+    REQUIRE(h_out);
+    REQUIRE(topk_idx);
+    REQUIRE(topk_gate);
+    REQUIRE(keep);
+    if (!(tau_gsp >= 0.f) || !(tau_rcr >= 0.f)) return fail(ACE_EINVAL, "thresholds must be >= 0 (got %g, %g)",
+                                                            double(tau_gsp), double(tau_rcr));
+    if (d->T == 0) return ok();
+    ace::RouteArgs a;
+    a.x = x;
+    a.gamma = gamma;
+    a.w_router = w_router;
+    a.bias = router_bias;
+    a.logits_in = logits_in;
+    a.logits_out = logits_out;
+    a.a_gsp = a_gsp;
+    a.a_rcr = a_rcr;
+    a.tau_gsp = tau_gsp;
+    a.tau_rcr = tau_rcr;
+    a.h_out = h_out;
+    a.topk_idx = topk_idx;
+    a.topk_gate = topk_gate;
+    a.keep = keep;
+    a.T = d->T;
+    a.H = d->H;
+    a.E = d->E;
+    a.k = d->k;
+    a.norm_topk = d->norm_topk;
+    a.fusion = d->fusion;
+    a.eps = d->rms_eps;
+    hipError_t e = ace::launch_route(d->dtype, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("route_skip launch", e);
+    return ok();
+  } catch (...) {
+    return fail(ACE_EHIP, "unexpected host exception in moe_route_skip");
+  }
+}
+
+ace_status moe_dispatch(const ace_moe_desc* d, const int32_t* topk_idx, const float* topk_gate, const uint8_t* keep,
+                        int32_t* expert_offsets, int32_t* sorted_token, float* sorted_gate, int32_t* slot_pos,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    ace_status st = check_desc(d);
+    if (st != ACE_OK) return st;
+    REQUIRE(topk_idx);
+    REQUIRE(topk_gate);
+    REQUIRE(keep);
+    REQUIRE(expert_offsets);
+    REQUIRE(sorted_token);
+    REQUIRE(sorted_gate);
+    REQUIRE(slot_pos);
+    REQUIRE(workspace);
+    const size_t need = ace::dispatch_workspace_bytes(std::max(d->T, 1), d->E);
+    if (workspace_bytes < need)
+      return fail(ACE_EWORKSPACE, "workspace_bytes=%zu < %zu needed", workspace_bytes, need);
+    if (d->T == 0) return ok();
+    const size_t nchunks = (size_t(d->T) + 63) / 64;
+    const size_t cnt_bytes = ((nchunks * size_t(d->E) * sizeof(int32_t)) + 255) & ~size_t(255);
+    ace::DispatchArgs a;
+    a.idx = topk_idx;
+    a.gate = topk_gate;
+    a.keep = keep;
+    a.offsets = expert_offsets;
+    a.sorted_token = sorted_token;
+    a.sorted_gate = sorted_gate;
+    a.slot_pos = slot_pos;
+    a.ws_cnt = static_cast<int32_t*>(workspace);
+    a.ws_mask = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) + cnt_bytes);
+    a.T = d->T;
+    a.E = d->E;
+    a.k = d->k;
+    hipError_t e = ace::launch_dispatch(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("dispatch launch", e);
+    return ok();
+  } catch (...) {
+    return fail(ACE_EHIP, "unexpected host exception in moe_dispatch");
+  }
+}
+
+ace_status moe_expert_forward(const ace_moe_desc* d, int32_t path, const void* h, const void* w_gate,
+                              const void* w_up, const void* w_down, const int32_t* expert_offsets,
+                              const int32_t* sorted_token, const float* sorted_gate, void* act, float* slot_out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    ace_status st = check_desc(d);
+    if (st != ACE_OK) return st;
+    if (path < ACE_PATH_AUTO || path > ACE_PATH_STREAM) return fail(ACE_EINVAL, "path=%d is not an ace_path", path);
+    REQUIRE(h);
+    REQUIRE(w_gate);
+    REQUIRE(w_up);
+    REQUIRE(w_down);
+    REQUIRE(expert_offsets);
+    REQUIRE(sorted_token);
+    REQUIRE(sorted_gate);
+    REQUIRE(act);
+    REQUIRE(slot_out);
+    (void)workspace;
+    (void)workspace_bytes;
+    if (d->T == 0) return ok();
+    int ncu = 0;
+    st = num_cu(&ncu);
+    if (st != ACE_OK) return st;
+    const bool stream_path =
+        path == ACE_PATH_STREAM || (path == ACE_PATH_AUTO && int64_t(d->T) * d->k <= 256);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
+    g_ev_start = g_ev_stop = nullptr;
+
+    ace::ExpertArgs gu;
+    gu.A = h;
+    gu.W0 = w_gate;
+    gu.W1 = w_up;
+    gu.offsets = expert_offsets;
+    gu.sorted_token = sorted_token;
+    gu.sorted_gate = sorted_gate;
+    gu.out = act;
+    gu.K = d->H;
+    gu.N = d->I;
+    gu.E = d->E;
+    hipError_t e;
+    if (ev0) {
+      e = hipEventRecord(ev0, s);
+      if (e != hipSuccess) return hip_fail("hipEventRecord", e);
+    }
+    e = ace::launch_expert(d->dtype, 0, stream_path, gu, d->T, d->k, ncu, s);
+    if (e != hipSuccess) return hip_fail("gate/up launch", e);
+    if (ev1) {
+      e = hipEventRecord(ev1, s);
+      if (e != hipSuccess) return hip_fail("hipEventRecord", e);
+    }
+    ace::ExpertArgs dn = gu;
+    dn.A = act;
+    dn.W0 = w_down;
+    dn.W1 = nullptr;
+    dn.out = slot_out;
+    dn.K = d->I;
+    dn.N = d->H;
+    e = ace::launch_expert(d->dtype, 1, stream_path, dn, d->T, d->k, ncu, s);
+    if (e != hipSuccess) return hip_fail("down launch", e);
+    return ok();
+  } catch (...) {
+    return fail(ACE_EHIP, "unexpected host exception in moe_expert_forward");
+  }
+}
+
+ace_status moe_combine(const ace_moe_desc* d, const int32_t* slot_pos, const float* slot_out, const void* residual,
+                       void* y, void* stream) {
+  try {
+    ace_status st = check_desc(d);
+    if (st != ACE_OK) return st;
+    REQUIRE(slot_pos);
+    REQUIRE(slot_out);
+    REQUIRE(y);
+    if (d->T == 0) return ok();
+    ace::CombineArgs a;
+    a.slot_pos = slot_pos;
+    a.slot_out = slot_out;
+    a.residual = residual;
+    a.y = y;
+    a.T = d->T;
+    a.H = d->H;
+    a.k = d->k;
+    hipError_t e = ace::launch_combine(d->dtype, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("combine launch", e);
+    return ok();
+  } catch (...) {
+    return fail(ACE_EHIP, "unexpected host exception in moe_combine");
+  }
+}
+
+ace_status moe_set_kernel_events(void* start, void* stop) {
+  if ((start == nullptr) != (stop == nullptr)) return fail(ACE_EINVAL, "start and stop must both be set or both NULL");
+  g_ev_start = static_cast<hipEvent_t>(start);
+  g_ev_stop = static_cast<hipEvent_t>(stop);
+  return ok();
+}
+
+}  // extern "C"

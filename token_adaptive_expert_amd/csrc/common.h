@@ -1,0 +1,82 @@
+// Shared device helpers for the gfx950 kernels: storage types, bf16 rounding,
+// wave reductions and the MFMA fragment types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ace {
+
+// bf16 is stored as its 16-bit pattern (the upper half of an IEEE float32).
+struct bf16_t {
+  uint16_t bits;
+};
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// float32 -> bf16, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// Storage traits: a 16-byte lane load holds EPL elements of the type.
+template <typename T> struct St;
+template <> struct St<float> {
+  static constexpr int EPL = 4;
+  __device__ static float load(const float* p, int64_t i) { return p[i]; }
+  __device__ static float to_f32(float v) { return v; }
+  __device__ static float from_f32(float v) { return v; }
+};
+template <> struct St<bf16_t> {
+  static constexpr int EPL = 8;
+  __device__ static float to_f32(bf16_t v) { return bf16_to_f32(v.bits); }
+  __device__ static bf16_t from_f32(float v) { return bf16_t{f32_to_bf16(v)}; }
+};
+
+// Wave64 reductions (all lanes get the result).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// 16-byte global load / store helpers.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// MFMA wrappers.  Fragment layouts (checked on gfx950):
+//  16x16x32 bf16: lane l holds A[l%16][8*(l/16)+j] and B[8*(l/16)+j][l%16], j<8;
+//  16x16x4 f32:   lane l holds A[l%16][l/16] and B[l/16][l%16];
+//  both:          lane l holds D[4*(l/16)+j][l%16], j<4.
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// One 16-byte fragment pair -> MFMA accumulate.  A 16-byte lane load covers a
+// "k-step": 32 bf16 values (one 16x16x32 MFMA) or 16 f32 values (four 16x16x4
+// MFMAs; lane group q holds k = 4q..4q+3 and MFMA j takes element j, the same
+// k permutation on both operands, so the sum over k is unchanged).
+template <typename T> __device__ __forceinline__ f32x4 mma_step(u32x4 a, u32x4 b, f32x4 c);
+template <> __device__ __forceinline__ f32x4 mma_step<bf16_t>(u32x4 a, u32x4 b, f32x4 c) { return mfma_bf16(a, b, c); }
+template <> __device__ __forceinline__ f32x4 mma_step<float>(u32x4 a, u32x4 b, f32x4 c) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c = mfma_f32(__uint_as_float(a[j]), __uint_as_float(b[j]), c);
+  return c;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+}  // namespace ace

@@ -1,0 +1,72 @@
+// Kernel argument blocks and host-side launchers shared by the C ABI.
+#pragma once
+
+#include "common.h"
+
+namespace ace {
+
+struct RouteArgs {
+  const void* x;
+  const float* gamma;
+  const float* w_router;
+  const float* bias;
+  const float* logits_in;
+  float* logits_out;
+  const float* a_gsp;
+  const float* a_rcr;
+  float tau_gsp, tau_rcr;
+  void* h_out;
+  int32_t* topk_idx;
+  float* topk_gate;
+  uint8_t* keep;
+  int T, H, E, k, norm_topk, fusion;
+  float eps;
+};
+
+struct DispatchArgs {
+  const int32_t* idx;
+  const float* gate;
+  const uint8_t* keep;
+  int32_t* offsets;
+  int32_t* sorted_token;
+  float* sorted_gate;
+  int32_t* slot_pos;
+  int32_t* ws_cnt;     // [nchunks, E] counts, then segment bases
+  uint64_t* ws_mask;   // [nchunks, E] 64-token masks
+  int T, E, k;
+};
+
+struct ExpertArgs {
+  const void* A;              // gate/up: h [T, H] (rows gathered by sorted_token); down: act [*, I]
+  const void* W0;             // gate/up: w_gate; down: w_down
+  const void* W1;             // gate/up: w_up; down: unused
+  const int32_t* offsets;     // [E+1]
+  const int32_t* sorted_token;
+  const float* sorted_gate;
+  void* out;                  // gate/up: act [*, I] (dtype); down: slot_out [*, H] f32
+  int K;                      // contraction length: H (gate/up) or I (down)
+  int N;                      // weight rows per expert: I (gate/up) or H (down)
+  int E;
+};
+
+struct CombineArgs {
+  const int32_t* slot_pos;
+  const float* slot_out;
+  const void* residual;
+  void* y;
+  int T, H, k;
+};
+
+template <typename T> __global__ void route_skip_kernel(RouteArgs a);
+int route_tokens_per_block();
+
+// Host launchers (return the launch status).
+hipError_t launch_route(int dtype, const RouteArgs& a, hipStream_t s);
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+size_t dispatch_workspace_bytes(int T, int E);
+// kind 0: gate/up, 1: down; stream_path selects the small-batch tiling.
+hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs& a, int T, int k, int num_cu,
+                         hipStream_t s);
+hipError_t launch_combine(int dtype, const CombineArgs& a, hipStream_t s);
+
+}  // namespace ace

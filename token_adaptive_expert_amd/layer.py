@@ -1,0 +1,112 @@
+"""Buffer-owning wrapper around the four C-ABI calls of one MoE layer forward.
+
+All arithmetic runs in the HIP library; this file only allocates device
+buffers (torch) and calls moe_route_skip -> moe_dispatch -> moe_expert_forward
+-> moe_combine on one stream, with no host synchronisation in between.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+from . import _lib
+
+
+@dataclasses.dataclass
+class LayerBuffers:
+    """Outputs and scratch of one forward, sized for up to T tokens."""
+
+    T: int
+    h: torch.Tensor
+    logits: torch.Tensor
+    topk_idx: torch.Tensor
+    topk_gate: torch.Tensor
+    keep: torch.Tensor
+    offsets: torch.Tensor
+    sorted_token: torch.Tensor
+    sorted_gate: torch.Tensor
+    slot_pos: torch.Tensor
+    act: torch.Tensor
+    slot_out: torch.Tensor
+    workspace: torch.Tensor
+    y: torch.Tensor
+
+    @staticmethod
+    def allocate(T, H, E, I, k, dtype, device) -> "LayerBuffers":
+        desc = _lib.make_desc(max(T, 1), H, E, I, k, dtype)
+        ws = _lib.moe_workspace_bytes(desc)
+        if ws == 0:
+            raise _lib.AceMoeError(_lib.ACE_EINVAL, "moe_workspace_bytes", _lib.moe_last_error())
+        slots = max(T * k, 1)
+        z = dict(device=device)
+        return LayerBuffers(
+            T=T,
+            h=torch.empty(T, H, dtype=dtype, **z),
+            logits=torch.empty(T, E, dtype=torch.float32, **z),
+            topk_idx=torch.empty(T, k, dtype=torch.int32, **z),
+            topk_gate=torch.empty(T, k, dtype=torch.float32, **z),
+            keep=torch.empty(T, k, dtype=torch.uint8, **z),
+            offsets=torch.empty(E + 1, dtype=torch.int32, **z),
+            sorted_token=torch.empty(slots, dtype=torch.int32, **z),
+            sorted_gate=torch.empty(slots, dtype=torch.float32, **z),
+            slot_pos=torch.empty(T, k, dtype=torch.int32, **z),
+            act=torch.empty(slots, I, dtype=dtype, **z),
+            slot_out=torch.empty(slots, H, dtype=torch.float32, **z),
+            workspace=torch.empty(ws, dtype=torch.uint8, **z),
+            y=torch.empty(T, H, dtype=dtype, **z),
+        )
+
+
+class AceMoeLayer:
+    """One routed SwiGLU MoE layer with ACE slot skipping (device tensors).
+
+    gamma [H] f32, w_router [E,H] f32, router_bias [E] f32 or None,
+    w_gate/w_up [E,I,H] and w_down [E,H,I] in the activation dtype,
+    a_gsp/a_rcr [E] f32 tables."""
+
+    def __init__(self, gamma, w_router, router_bias, w_gate, w_up, w_down, a_gsp, a_rcr, k, norm_topk=1,
+                 fusion="max", rms_eps=1e-6):
+        self.gamma, self.w_router, self.router_bias = gamma, w_router, router_bias
+        self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
+        self.a_gsp, self.a_rcr = a_gsp, a_rcr
+        self.E, self.I, self.H = w_gate.shape
+        self.k, self.norm_topk, self.fusion, self.rms_eps = int(k), int(norm_topk), fusion, float(rms_eps)
+        self.dtype = w_gate.dtype
+
+    def desc(self, T: int):
+        return _lib.make_desc(T, self.H, self.E, self.I, self.k, self.dtype, self.norm_topk, self.fusion, self.rms_eps)
+
+    def buffers(self, T: int) -> LayerBuffers:
+        return LayerBuffers.allocate(T, self.H, self.E, self.I, self.k, self.dtype, self.w_gate.device)
+
+    def route(self, x, tau_gsp, tau_rcr, b: LayerBuffers, logits_in=None, want_logits=True, stream=None):
+        T = x.shape[0]
+        d = self.desc(T)
+        _lib.moe_route_skip(d, x, self.gamma, self.w_router, self.router_bias, logits_in,
+                            b.logits if want_logits else None, self.a_gsp, self.a_rcr, tau_gsp, tau_rcr, b.h,
+                            b.topk_idx, b.topk_gate, b.keep, stream)
+
+    def dispatch(self, T: int, b: LayerBuffers, stream=None):
+        _lib.moe_dispatch(self.desc(T), b.topk_idx, b.topk_gate, b.keep, b.offsets, b.sorted_token, b.sorted_gate,
+                          b.slot_pos, b.workspace, None, stream)
+
+    def experts(self, T: int, b: LayerBuffers, path=_lib.ACE_PATH_AUTO, stream=None):
+        _lib.moe_expert_forward(self.desc(T), path, b.h, self.w_gate, self.w_up, self.w_down, b.offsets,
+                                b.sorted_token, b.sorted_gate, b.act, b.slot_out, b.workspace, None, stream)
+
+    def combine(self, T: int, b: LayerBuffers, residual=None, stream=None):
+        _lib.moe_combine(self.desc(T), b.slot_pos, b.slot_out, residual, b.y, stream)
+
+    def forward(self, x, tau_gsp, tau_rcr, b: LayerBuffers | None = None, path=_lib.ACE_PATH_AUTO, logits_in=None,
+                want_logits=True, residual=None, stream=None) -> torch.Tensor:
+        T = x.shape[0]
+        if b is None:
+            b = self.buffers(T)
+        if b.T < T:
+            raise ValueError(f"buffers sized for {b.T} tokens, got {T}")
+        self.route(x, tau_gsp, tau_rcr, b, logits_in, want_logits, stream)
+        self.dispatch(T, b, stream)
+        self.experts(T, b, path, stream)
+        self.combine(T, b, residual, stream)
+        return b.y[:T]
