@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the ACE-skipped MoE layer forward on one MI355X.
+
+A step is one pass of the whole layer (moe_route_skip -> moe_dispatch ->
+moe_expert_forward -> moe_combine) over one batch.  The headline workload is
+a Qwen3-30B-A3B-shaped layer (hidden 2048, 128 experts, top-8, expert
+intermediate 768, bf16) at T = 1024 prefill tokens and 60% skip, thresholds
+from on-device quantile mapping on the batch itself.  Inputs are seeded
+synthetic data already resident in HBM; the expert weights rotate over
+several copies so that no step finds the previous step's weights in cache.
+
+Prints one JSON line.  Extra fields: decode µs/layer at M = 1..64 tokens,
+prefill throughput at other skip rates, and the oracle timed on host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--skip", type=float, default=0.6)
+    p.add_argument("--copies", type=int, default=8, help="weight copies rotated over the steps")
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=1024, help="tokens in the oracle's timed sample")
+    p.add_argument("--path", type=int, default=0, help="0 auto, 1 grouped, 2 stream")
+    p.add_argument("--layout", choices=["packed", "linear"], default="packed",
+                   help="expert weight layout (packed once at setup, like the offline tables)")
+    return p.parse_args()
+
+
+class Bench:
+    def __init__(self, args):
+        import torch
+        import workloads
+        import token_adaptive_expert_amd as ace
+        from workloads.torch_io import layer_to_torch
+
+        self.torch, self.ace, self.workloads = torch, ace, workloads
+        self.args = args
+        self.dev = torch.device("cuda:0")
+        self.S = workloads.CONFIGS["qwen3_30b_a3b"]
+        t0 = time.time()
+        self.L = workloads.make_layer(self.S, seed=0)
+        P = layer_to_torch(self.L, self.dev)
+        self.P = P
+        # weight copies: copy 0 is the generated layer, the rest are device clones
+        self.layers = []
+        for c in range(max(1, args.copies)):
+            if c == 0:
+                Q = P
+            else:
+                Q = {n: (None if v is None else v.clone()) for n, v in P.items() if n != "x"}
+            lay = ace.AceMoeLayer(Q["gamma"], Q["w_router"], Q["router_bias"], Q["w_gate"], Q["w_up"], Q["w_down"],
+                                  Q["a_gsp"], Q["a_rcr"], self.S.k, self.S.norm_topk, "max", self.S.rms_eps)
+            if args.layout == "packed":
+                lay = lay.packed()
+                if c > 0:
+                    del Q["w_gate"], Q["w_up"], Q["w_down"]
+            self.layers.append(lay)
+        torch.cuda.synchronize()
+        self.setup_s = time.time() - t0
+
+    # ------------------------------------------------------------ helpers
+    def calibrate(self, x, rate):
+        """Thresholds for `rate` on batch x by on-device quantile mapping."""
+        torch, ace = self.torch, self.ace
+        lay = self.layers[0]
+        T = x.shape[0]
+        b = lay.buffers(T)
+        lay.route(x, 0.0, 0.0, b)
+        d = lay.desc(T)
+        ws = torch.empty(ace.moe_calibrate_workspace_bytes(d), dtype=torch.uint8, device=self.dev)
+        tau = torch.zeros(2, dtype=torch.float32, device=self.dev)
+        ace.moe_calibrate_thresholds(d, b.topk_idx, b.topk_gate, lay.a_gsp, lay.a_rcr, rate, tau, None, ws)
+        t = tau.cpu().numpy()
+        return float(t[0]), float(t[1])
+
+    def run_steps(self, x, tau, steps, warmup, path):
+        """Whole-layer steps, weights rotating over the copies.  Returns
+        (ms per step, buffers of the last step)."""
+        torch = self.torch
+        T = x.shape[0]
+        bufs = self.layers[0].buffers(T)
+        nl = len(self.layers)
+        for i in range(warmup):
+            self.layers[i % nl].forward(x, tau[0], tau[1], bufs, path)
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            self.layers[(warmup + i) % nl].forward(x, tau[0], tau[1], bufs, path)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / steps, bufs
+
+    def stage_ms(self, x, tau, stage, steps, path):
+        """Mean duration of one expert kernel (gate/up or down) launched back to
+        back on the current stream, HIP events around the whole run, weights
+        rotating over the copies; routing and dispatch are done once before."""
+        torch = self.torch
+        T = x.shape[0]
+        bufs = self.layers[0].buffers(T)
+        self.layers[0].forward(x, tau[0], tau[1], bufs, path)
+        nl = len(self.layers)
+        for i in range(3):
+            self.layers[i % nl].experts(T, bufs, path | stage)
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            self.layers[(3 + i) % nl].experts(T, bufs, path | stage)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / steps
+
+    def copy_ceiling(self, nbytes=2 << 30, reps=10):
+        """Read+write bandwidth of a plain device-to-device copy (torch), as a
+        measured ceiling beside the datasheet peak."""
+        torch = self.torch
+        a = torch.empty(nbytes // 2, dtype=torch.uint8, device=self.dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(reps):
+            b.copy_(a)
+        stop.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / reps
+        del a, b
+        return 2 * (nbytes // 2) / (ms * 1e-3) / 1e9
+
+    def counts(self, bufs):
+        off = bufs.offsets.cpu().numpy().astype(np.int64)
+        n_e = np.diff(off)
+        return int(off[-1]), int((n_e > 0).sum())
+
+    # ------------------------------------------------------------ legs
+    def prefill(self, rate, kernel_timing=True):
+        """Whole-layer steps timed alone; then each expert kernel timed alone."""
+        x = self.P["x"]
+        tau = self.calibrate(x, rate) if rate > 0 else (0.0, 0.0)
+        ms, bufs = self.run_steps(x, tau, self.args.steps, self.args.warmup, self.args.path)
+        gu = dn = None
+        if kernel_timing:
+            gu = self.stage_ms(x, tau, self.ace.ACE_STAGE_GATEUP, self.args.steps, self.args.path)
+            dn = self.stage_ms(x, tau, self.ace.ACE_STAGE_DOWN, self.args.steps, self.args.path)
+        n_kept, U = self.counts(bufs)
+        return dict(tau=tau, ms=ms, gateup_ms=gu, down_ms=dn, n_kept=n_kept, U=U)
+
+    def decode(self, tau):
+        torch, workloads = self.torch, self.workloads
+        from workloads.torch_io import to_torch
+        out = {}
+        S = self.S
+        for M in workloads.DECODE_M:
+            Sd = workloads.CONFIGS["qwen3_30b_a3b_decode"].with_tokens(M)
+            x = to_torch(workloads.make_tokens(Sd, seed=0, step=1), self.dev)
+            ms, bufs = self.run_steps(x, tau, max(self.args.steps, 50), self.args.warmup, 0)
+            n_kept, U = self.counts(bufs)
+            wbytes = U * 3 * S.H * S.I * 2
+            out[M] = dict(us=ms * 1e3, U=U, n_kept=n_kept, retained_weight_MB=wbytes / 1e6,
+                          hbm_frac=(wbytes / (ms * 1e-3)) / (HBM_PEAK_GBS * 1e9))
+        return out
+
+
+def cpu_baseline(L, S, tau, ntok):
+    """The oracle, as it stands, on the first `ntok` tokens of the batch."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    x = L["x"][:ntok]
+    t0 = time.time()
+    oracle.moe_layer(x, L["gamma"], L["w_router"], L["router_bias"], L["w_gate"], L["w_up"], L["w_down"],
+                     L["a_gsp"], L["a_rcr"], tau[0], tau[1], S.k, bool(S.norm_topk), S.rms_eps, S.dtype)
+    dt = time.time() - t0
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {ntok} of the {S.T} prefill tokens, same layer and thresholds, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    B = Bench(args)
+    S = B.S
+    head = B.prefill(args.skip)
+    T = S.T
+    value = T / (head["ms"] * 1e-3)
+    # dominant kernel: grouped gate/up GEMM (+SiLU); algorithmic bytes per launch
+    gu_bytes = head["U"] * 2 * S.H * S.I * 2 + T * S.H * 2 + head["n_kept"] * S.I * 2
+    gu_gbs = gu_bytes / (head["gateup_ms"] * 1e-3) / 1e9
+    dn_bytes = head["U"] * S.H * S.I * 2 + head["n_kept"] * (S.I * 2 + S.H * 4)
+    layer_bytes = head["U"] * 3 * S.H * S.I * 2 + S.E * S.H * 4 + T * S.H * 4 + 8 * S.E
+    layer_flops = head["n_kept"] * 6 * S.H * S.I + 2 * T * S.H * S.E
+    res = {
+        "metric": "ACE-skipped MoE-layer tokens/s (T=1024 prefill) + decode µs/layer, % roofline",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3_30b_a3b MoE layer prefill: T=1024 H=2048 E=128 I=768 top-8, bf16, "
+                               f"{int(args.skip * 100)}% skip, {args.copies} rotated weight copies",
+                   "weight_layout": args.layout,
+                   "T": T, "H": S.H, "E": S.E, "I": S.I, "k": S.k, "skip_target": args.skip,
+                   "skip_realized": round(1 - head["n_kept"] / (T * S.k), 5), "active_experts": head["U"],
+                   "tau": [head["tau"][0], head["tau"][1]]},
+        "roofline": {"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "expert_gemm gate/up+SiLU (grouped)", "kernel_ms": round(head["gateup_ms"], 5),
+                     "alg_bytes_per_launch": gu_bytes,
+                     "down_kernel_ms": round(head["down_ms"], 5),
+                     "down_achieved": round(dn_bytes / (head["down_ms"] * 1e-3) / 1e9, 1)},
+        "layer_roofline": {"alg_bytes": layer_bytes, "alg_flops": layer_flops,
+                           "hbm_frac": round(layer_bytes / (head["ms"] * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                           "mfma_frac": round(layer_flops / (head["ms"] * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+                           "us_per_layer": round(head["ms"] * 1e3, 2)},
+    }
+    res["hbm_copy_ceiling_GBs"] = round(B.copy_ceiling(), 1)
+    if not args.no_sweep:
+        sweep = {}
+        for r in (0.0, 0.5):
+            o = B.prefill(r, kernel_timing=False)
+            sweep[str(r)] = {"tokens_per_s": round(T / (o["ms"] * 1e-3), 1), "us_per_layer": round(o["ms"] * 1e3, 2),
+                             "active_experts": o["U"], "n_kept": o["n_kept"]}
+        sweep[str(args.skip)] = {"tokens_per_s": res["value"], "us_per_layer": res["layer_roofline"]["us_per_layer"],
+                                 "active_experts": head["U"], "n_kept": head["n_kept"]}
+        res["prefill_by_skip"] = sweep
+    if not args.no_decode:
+        dec = B.decode(head["tau"])
+        res["decode_us_per_layer"] = {str(m): round(v["us"], 2) for m, v in dec.items()}
+        res["decode_detail"] = {str(m): {k2: (round(v2, 4) if isinstance(v2, float) else v2) for k2, v2 in v.items()}
+                                for m, v in dec.items()}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(B.L, S, head["tau"], args.cpu_tokens)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

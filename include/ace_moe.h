@@ -57,6 +57,10 @@ typedef enum { ACE_F32 = 0, ACE_BF16 = 1 } ace_dtype;
  * STREAM tiles 16 rows and splits weights finer, for small batches whose cost
  * is reading the retained experts' weights (decode).  AUTO picks by T*k. */
 typedef enum { ACE_PATH_AUTO = 0, ACE_PATH_GROUPED = 1, ACE_PATH_STREAM = 2 } ace_path;
+/* Optional bits or-ed into the path argument of moe_expert_forward to run
+ * only one of its two kernels (for timing a stage alone); no bit = both. */
+#define ACE_STAGE_GATEUP 0x100
+#define ACE_STAGE_DOWN 0x200
 
 /* How the two views are fused into the skip decision (Methodology section 3;
  * the alternatives are the page's ablations, Tables 4 and 5).  With
@@ -73,6 +77,14 @@ typedef enum {
   ACE_FUSE_GSP = 3, ACE_FUSE_RCR = 4, ACE_FUSE_SCORE = 5
 } ace_fusion;
 
+/* Layout of the expert weights passed to moe_expert_forward.
+ * LINEAR: nn.Linear [E, N, K] (w_gate/w_up: N = I, K = H; w_down: N = H, K = I).
+ * PACKED: the same values as made by moe_pack_weights, grouped so that each
+ *   wave load reads one contiguous 1 KB block:
+ *   [E][N/16][K/KS][64][V] with V = 16 bytes / element size (8 bf16, 4 f32)
+ *   and KS = 4*V; entry [e][g][j][l][v] = linear[e][16*g + l%16][KS*j + V*(l/16) + v]. */
+typedef enum { ACE_LAYOUT_LINEAR = 0, ACE_LAYOUT_PACKED = 1 } ace_weight_layout;
+
 typedef struct {
   int32_t T;         /* tokens in the batch (rows of x) */
   int32_t H;         /* hidden size */
@@ -83,6 +95,7 @@ typedef struct {
   int32_t norm_topk; /* 1: gates renormalised over the k selected experts */
   int32_t fusion;    /* ace_fusion */
   float rms_eps;     /* RMSNorm epsilon, added to the mean square */
+  int32_t weight_layout; /* ace_weight_layout of w_gate, w_up, w_down */
 } ace_moe_desc;
 
 int moe_abi_version(void);
@@ -97,18 +110,20 @@ size_t moe_workspace_bytes(const ace_moe_desc* d);
  * moe_route_skip -- RMSNorm, router, top-k gates and the ACE skip mask.
  *   h[t]      = x[t] / sqrt(mean_j x[t,j]^2 + rms_eps) * gamma   (x = x̄Γ, Theoretical
  *               Foundation), stored in dtype.
- *   logits[t] = h[t] . w_router^T (+ router_bias), float32 accumulation.
+ *   logits[t] = h[t] . w_router^T (+ router_bias), float32 accumulation in a
+ *               fixed order (deterministic).
  *   topk_idx  = the k largest logits, descending, equal logits to the lower
  *               expert index; slot 0 is the top-1 expert.
  *   topk_gate = softmax of the logits in float64 (over all E, or over the k
  *               selected when norm_topk), rounded to float32.
  *   keep      = the fusion rule above with (tau_gsp, tau_rcr); keep[t,0] = 1.
- * In:  x [T,H] dtype; gamma [H] f32; w_router [E,H] f32; router_bias [E] f32
- *      or NULL; logits_in [T,E] f32 or NULL (when given, used instead of the
- *      router product, which is then not computed); a_gsp, a_rcr [E] f32, > 0;
- *      tau_gsp, tau_rcr >= 0.
- * Out: h_out [T,H] dtype; logits_out [T,E] f32 or NULL; topk_idx [T,k] i32;
- *      topk_gate [T,k] f32; keep [T,k] u8 (0/1).
+ * In:  x [T,H] dtype; gamma [H] f32; w_router [E,H] f32 (may be NULL when
+ *      logits_in is given); router_bias [E] f32 or NULL; logits_in [T,E] f32
+ *      or NULL (when given, used instead of the router product, which is then
+ *      not computed); a_gsp, a_rcr [E] f32, > 0; tau_gsp, tau_rcr >= 0.
+ * Out: h_out [T,H] dtype; logits_out [T,E] f32 (required: the router writes
+ *      its logits there, or logits_in is copied there; must not alias
+ *      logits_in); topk_idx [T,k] i32; topk_gate [T,k] f32; keep [T,k] u8.
  * Logits must be finite; results for NaN logits are unspecified.
  */
 ace_status moe_route_skip(const ace_moe_desc* d, const void* x, const float* gamma, const float* w_router,
@@ -155,6 +170,37 @@ ace_status moe_expert_forward(const ace_moe_desc* d, int32_t path, const void* h
  */
 ace_status moe_combine(const ace_moe_desc* d, const int32_t* slot_pos, const float* slot_out, const void* residual,
                        void* y, void* stream);
+
+/*
+ * moe_calibrate_thresholds -- per-layer thresholds (tau_gsp, tau_rcr) by
+ * quantile mapping (Efficiency Results, Table 6) for a target skip rate over
+ * all T*k routed slots, matched to the given batch's own routing.
+ * Reading used: eligible slots are all but the top-1; each view ranks their
+ * scores g*A(e) ascending (ties by slot order); a slot's fused rank is the
+ * larger of its two ranks (max-fusion); with n = floor(skip_rate*T*k + 1/2),
+ * m is the largest level with #{fused rank < m} <= n, and tau_v lies strictly
+ * between view v's (m-1)-th and m-th smallest score (float32 midpoint).  Then
+ * moe_route_skip with these thresholds skips n-1 or n slots of this batch.
+ * n = 0 gives (0, 0); skipping every eligible slot gives just above the
+ * largest scores.
+ * In:  topk_idx, topk_gate [T,k] (from moe_route_skip; thresholds passed to
+ *      it do not matter); a_gsp, a_rcr [E]; skip_rate in [0, (k-1)/k].
+ * Out: tau_out [2] f32 (device); level_out [2] i32 (m, n) or NULL.
+ * workspace: >= moe_calibrate_workspace_bytes(d) bytes.
+ */
+size_t moe_calibrate_workspace_bytes(const ace_moe_desc* d);
+ace_status moe_calibrate_thresholds(const ace_moe_desc* d, const int32_t* topk_idx, const float* topk_gate,
+                                    const float* a_gsp, const float* a_rcr, float skip_rate, float* tau_out,
+                                    int32_t* level_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_pack_weights -- copy expert weights from the LINEAR layout into the
+ * PACKED layout (see ace_weight_layout), typically once when a checkpoint is
+ * loaded.  which = 0: a gate or up projection [E, I, H]; which = 1: the down
+ * projection [E, H, I].  src and dst hold E*N*K elements of desc->dtype and
+ * must not overlap.  desc->weight_layout is ignored here.
+ */
+ace_status moe_pack_weights(const ace_moe_desc* d, int32_t which, const void* src, void* dst, void* stream);
 
 /*
  * moe_set_kernel_events -- for profiling callers: the next moe_expert_forward

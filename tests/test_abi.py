@@ -40,8 +40,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_desc_layout_matches_header():
     m, _ = _lib()
-    # nine 4-byte fields, no padding
-    assert ctypes.sizeof(m.MoeDesc) == 36
+    # ten 4-byte fields, no padding
+    assert ctypes.sizeof(m.MoeDesc) == 40
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -55,14 +55,15 @@ def test_desc_layout_matches_header():
     (dict(dtype=7), 1, "dtype=7"),
     (dict(fusion=9), 1, "fusion=9"),
     (dict(norm_topk=2), 1, "norm_topk=2"),
+    (dict(weight_layout=3), 1, "weight_layout=3"),
 ])
 def test_bad_descriptors_are_rejected_before_launch(kw, status, needle):
     m, lib = _lib()
-    base = dict(T=8, H=256, E=16, I=128, k=4, dtype=1, norm_topk=1, fusion=0, rms_eps=1e-6)
+    base = dict(T=8, H=256, E=16, I=128, k=4, dtype=1, norm_topk=1, fusion=0, rms_eps=1e-6, weight_layout=0)
     base.update(kw)
     d = m.MoeDesc(**base)
     fake = 0x1000  # never dereferenced: validation fails first
-    st = lib.moe_route_skip(ctypes.byref(d), fake, fake, fake, None, None, None, fake, fake, 0.0, 0.0, fake, fake,
+    st = lib.moe_route_skip(ctypes.byref(d), fake, fake, fake, None, None, fake, fake, fake, 0.0, 0.0, fake, fake,
                             fake, fake, None)
     assert st == status
     assert needle in lib.moe_last_error().decode()
@@ -72,12 +73,18 @@ def test_bad_descriptors_are_rejected_before_launch(kw, status, needle):
 def test_null_pointers_named():
     m, lib = _lib()
     d = m.make_desc(8, 256, 16, 128, 4, "bf16")
-    st = lib.moe_route_skip(ctypes.byref(d), None, 0x1000, 0x1000, None, None, None, 0x1000, 0x1000, 0.0, 0.0,
+    st = lib.moe_route_skip(ctypes.byref(d), None, 0x1000, 0x1000, None, None, 0x1000, 0x1000, 0x1000, 0.0, 0.0,
                             0x1000, 0x1000, 0x1000, 0x1000, None)
     assert st == 1 and "x is NULL" in lib.moe_last_error().decode()
+    st = lib.moe_route_skip(ctypes.byref(d), 0x1000, 0x1000, 0x1000, None, None, None, 0x1000, 0x1000, 0.0, 0.0,
+                            0x1000, 0x1000, 0x1000, 0x1000, None)
+    assert st == 1 and "logits_out is NULL" in lib.moe_last_error().decode()
+    st = lib.moe_route_skip(ctypes.byref(d), 0x1000, 0x1000, 0x1000, None, 0x2000, 0x2000, 0x1000, 0x1000, 0.0, 0.0,
+                            0x1000, 0x1000, 0x1000, 0x1000, None)
+    assert st == 1 and "alias" in lib.moe_last_error().decode()
     st = lib.moe_combine(ctypes.byref(d), 0x1000, None, None, 0x1000, None)
     assert st == 1 and "slot_out is NULL" in lib.moe_last_error().decode()
-    st = lib.moe_route_skip(ctypes.byref(d), 0x1000, 0x1000, 0x1000, None, None, None, 0x1000, 0x1000, -1.0, 0.0,
+    st = lib.moe_route_skip(ctypes.byref(d), 0x1000, 0x1000, 0x1000, None, None, 0x1000, 0x1000, 0x1000, -1.0, 0.0,
                             0x1000, 0x1000, 0x1000, 0x1000, None)
     assert st == 1 and "thresholds" in lib.moe_last_error().decode()
     assert lib.moe_route_skip(None, *([0x1000] * 8), 0.0, 0.0, *([0x1000] * 4), None) == 1
@@ -96,7 +103,7 @@ def test_empty_batch_is_a_no_op():
     m, lib = _lib()
     d = m.make_desc(0, 256, 16, 128, 4, "f32")
     f = 0x1000
-    assert lib.moe_route_skip(ctypes.byref(d), f, f, f, None, None, None, f, f, 0.0, 0.0, f, f, f, f, None) == 0
+    assert lib.moe_route_skip(ctypes.byref(d), f, f, f, None, None, f, f, f, 0.0, 0.0, f, f, f, f, None) == 0
     assert lib.moe_dispatch(ctypes.byref(d), f, f, f, f, f, f, f, f, 1 << 20, None) == 0
     assert lib.moe_expert_forward(ctypes.byref(d), 0, f, f, f, f, f, f, f, f, f, None, 0, None) == 0
     assert lib.moe_combine(ctypes.byref(d), f, f, None, f, None) == 0
@@ -110,3 +117,11 @@ def test_bad_path_and_events():
     assert lib.moe_expert_forward(ctypes.byref(d), 5, f, f, f, f, f, f, f, f, f, None, 0, None) == 1
     assert lib.moe_set_kernel_events(f, None) == 1
     assert lib.moe_set_kernel_events(None, None) == 0
+
+
+def test_pack_rejects_overlap_and_bad_kind():
+    m, lib = _lib()
+    d = m.make_desc(8, 256, 16, 128, 4, "bf16")
+    assert lib.moe_pack_weights(ctypes.byref(d), 2, 0x1000, 0x100000000, None) == 1
+    assert lib.moe_pack_weights(ctypes.byref(d), 0, 0x1000, 0x1000 + 64, None) == 1
+    assert "overlap" in lib.moe_last_error().decode()

@@ -241,3 +241,100 @@ def test_qwen3_decode_steps(qwen, dev, M):
     for path in PATHS:
         gp = gl.run(tg, tr, path=path)
         assert rel_l2(values(gp["y"]), ref["y"]) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------- on-device quantile mapping
+def _calibrate(gl, g, rate, dev):
+    S = gl.S
+    T = g["topk_idx"].shape[0]
+    d = gl.layer.desc(T)
+    ws = torch.empty(ace.moe_calibrate_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    tau = torch.full((2,), -1.0, dtype=torch.float32, device=dev)
+    lvl = torch.full((2,), -1, dtype=torch.int32, device=dev)
+    idx = torch.from_numpy(g["topk_idx"]).to(dev)
+    gate = torch.from_numpy(g["topk_gate"]).to(dev)
+    ace.moe_calibrate_thresholds(d, idx, gate, gl.P["a_gsp"], gl.P["a_rcr"], rate, tau, lvl, ws)
+    torch.cuda.synchronize()
+    return tau.cpu().numpy(), lvl.cpu().numpy()
+
+
+@pytest.mark.parametrize("rate", [0.0, 0.1, 0.3, 0.5, 0.6, 0.75])
+def test_calibration_matches_oracle(tiny, dev, rate):
+    L, _, _ = tiny
+    S = L["shape"]
+    gl = GpuLayer(L, dev)
+    g = gl.run(0.0, 0.0)
+    tau, lvl = _calibrate(gl, g, rate, dev)
+    tg, tr, m, n = oracle.quantile_thresholds(g["topk_idx"], g["topk_gate"], L["a_gsp"], L["a_rcr"], rate)
+    assert tau[0] == tg and tau[1] == tr and lvl[1] == n and (n == 0 or lvl[0] == m)
+    gk = gl.run(tau[0], tau[1])
+    skipped = int((~gk["keep"]).sum())
+    assert skipped in (n - 1, n) if n else skipped == 0
+
+
+def test_calibration_with_tied_scores(tiny, dev):
+    """Equal logits make every gate 1/k, so slots of one expert tie exactly;
+    ties are ranked by slot order on both sides."""
+    L, _, _ = tiny
+    S = L["shape"]
+    gl = GpuLayer(L, dev)
+    g = gl.run(0.0, 0.0, logits_in=np.zeros((S.T, S.E), np.float32))
+    for rate in (0.25, 0.5):
+        tau, lvl = _calibrate(gl, g, rate, dev)
+        tg, tr, m, n = oracle.quantile_thresholds(g["topk_idx"], g["topk_gate"], L["a_gsp"], L["a_rcr"], rate)
+        assert tau[0] == tg and tau[1] == tr and lvl[0] == m
+
+
+@pytest.mark.parametrize("rate", [0.5, 0.6])
+def test_calibration_full_size(qwen, dev, rate):
+    L, _, _ = qwen
+    gl = GpuLayer(L, dev)
+    g = gl.run(0.0, 0.0)
+    tau, lvl = _calibrate(gl, g, rate, dev)
+    tg, tr, m, n = oracle.quantile_thresholds(g["topk_idx"], g["topk_gate"], L["a_gsp"], L["a_rcr"], rate)
+    assert tau[0] == tg and tau[1] == tr and lvl[0] == m and lvl[1] == n
+
+
+# ---------------------------------------------------------------- packed weight layout
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("which", ["tiny", "bf16"])
+def test_packed_layout_matches_linear_bitwise(tiny, dev, path, which):
+    """The packed layout only moves weight bytes; the MFMA sequence is the
+    same, so every output bit must match the linear layout."""
+    if which == "tiny":
+        L, tg, tr = tiny
+    else:
+        L, tg, tr = _bf16_case(T=77, H=384, E=12, I=640, k=3, rate=0.4, cfg_id=107)
+    gl = GpuLayer(L, dev)
+    a = gl.run(tg, tr, path)
+    gl.layer = gl.layer.packed()
+    torch.cuda.synchronize()
+    b = gl.run(tg, tr, path)
+    n = int(a["offsets"][-1])
+    for name in ("act", "slot_out"):
+        assert np.array_equal(a[name][:n].view(np.uint8), b[name][:n].view(np.uint8)), name
+    assert np.array_equal(a["y"].view(np.uint8), b["y"].view(np.uint8))
+    # the packed copy is a permutation of the linear one
+    w = gl.P["w_gate"].cpu()
+    pw = gl.layer.w_gate.cpu()
+    assert torch.equal(torch.sort(w.reshape(-1).view(torch.int16) if w.dtype == torch.bfloat16 else w.reshape(-1))[0],
+                       torch.sort(pw.reshape(-1).view(torch.int16) if pw.dtype == torch.bfloat16 else pw.reshape(-1))[0])
+
+
+def test_packed_layout_formula(dev):
+    """Entries of the packed layout checked against its definition in the header."""
+    E, H, I = 2, 128, 256
+    d = ace.make_desc(1, H, E, I, 1, "f32")
+    for which, (N, K) in ((0, (I, H)), (1, (H, I))):
+        src = torch.arange(E * N * K, dtype=torch.float32, device=dev).reshape(E, N, K)
+        dst = torch.empty_like(src)
+        ace.moe_pack_weights(d, which, src, dst)
+        torch.cuda.synchronize()
+        V, KS = 4, 16
+        flat = dst.reshape(-1).cpu().numpy()
+        lin = src.cpu().numpy()
+        Ng, Kj = N // 16, K // KS
+        for (e, g, j, l, v) in [(0, 0, 0, 0, 0), (1, 3, 5, 37, 2), (1, Ng - 1, Kj - 1, 63, 3), (0, 2, 1, 16, 1)]:
+            idx = (((e * Ng + g) * Kj + j) * 64 + l) * V + v
+            assert flat[idx] == lin[e, 16 * g + l % 16, KS * j + V * (l // 16) + v]
+        assert np.array_equal(np.sort(flat), np.sort(lin.reshape(-1)))

@@ -2,12 +2,15 @@
 expert-slot skipping.  The arithmetic lives in the HIP library built from
 ``csrc/``; this package holds its ctypes binding and a buffer-owning layer
 wrapper (torch supplies device memory and streams)."""
-from ._lib import (ACE_BF16, ACE_F32, ACE_PATH_AUTO, ACE_PATH_GROUPED, ACE_PATH_STREAM, AceMoeError, MoeDesc,
-                   load, make_desc, moe_abi_version, moe_combine, moe_dispatch, moe_expert_forward,
+from ._lib import (ACE_BF16, ACE_F32, ACE_PATH_AUTO, ACE_PATH_GROUPED, ACE_PATH_STREAM, ACE_STAGE_DOWN,
+                   ACE_STAGE_GATEUP, AceMoeError, MoeDesc,
+                   ACE_LAYOUT_LINEAR, ACE_LAYOUT_PACKED, load, make_desc, moe_abi_version, moe_calibrate_thresholds, moe_calibrate_workspace_bytes, moe_combine,
+                   moe_dispatch, moe_expert_forward, moe_pack_weights,
                    moe_last_error, moe_route_skip, moe_set_kernel_events, moe_workspace_bytes)
 from .layer import AceMoeLayer, LayerBuffers
 
-__all__ = ["ACE_BF16", "ACE_F32", "ACE_PATH_AUTO", "ACE_PATH_GROUPED", "ACE_PATH_STREAM", "AceMoeError", "MoeDesc",
-           "load", "make_desc", "moe_abi_version", "moe_combine", "moe_dispatch", "moe_expert_forward",
+__all__ = ["ACE_BF16", "ACE_F32", "ACE_PATH_AUTO", "ACE_PATH_GROUPED", "ACE_PATH_STREAM", "ACE_STAGE_DOWN",
+           "ACE_STAGE_GATEUP", "AceMoeError", "MoeDesc",
+           "ACE_LAYOUT_LINEAR", "ACE_LAYOUT_PACKED", "load", "make_desc", "moe_pack_weights", "moe_abi_version", "moe_calibrate_thresholds", "moe_calibrate_workspace_bytes", "moe_combine", "moe_dispatch", "moe_expert_forward",
            "moe_last_error", "moe_route_skip", "moe_set_kernel_events", "moe_workspace_bytes", "AceMoeLayer",
            "LayerBuffers"]

@@ -18,12 +18,14 @@ LIB_PATH = os.environ.get("ACE_MOE_LIB") or os.path.join(PKG, "lib", "libace_moe
 ACE_OK, ACE_EINVAL, ACE_EUNSUPPORTED, ACE_EWORKSPACE, ACE_EHIP = range(5)
 ACE_F32, ACE_BF16 = 0, 1
 ACE_PATH_AUTO, ACE_PATH_GROUPED, ACE_PATH_STREAM = 0, 1, 2
+ACE_STAGE_GATEUP, ACE_STAGE_DOWN = 0x100, 0x200
 FUSION = {"max": 0, "min": 1, "mean": 2, "gsp": 3, "rcr": 4, "score": 5}
 
 STATUS_NAMES = {0: "ACE_OK", 1: "ACE_EINVAL", 2: "ACE_EUNSUPPORTED", 3: "ACE_EWORKSPACE", 4: "ACE_EHIP"}
 
 EXPORTS = ["moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_route_skip", "moe_dispatch",
-           "moe_expert_forward", "moe_combine", "moe_set_kernel_events"]
+           "moe_expert_forward", "moe_combine", "moe_calibrate_workspace_bytes", "moe_calibrate_thresholds",
+           "moe_pack_weights", "moe_set_kernel_events"]
 
 
 class AceMoeError(RuntimeError):
@@ -35,17 +37,21 @@ class AceMoeError(RuntimeError):
 class MoeDesc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("dtype", ctypes.c_int32), ("norm_topk", ctypes.c_int32),
-                ("fusion", ctypes.c_int32), ("rms_eps", ctypes.c_float)]
+                ("fusion", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("weight_layout", ctypes.c_int32)]
 
 
-def make_desc(T, H, E, I, k, dtype, norm_topk=1, fusion="max", rms_eps=1e-6) -> MoeDesc:
+ACE_LAYOUT_LINEAR, ACE_LAYOUT_PACKED = 0, 1
+
+
+def make_desc(T, H, E, I, k, dtype, norm_topk=1, fusion="max", rms_eps=1e-6, weight_layout=0) -> MoeDesc:
     if isinstance(dtype, torch.dtype):
         dtype = {torch.float32: ACE_F32, torch.bfloat16: ACE_BF16}[dtype]
     elif isinstance(dtype, str):
         dtype = {"f32": ACE_F32, "bf16": ACE_BF16}[dtype]
     if isinstance(fusion, str):
         fusion = FUSION[fusion]
-    return MoeDesc(int(T), int(H), int(E), int(I), int(k), int(dtype), int(norm_topk), int(fusion), float(rms_eps))
+    return MoeDesc(int(T), int(H), int(E), int(I), int(k), int(dtype), int(norm_topk), int(fusion), float(rms_eps),
+                   int(weight_layout))
 
 
 _lib = None
@@ -75,6 +81,12 @@ def load() -> ctypes.CDLL:
     lib.moe_expert_forward.argtypes = [D, I32, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.moe_combine.restype = ctypes.c_int
     lib.moe_combine.argtypes = [D, P, P, P, P, P]
+    lib.moe_calibrate_workspace_bytes.restype = SZ
+    lib.moe_calibrate_workspace_bytes.argtypes = [D]
+    lib.moe_calibrate_thresholds.restype = ctypes.c_int
+    lib.moe_calibrate_thresholds.argtypes = [D, P, P, P, P, F32, P, P, P, SZ, P]
+    lib.moe_pack_weights.restype = ctypes.c_int
+    lib.moe_pack_weights.argtypes = [D, I32, P, P, P]
     lib.moe_set_kernel_events.restype = ctypes.c_int
     lib.moe_set_kernel_events.argtypes = [P, P]
     _lib = lib
@@ -144,6 +156,24 @@ def moe_expert_forward(desc, path, h, w_gate, w_up, w_down, expert_offsets, sort
 def moe_combine(desc, slot_pos, slot_out, residual, y, stream=None):
     _check(load().moe_combine(ctypes.byref(desc), _ptr(slot_pos), _ptr(slot_out), _ptr(residual), _ptr(y),
                               _stream(stream)), "moe_combine")
+
+
+def moe_calibrate_workspace_bytes(desc: MoeDesc) -> int:
+    return int(load().moe_calibrate_workspace_bytes(ctypes.byref(desc)))
+
+
+def moe_calibrate_thresholds(desc, topk_idx, topk_gate, a_gsp, a_rcr, skip_rate, tau_out, level_out, workspace,
+                             workspace_bytes=None, stream=None):
+    nbytes = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    _check(load().moe_calibrate_thresholds(ctypes.byref(desc), _ptr(topk_idx), _ptr(topk_gate), _ptr(a_gsp),
+                                           _ptr(a_rcr), float(skip_rate), _ptr(tau_out), _ptr(level_out),
+                                           _ptr(workspace), int(nbytes), _stream(stream)),
+           "moe_calibrate_thresholds")
+
+
+def moe_pack_weights(desc, which, src, dst, stream=None):
+    _check(load().moe_pack_weights(ctypes.byref(desc), int(which), _ptr(src), _ptr(dst), _stream(stream)),
+           "moe_pack_weights")
 
 
 def moe_set_kernel_events(start, stop):

@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdarg>
+#include <cmath>
 #include <cstdio>
 #include <string>
 
@@ -65,6 +66,8 @@ ace_status check_desc(const ace_moe_desc* d) {
     return fail(ACE_EINVAL, "fusion=%d is not an ace_fusion", d->fusion);
   if (d->norm_topk != 0 && d->norm_topk != 1) return fail(ACE_EINVAL, "norm_topk=%d must be 0 or 1", d->norm_topk);
   if (!(d->rms_eps >= 0.f)) return fail(ACE_EINVAL, "rms_eps must be >= 0");
+  if (d->weight_layout != ACE_LAYOUT_LINEAR && d->weight_layout != ACE_LAYOUT_PACKED)
+    return fail(ACE_EINVAL, "weight_layout=%d is not an ace_weight_layout", d->weight_layout);
   if (d->E > 256) return fail(ACE_EUNSUPPORTED, "E=%d > 256", d->E);
   if (d->k > 16 || d->k > d->E) return fail(ACE_EUNSUPPORTED, "k=%d must be <= min(E, 16)", d->k);
   if (d->H % 128 != 0) return fail(ACE_EUNSUPPORTED, "H=%d is not a multiple of 128", d->H);
@@ -100,6 +103,8 @@ ace_status moe_route_skip(const ace_moe_desc* d, const void* x, const float* gam
     REQUIRE(x);
     REQUIRE(gamma);
     if (logits_in == nullptr) REQUIRE(w_router);
+    REQUIRE(logits_out);
+    if (logits_in == logits_out) return fail(ACE_EINVAL, "logits_in and logits_out must not alias");
     REQUIRE(a_gsp);
     REQUIRE(a_rcr);
     REQUIRE(h_out);
@@ -157,8 +162,6 @@ ace_status moe_dispatch(const ace_moe_desc* d, const int32_t* topk_idx, const fl
     if (workspace_bytes < need)
       return fail(ACE_EWORKSPACE, "workspace_bytes=%zu < %zu needed", workspace_bytes, need);
     if (d->T == 0) return ok();
-    const size_t nchunks = (size_t(d->T) + 63) / 64;
-    const size_t cnt_bytes = ((nchunks * size_t(d->E) * sizeof(int32_t)) + 255) & ~size_t(255);
     ace::DispatchArgs a;
     a.idx = topk_idx;
     a.gate = topk_gate;
@@ -167,8 +170,6 @@ ace_status moe_dispatch(const ace_moe_desc* d, const int32_t* topk_idx, const fl
     a.sorted_token = sorted_token;
     a.sorted_gate = sorted_gate;
     a.slot_pos = slot_pos;
-    a.ws_cnt = static_cast<int32_t*>(workspace);
-    a.ws_mask = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) + cnt_bytes);
     a.T = d->T;
     a.E = d->E;
     a.k = d->k;
@@ -187,6 +188,10 @@ ace_status moe_expert_forward(const ace_moe_desc* d, int32_t path, const void* h
   try {
     ace_status st = check_desc(d);
     if (st != ACE_OK) return st;
+    const int stages = path & (ACE_STAGE_GATEUP | ACE_STAGE_DOWN);
+    const bool run_gu = stages == 0 || (stages & ACE_STAGE_GATEUP);
+    const bool run_dn = stages == 0 || (stages & ACE_STAGE_DOWN);
+    path &= ~(ACE_STAGE_GATEUP | ACE_STAGE_DOWN);
     if (path < ACE_PATH_AUTO || path > ACE_PATH_STREAM) return fail(ACE_EINVAL, "path=%d is not an ace_path", path);
     REQUIRE(h);
     REQUIRE(w_gate);
@@ -220,13 +225,16 @@ ace_status moe_expert_forward(const ace_moe_desc* d, int32_t path, const void* h
     gu.K = d->H;
     gu.N = d->I;
     gu.E = d->E;
+    gu.packed = d->weight_layout == ACE_LAYOUT_PACKED ? 1 : 0;
     hipError_t e;
     if (ev0) {
       e = hipEventRecord(ev0, s);
       if (e != hipSuccess) return hip_fail("hipEventRecord", e);
     }
-    e = ace::launch_expert(d->dtype, 0, stream_path, gu, d->T, d->k, ncu, s);
-    if (e != hipSuccess) return hip_fail("gate/up launch", e);
+    if (run_gu) {
+      e = ace::launch_expert(d->dtype, 0, stream_path, gu, d->T, d->k, ncu, s);
+      if (e != hipSuccess) return hip_fail("gate/up launch", e);
+    }
     if (ev1) {
       e = hipEventRecord(ev1, s);
       if (e != hipSuccess) return hip_fail("hipEventRecord", e);
@@ -238,8 +246,10 @@ ace_status moe_expert_forward(const ace_moe_desc* d, int32_t path, const void* h
     dn.out = slot_out;
     dn.K = d->I;
     dn.N = d->H;
-    e = ace::launch_expert(d->dtype, 1, stream_path, dn, d->T, d->k, ncu, s);
-    if (e != hipSuccess) return hip_fail("down launch", e);
+    if (run_dn) {
+      e = ace::launch_expert(d->dtype, 1, stream_path, dn, d->T, d->k, ncu, s);
+      if (e != hipSuccess) return hip_fail("down launch", e);
+    }
     return ok();
   } catch (...) {
     return fail(ACE_EHIP, "unexpected host exception in moe_expert_forward");
@@ -268,6 +278,73 @@ ace_status moe_combine(const ace_moe_desc* d, const int32_t* slot_pos, const flo
     return ok();
   } catch (...) {
     return fail(ACE_EHIP, "unexpected host exception in moe_combine");
+  }
+}
+
+size_t moe_calibrate_workspace_bytes(const ace_moe_desc* d) {
+  if (check_desc(d) != ACE_OK) return 0;
+  return std::max<size_t>(ace::calib_workspace_bytes(d->T, d->k), 256);
+}
+
+ace_status moe_calibrate_thresholds(const ace_moe_desc* d, const int32_t* topk_idx, const float* topk_gate,
+                                    const float* a_gsp, const float* a_rcr, float skip_rate, float* tau_out,
+                                    int32_t* level_out, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    ace_status st = check_desc(d);
+    if (st != ACE_OK) return st;
+    REQUIRE(topk_idx);
+    REQUIRE(topk_gate);
+    REQUIRE(a_gsp);
+    REQUIRE(a_rcr);
+    REQUIRE(tau_out);
+    REQUIRE(workspace);
+    const double max_rate = double(d->k - 1) / double(d->k);
+    if (!(skip_rate >= 0.f) || double(skip_rate) > max_rate + 1e-7)
+      return fail(ACE_EINVAL, "skip_rate=%g outside [0, (k-1)/k = %g]", double(skip_rate), max_rate);
+    const size_t need = std::max<size_t>(ace::calib_workspace_bytes(d->T, d->k), 256);
+    if (workspace_bytes < need)
+      return fail(ACE_EWORKSPACE, "workspace_bytes=%zu < %zu needed", workspace_bytes, need);
+    if (d->T == 0) return ok();
+    const int64_t slots = int64_t(d->T) * d->k;
+    const int64_t N = int64_t(d->T) * (d->k - 1);
+    int64_t n = int64_t(std::floor(double(skip_rate) * double(slots) + 0.5));
+    n = std::min(n, N);
+    ace::CalibArgs a{};
+    a.idx = topk_idx;
+    a.gate = topk_gate;
+    a.a_gsp = a_gsp;
+    a.a_rcr = a_rcr;
+    a.tau_out = tau_out;
+    a.level_out = level_out;
+    a.T = d->T;
+    a.k = d->k;
+    a.N = int(N);
+    a.n_target = int(n);
+    hipError_t e = ace::launch_calibrate(a, workspace, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("calibrate launch", e);
+    return ok();
+  } catch (...) {
+    return fail(ACE_EHIP, "unexpected host exception in moe_calibrate_thresholds");
+  }
+}
+
+ace_status moe_pack_weights(const ace_moe_desc* d, int32_t which, const void* src, void* dst, void* stream) {
+  try {
+    ace_status st = check_desc(d);
+    if (st != ACE_OK) return st;
+    if (which != 0 && which != 1) return fail(ACE_EINVAL, "which=%d must be 0 (gate/up) or 1 (down)", which);
+    REQUIRE(src);
+    REQUIRE(dst);
+    const int N = which == 0 ? d->I : d->H, K = which == 0 ? d->H : d->I;
+    const size_t bytes = size_t(d->E) * N * K * (d->dtype == ACE_BF16 ? 2 : 4);
+    const uint8_t* s0 = static_cast<const uint8_t*>(src);
+    const uint8_t* d0 = static_cast<const uint8_t*>(dst);
+    if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(ACE_EINVAL, "src and dst overlap");
+    hipError_t e = ace::launch_pack(d->dtype, src, dst, d->E, N, K, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("pack launch", e);
+    return ok();
+  } catch (...) {
+    return fail(ACE_EHIP, "unexpected host exception in moe_pack_weights");
   }
 }
 

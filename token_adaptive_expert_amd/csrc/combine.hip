@@ -9,7 +9,7 @@
 namespace ace {
 
 namespace {
-constexpr int NW = 4;
+constexpr int NTHR = 256;
 
 template <typename T> __device__ __forceinline__ f32x4 load4(const T* p);
 template <> __device__ __forceinline__ f32x4 load4<float>(const float* p) {
@@ -32,36 +32,51 @@ template <> __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, f32x4 v) {
 }
 }  // namespace
 
-template <typename T>
-__global__ __launch_bounds__(NW * 64) void combine_kernel(CombineArgs a) {
-  const int t = blockIdx.x * NW + wave_id();
-  if (t >= a.T) return;
-  const int l = lane_id(), H = a.H, k = a.k;
-  const T* res = reinterpret_cast<const T*>(a.residual);
-  T* y = reinterpret_cast<T*>(a.y);
-  for (int col = l * 4; col < H; col += 256) {
-    f32x4 acc = res ? load4<T>(res + int64_t(t) * H + col) : f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < k; ++i) {
-      const int p = a.slot_pos[int64_t(t) * k + i];
-      if (p >= 0) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(a.slot_out + int64_t(p) * H + col);
-        acc[0] += v[0];
-        acc[1] += v[1];
-        acc[2] += v[2];
-        acc[3] += v[3];
-      }
-    }
-    store4<T>(y + int64_t(t) * H + col, acc);
+// grid: (T, ceil(H / 1024)); each thread owns 4 columns of one token.  The
+// slot positions are read first (one scalar load), then every kept slot's
+// row is requested before the ordered sum, so the loads overlap.
+template <typename T, int KMAX>
+__global__ __launch_bounds__(NTHR) void combine_kernel(CombineArgs a) {
+  const int t = blockIdx.x;
+  const int col = (blockIdx.y * NTHR + threadIdx.x) * 4;
+  const int H = a.H, k = a.k;
+  if (col >= H) return;
+  const int32_t* sp = a.slot_pos + int64_t(t) * k;
+  int p[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) p[i] = sp[min(i, k - 1)];
+  f32x4 v[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) {
+    v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (i < k && p[i] >= 0) v[i] = *reinterpret_cast<const f32x4*>(a.slot_out + int64_t(p[i]) * H + col);
   }
+  const T* res = reinterpret_cast<const T*>(a.residual);
+  f32x4 acc = res ? load4<T>(res + int64_t(t) * H + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) {
+    acc[0] += v[i][0];
+    acc[1] += v[i][1];
+    acc[2] += v[i][2];
+    acc[3] += v[i][3];
+  }
+  store4<T>(reinterpret_cast<T*>(a.y) + int64_t(t) * H + col, acc);
+}
+
+template <typename T>
+hipError_t launch_combine_t(const CombineArgs& a, hipStream_t s) {
+  const dim3 grid(a.T, (a.H + NTHR * 4 - 1) / (NTHR * 4)), block(NTHR);
+  if (a.k <= 4)
+    hipLaunchKernelGGL((combine_kernel<T, 4>), grid, block, 0, s, a);
+  else if (a.k <= 8)
+    hipLaunchKernelGGL((combine_kernel<T, 8>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((combine_kernel<T, 16>), grid, block, 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(int dtype, const CombineArgs& a, hipStream_t s) {
-  const dim3 grid((a.T + NW - 1) / NW), block(NW * 64);
-  if (dtype == 1)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, s, a);
-  return hipGetLastError();
+  return dtype == 1 ? launch_combine_t<bf16_t>(a, s) : launch_combine_t<float>(a, s);
 }
 
 }  // namespace ace

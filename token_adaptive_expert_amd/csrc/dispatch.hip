@@ -1,15 +1,21 @@
-// Expert dispatch: group the kept (token, slot) pairs by expert, in token
-// order within each expert, with integer work only.
+// Expert dispatch: group the kept routed slots by expert, in token order
+// within each expert, with integer work only.
 //
 // The article page on ACE says only that surviving slots go through
 // "optimized expert dispatch"; this grouping is the layout the expert GEMMs
-// read.  One workgroup of 16 waves handles the whole batch in three phases:
-//   1. each 64-token chunk builds, per expert, the 64-bit mask of its tokens
-//      that kept that expert (LDS bitwise OR: order-independent) and counts it;
-//   2. per expert, chunk counts are prefix-summed into segment bases, and
-//      expert totals into expert_offsets;
-//   3. each kept slot's row = base[chunk][e] + popcount of the mask bits of
-//      lower tokens in its chunk.
+// read.  Slots are numbered s = t*k + i.  A token routes to k distinct
+// experts, so within one expert, slot order is token order.  One workgroup
+// of 16 waves handles the batch; wave w owns a contiguous run of 64-slot
+// chunks (so slot order is wave order, then chunk order, then lane order)
+// and every load is one coalesced 64-lane read.  Everything stays in LDS:
+//   1. each wave counts its kept slots per expert (LDS integer atomics:
+//      order-independent totals);
+//   2. expert totals -> expert_offsets (exclusive scan); per expert, the wave
+//      counts -> each wave's first row inside the expert's segment;
+//   3. each wave walks its chunks again in order: per chunk, the 64-bit mask
+//      of its lanes holding each expert (LDS bitwise OR); a kept slot's row is
+//      its wave's running row for that expert + the popcount of the mask bits
+//      of lower lanes.
 // Every result is a function of the inputs alone, independent of timing.
 #include "kernels.h"
 
@@ -19,103 +25,124 @@ namespace {
 constexpr int NW = 16;
 constexpr int NTHR = NW * 64;
 constexpr int EMAX = 256;
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+struct SlotVals {
+  int e;
+  int kept;
+  float g;
+};
+
+// Slot s of chunk c for this lane (index clamped so the load is always in
+// bounds; callers check s < nslots).
+__device__ __forceinline__ SlotVals load_slot(const DispatchArgs& a, int64_t s, int64_t nslots, bool with_gate) {
+  const int64_t sc = s < nslots ? s : nslots - 1;
+  SlotVals v;
+  v.e = a.idx[sc];
+  v.kept = a.keep[sc];
+  v.g = with_gate ? a.gate[sc] : 0.f;
+  return v;
+}
 }  // namespace
 
 __global__ __launch_bounds__(NTHR) void dispatch_kernel(DispatchArgs a) {
   __shared__ uint32_t s_bits[NW][EMAX][2];
-  __shared__ int32_t s_tot[EMAX];
+  __shared__ int32_t s_run[NW][EMAX];
+  __shared__ int32_t s_off[EMAX + 1];
+  __shared__ int32_t s_wsum[NTHR / 64];
   const int w = wave_id(), l = lane_id(), tid = threadIdx.x;
-  const int T = a.T, E = a.E, k = a.k;
-  const int nchunks = (T + 63) / 64;
-  const int iters = (nchunks + NW - 1) / NW;
+  const int E = a.E, k = a.k;
+  const int64_t nslots = int64_t(a.T) * k;
+  const int nchunks = int((nslots + 63) / 64);
+  const int cpw = (nchunks + NW - 1) / NW;
+  const int c0 = w * cpw, c1 = min(nchunks, c0 + cpw);
 
-  // phase 1: per-chunk expert masks and counts
-  for (int it = 0; it < iters; ++it) {
-    const int c = it * NW + w;
-    for (int e = l; e < E; e += 64) {
-      s_bits[w][e][0] = 0u;
-      s_bits[w][e][1] = 0u;
+  // 1. per-wave expert counts
+  for (int e = l; e < E; e += 64) s_run[w][e] = 0;
+  wave_sync_lds();
+  if (c0 < c1) {
+    SlotVals cur = load_slot(a, int64_t(c0) * 64 + l, nslots, false);
+    for (int c = c0; c < c1; ++c) {
+      const SlotVals nxt = load_slot(a, int64_t(min(c + 1, c1 - 1)) * 64 + l, nslots, false);
+      const int64_t s = int64_t(c) * 64 + l;
+      if (s < nslots && cur.kept && unsigned(cur.e) < unsigned(E)) atomicAdd(&s_run[w][cur.e], 1);
+      cur = nxt;
     }
-    __syncthreads();
-    if (c < nchunks) {
-      const int t = c * 64 + l;
-      if (t < T) {
-        for (int i = 0; i < k; ++i) {
-          const int64_t o = int64_t(t) * k + i;
-          const int e = a.idx[o];
-          if (a.keep[o] && unsigned(e) < unsigned(E)) atomicOr(&s_bits[w][e][l >> 5], 1u << (l & 31));
+  }
+  __syncthreads();
+
+  // 2. expert totals and exclusive scan over experts (thread e < E owns expert e)
+  int tot = 0;
+  if (tid < E) {
+    for (int ww = 0; ww < NW; ++ww) {
+      const int v = s_run[ww][tid];
+      s_run[ww][tid] = tot;  // exclusive prefix over waves, within the expert
+      tot += v;
+    }
+  }
+  int inc = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(inc, o, 64);
+    if (l >= o) inc += v;
+  }
+  if (l == 63) s_wsum[w] = inc;
+  __syncthreads();
+  if (tid < E) {
+    int base = 0;
+    for (int ww = 0; ww < w; ++ww) base += s_wsum[ww];
+    const int excl = base + inc - tot;
+    s_off[tid] = excl;
+    a.offsets[tid] = excl;
+    if (tid == E - 1) a.offsets[E] = excl + tot;
+  }
+  __syncthreads();
+  for (int e = l; e < E; e += 64) s_run[w][e] += s_off[e];
+  wave_sync_lds();
+
+  // 3. scatter, chunk by chunk in slot order
+  if (c0 < c1) {
+    const uint64_t below = (uint64_t(1) << l) - 1u;
+    SlotVals cur = load_slot(a, int64_t(c0) * 64 + l, nslots, true);
+    for (int c = c0; c < c1; ++c) {
+      const SlotVals nxt = load_slot(a, int64_t(min(c + 1, c1 - 1)) * 64 + l, nslots, true);
+      const int64_t s = int64_t(c) * 64 + l;
+      const bool live = s < nslots && cur.kept && unsigned(cur.e) < unsigned(E);
+      for (int e = l; e < E; e += 64) {
+        s_bits[w][e][0] = 0u;
+        s_bits[w][e][1] = 0u;
+      }
+      wave_sync_lds();
+      if (live) atomicOr(&s_bits[w][cur.e][l >> 5], 1u << (l & 31));
+      wave_sync_lds();
+      if (s < nslots) {
+        if (live) {
+          const uint64_t m = uint64_t(s_bits[w][cur.e][0]) | (uint64_t(s_bits[w][cur.e][1]) << 32);
+          const int pos = s_run[w][cur.e] + __popcll(m & below);
+          a.sorted_token[pos] = int(s / k);
+          a.sorted_gate[pos] = cur.g;
+          a.slot_pos[s] = pos;
+        } else {
+          a.slot_pos[s] = -1;
         }
       }
-    }
-    __syncthreads();
-    if (c < nchunks) {
-      for (int e = l; e < E; e += 64) {
-        const uint64_t m = uint64_t(s_bits[w][e][0]) | (uint64_t(s_bits[w][e][1]) << 32);
-        a.ws_mask[int64_t(c) * E + e] = m;
-        a.ws_cnt[int64_t(c) * E + e] = __popcll(m);
-      }
-    }
-    __syncthreads();
-  }
-  __threadfence();
-  __syncthreads();
-
-  // phase 2: expert totals, offsets, per-chunk segment bases
-  if (tid < E) {
-    int s = 0;
-    for (int c = 0; c < nchunks; ++c) s += a.ws_cnt[int64_t(c) * E + tid];
-    s_tot[tid] = s;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
-      const int v = s_tot[e];
-      s_tot[e] = run;
-      a.offsets[e] = run;
-      run += v;
-    }
-    a.offsets[E] = run;
-  }
-  __syncthreads();
-  if (tid < E) {
-    int run = s_tot[tid];
-    for (int c = 0; c < nchunks; ++c) {
-      const int64_t o = int64_t(c) * E + tid;
-      const int v = a.ws_cnt[o];
-      a.ws_cnt[o] = run;
-      run += v;
-    }
-  }
-  __threadfence();
-  __syncthreads();
-
-  // phase 3: scatter
-  for (int c = w; c < nchunks; c += NW) {
-    const int t = c * 64 + l;
-    if (t >= T) continue;
-    const uint64_t below = (uint64_t(1) << l) - 1u;
-    for (int i = 0; i < k; ++i) {
-      const int64_t o = int64_t(t) * k + i;
-      const int e = a.idx[o];
-      if (a.keep[o] && unsigned(e) < unsigned(E)) {
-        const int64_t ce = int64_t(c) * E + e;
-        const int pos = a.ws_cnt[ce] + __popcll(a.ws_mask[ce] & below);
-        a.sorted_token[pos] = t;
-        a.sorted_gate[pos] = a.gate[o];
-        a.slot_pos[o] = pos;
-      } else {
-        a.slot_pos[o] = -1;
-      }
+      wave_sync_lds();
+      for (int e = l; e < E; e += 64) s_run[w][e] += __popc(s_bits[w][e][0]) + __popc(s_bits[w][e][1]);
+      wave_sync_lds();
+      cur = nxt;
     }
   }
 }
 
 size_t dispatch_workspace_bytes(int T, int E) {
-  const size_t nchunks = (size_t(T) + 63) / 64;
-  const size_t cnt = nchunks * size_t(E) * sizeof(int32_t);
-  const size_t cnt_aligned = (cnt + 255) & ~size_t(255);
-  return cnt_aligned + nchunks * size_t(E) * sizeof(uint64_t);
+  (void)T;
+  (void)E;
+  return 256;
 }
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {

@@ -16,9 +16,9 @@
 //     ahead of the MFMAs;
 //   - the slot rows (gathered token rows of h, or act rows) are staged
 //     through LDS, double-buffered, and shared by all waves of the tile.
-// The grid is persistent: every workgroup derives the tile list from
-// expert_offsets (experts with no kept slot produce no tile, so their
-// weights are never read) and strides over it.
+// Every workgroup derives the tile list from expert_offsets (experts with no
+// kept slot produce no tile, so their weights are never read) and takes the
+// tile of its index.
 #include "kernels.h"
 
 namespace ace {
@@ -26,10 +26,11 @@ namespace ace {
 namespace {
 
 constexpr int ROWB = 256;        // bytes of one row per chunk
+constexpr int NXCD = 8;          // XCDs of an MI355X; only tile placement depends on it
 constexpr int LDS_PITCH = 272;   // padded row pitch in LDS (16 B pad: conflict-free fragment reads)
 
 template <typename T, int RB, int NW, int KIND>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 4 : 2)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void expert_gemm_kernel(ExpertArgs a) {
   constexpr int EPL = St<T>::EPL;
   constexpr int KS = 4 * EPL;      // k values per k-step
@@ -87,102 +88,122 @@ void expert_gemm_kernel(ExpertArgs a) {
   const int ntiles = total_mt * nb_count;
   const T* A = reinterpret_cast<const T*>(a.A);
 
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int mt = tile % total_mt;
-    const int nb = tile / total_mt;
-    // expert of this m-tile: last e with s_pref[e] <= mt
-    int lo = 0, hi = E;  // invariant: s_pref[lo] <= mt < s_pref[hi]
+  // Tile order: expert-major, then n-block, then the expert's m-tiles, so
+  // that tiles sharing slot rows (same m-tile) or weights (same n-block) are
+  // neighbours.  The list is cut into NXCD contiguous parts, one per XCD:
+  // workgroup id i runs on XCD i % NXCD (round-robin dispatch) and takes the
+  // (i / NXCD)-th tile of that XCD's part, so neighbours share one L2.
+  const int per_xcd = (ntiles + NXCD - 1) / NXCD;
+  for (int wg = blockIdx.x; wg < NXCD * per_xcd; wg += gridDim.x) {
+    const int g = (wg % NXCD) * per_xcd + wg / NXCD;
+    if (g >= ntiles) continue;
+    // expert of tile g: expert e owns tiles [nb_count*s_pref[e], nb_count*s_pref[e+1])
+    int lo = 0, hi = E;  // invariant: nb_count*s_pref[lo] <= g < nb_count*s_pref[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (s_pref[mid] <= mt) lo = mid; else hi = mid;
+      if (nb_count * s_pref[mid] <= g) lo = mid; else hi = mid;
     }
     const int e = lo;
-    const int row0 = s_off[e] + (mt - s_pref[e]) * BM;
+    const int mt_e = s_pref[e + 1] - s_pref[e];
+    const int local = g - nb_count * s_pref[e];
+    const int nb = local / mt_e;
+    const int mtl = local - nb * mt_e;
+    const int row0 = s_off[e] + mtl * BM;
     const int rows = min(BM, s_off[e + 1] - row0);
     const int nrb = (rows + 15) >> 4;
 
-    // weight row pointers of this lane's two groups
+    // this lane's weight fragment stream for each of its two 16-row groups:
+    // k-step j of group g is at wbase[g] + j * wstep.  Linear layout: row
+    // (n0 + l%16), k offset (l/16)*EPL.  Packed layout: fragment j of the
+    // group is one contiguous 1 KB block in lane order.
     const T* W0 = reinterpret_cast<const T*>(a.W0);
     const T* W1 = reinterpret_cast<const T*>(a.W1);
-    const T* wrow[2];
-    int col0;
-    if (KIND == 0) {
-      col0 = nb * ROWS_PER_WG + w * 16;
-      wrow[0] = W0 + (int64_t(e) * N + col0 + r16) * K + q * EPL;
-      wrow[1] = W1 + (int64_t(e) * N + col0 + r16) * K + q * EPL;
+    const int col0 = (KIND == 0) ? nb * ROWS_PER_WG + w * 16 : nb * ROWS_PER_WG + w * 32;
+    const int n0[2] = {col0, (KIND == 0) ? col0 : col0 + 16};
+    const T* wm[2] = {W0, (KIND == 0) ? W1 : W0};
+    const T* wbase[2];
+    int64_t wstep;
+    if (a.packed) {
+      const int64_t ksteps = K / KS;
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        wbase[g] = wm[g] + ((int64_t(e) * (N / 16) + n0[g] / 16) * ksteps) * (64 * EPL) + l * EPL;
+      wstep = 64 * EPL;
     } else {
-      col0 = nb * ROWS_PER_WG + w * 32;
-      wrow[0] = W0 + (int64_t(e) * N + col0 + r16) * K + q * EPL;
-      wrow[1] = W0 + (int64_t(e) * N + col0 + 16 + r16) * K + q * EPL;
+#pragma unroll
+      for (int g = 0; g < 2; ++g) wbase[g] = wm[g] + (int64_t(e) * N + n0[g] + r16) * K + q * EPL;
+      wstep = KS;
     }
 
-    // staged-row sources of this thread's units
+    // staged-row sources of this thread's units.  Rows past the tile's last
+    // slot row re-read that row: their MFMA output rows are never stored
+    // (an output row depends only on its own input row), and keeping every
+    // load unconditional keeps the loop body one schedulable block.
     const T* xsrc[UPT];
     int xoff[UPT];
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + u * NTHR;
+      const int unit = min(tid + u * NTHR, UNITS - 1);
       const int r = unit >> 4, seg = unit & 15;
       xoff[u] = r * LDS_PITCH + seg * 16;
-      xsrc[u] = nullptr;
-      if (unit < UNITS && r < rows) {
-        const int64_t src_row = (KIND == 0) ? int64_t(a.sorted_token[row0 + r]) : int64_t(row0 + r);
-        xsrc[u] = A + src_row * K + seg * EPL;
-      }
+      const int rr = min(r, rows - 1);
+      const int64_t src_row = (KIND == 0) ? int64_t(a.sorted_token[row0 + rr]) : int64_t(row0 + rr);
+      xsrc[u] = A + src_row * K + seg * EPL;
     }
 
     f32x4 acc[RB][2];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) acc[rb][0] = acc[rb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 wr[2][4], wn[2][4], xr[UPT];
-    // prologue: chunk 0
+    // weight chunks ride a three-stage register ring: while chunk c is
+    // multiplied, chunks c+1 and c+2 are in flight
+    u32x4 wA[2][4], wB[2][4], wC[2][4], xr[UPT];
+    auto load_w = [&](u32x4 (&dst)[2][4], int c) {
 #pragma unroll
-    for (int u = 0; u < UPT; ++u) xr[u] = xsrc[u] ? ld16(xsrc[u]) : u32x4{0u, 0u, 0u, 0u};
+      for (int g = 0; g < 2; ++g)
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+        for (int s = 0; s < 4; ++s) dst[g][s] = ld16(wbase[g] + (int64_t(c) * 4 + s) * wstep);
+    };
+    auto load_x = [&](int c) {
+      const int koff = c * KC;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) wr[g][s] = ld16(wrow[g] + s * KS);
+      for (int u = 0; u < UPT; ++u) xr[u] = ld16(xsrc[u] + koff);
+    };
+    auto store_x = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < UPT; ++u)
-      if (tid + u * NTHR < UNITS) *reinterpret_cast<u32x4*>(&s_x[0][xoff[u]]) = xr[u];
-    __syncthreads();
-
-    int buf = 0;
-    for (int c = 0; c < nch; ++c) {
-      const bool more = c + 1 < nch;
-      if (more) {
-        const int koff = (c + 1) * KC;
-#pragma unroll
-        for (int u = 0; u < UPT; ++u) xr[u] = xsrc[u] ? ld16(xsrc[u] + koff) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-#pragma unroll
-          for (int s = 0; s < 4; ++s) wn[g][s] = ld16(wrow[g] + koff + s * KS);
-      }
+      for (int u = 0; u < UPT; ++u)
+        if (UNITS % NTHR == 0 || tid + u * NTHR < UNITS) *reinterpret_cast<u32x4*>(&s_x[buf][xoff[u]]) = xr[u];
+    };
+    // One chunk.  Loads are issued X first, then weights: the X rows must land
+    // before the barrier, and the in-order completion counter then lets the
+    // weight loads of chunk c+2 stay in flight across it.
+    auto step = [&](u32x4 (&cur)[2][4], u32x4 (&nxt2)[2][4], int c) {
+      if (c + 1 < nch) load_x(c + 1);
+      if (c + 2 < nch) load_w(nxt2, c + 2);
+      const int buf = c & 1;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const u32x4 af =
               *reinterpret_cast<const u32x4*>(&s_x[buf][(rb * 16 + r16) * LDS_PITCH + s * 64 + q * 16]);
-          acc[rb][0] = mma_step<T>(af, wr[0][s], acc[rb][0]);
-          acc[rb][1] = mma_step<T>(af, wr[1][s], acc[rb][1]);
+          acc[rb][0] = mma_step<T>(af, cur[0][s], acc[rb][0]);
+          acc[rb][1] = mma_step<T>(af, cur[1][s], acc[rb][1]);
         }
       }
-      if (more) {
-#pragma unroll
-        for (int u = 0; u < UPT; ++u)
-          if (tid + u * NTHR < UNITS) *reinterpret_cast<u32x4*>(&s_x[buf ^ 1][xoff[u]]) = xr[u];
-      }
+      if (c + 1 < nch) store_x(buf ^ 1);
       __syncthreads();
-      if (more) {
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-#pragma unroll
-          for (int s = 0; s < 4; ++s) wr[g][s] = wn[g][s];
-      }
-      buf ^= 1;
+    };
+
+    load_x(0);
+    load_w(wA, 0);
+    if (nch > 1) load_w(wB, 1);
+    store_x(0);
+    __syncthreads();
+    for (int c = 0; c < nch; c += 3) {
+      step(wA, wC, c);
+      if (c + 1 < nch) step(wB, wA, c + 1);
+      if (c + 2 < nch) step(wC, wB, c + 2);
     }
 
     // epilogue
@@ -210,6 +231,27 @@ void expert_gemm_kernel(ExpertArgs a) {
   }
 }
 
+// Packed weight layout: [E][N/16][K/KS][64 lanes][16 bytes], where the
+// 16-byte unit of lane l in fragment (e, n-group, k-step j) holds row
+// n-group*16 + l%16, k values j*KS + (l/16)*EPL .. +EPL of the linear
+// [E][N][K] matrix.  One thread copies one 16-byte unit.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_weights_kernel(const T* __restrict__ src, T* __restrict__ dst, int64_t units,
+                                                           int N, int K) {
+  constexpr int EPL = St<T>::EPL;
+  constexpr int KS = 4 * EPL;
+  const int64_t u = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (u >= units) return;
+  const int l = int(u & 63);
+  const int64_t frag = u >> 6;
+  const int64_t ksteps = K / KS;
+  const int64_t j = frag % ksteps;
+  const int64_t rowgrp = frag / ksteps;  // e * (N/16) + n-group: rows of [E*N, K] in groups of 16
+  const int64_t row = rowgrp * 16 + (l & 15);
+  const int64_t k = j * KS + (l >> 4) * EPL;
+  st16(dst + u * EPL, ld16(src + row * K + k));
+}
+
 template <typename T, int RB, int NW, int KIND>
 hipError_t launch_one(const ExpertArgs& a, int ntok, int k, int num_cu, int wg_per_cu, hipStream_t s) {
   constexpr int BM = 16 * RB;
@@ -217,12 +259,31 @@ hipError_t launch_one(const ExpertArgs& a, int ntok, int k, int num_cu, int wg_p
   const int64_t slots = int64_t(ntok) * k;
   const int64_t mt_bound = (slots + BM - 1) / BM + std::min<int64_t>(a.E, slots);
   const int64_t tiles_bound = mt_bound * (a.N / ROWS_PER_WG);
-  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(tiles_bound, int64_t(num_cu) * wg_per_cu));
+  // one tile per workgroup: the grid covers the largest possible tile count
+  // and workgroups past the actual count exit at once; the hardware
+  // dispatcher then balances the tiles over the compute units.
+  (void)num_cu;
+  (void)wg_per_cu;
+  const int64_t grid = std::max<int64_t>(NXCD, std::min<int64_t>((tiles_bound + NXCD - 1) / NXCD * NXCD,
+                                                                   int64_t(1) << 30));
   hipLaunchKernelGGL((expert_gemm_kernel<T, RB, NW, KIND>), dim3(unsigned(grid)), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_pack(int dtype, const void* src, void* dst, int E, int N, int K, hipStream_t s) {
+  const int64_t bytes = int64_t(E) * N * K * (dtype == 1 ? 2 : 4);
+  const int64_t units = bytes / 16;
+  const dim3 grid(unsigned((units + 255) / 256)), block(256);
+  if (dtype == 1)
+    hipLaunchKernelGGL(pack_weights_kernel<bf16_t>, grid, block, 0, s, static_cast<const bf16_t*>(src),
+                       static_cast<bf16_t*>(dst), units, N, K);
+  else
+    hipLaunchKernelGGL(pack_weights_kernel<float>, grid, block, 0, s, static_cast<const float*>(src),
+                       static_cast<float*>(dst), units, N, K);
+  return hipGetLastError();
+}
 
 hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs& a, int T, int k, int num_cu,
                          hipStream_t s) {

@@ -31,8 +31,6 @@ struct DispatchArgs {
   int32_t* sorted_token;
   float* sorted_gate;
   int32_t* slot_pos;
-  int32_t* ws_cnt;     // [nchunks, E] counts, then segment bases
-  uint64_t* ws_mask;   // [nchunks, E] 64-token masks
   int T, E, k;
 };
 
@@ -47,6 +45,7 @@ struct ExpertArgs {
   int K;                      // contraction length: H (gate/up) or I (down)
   int N;                      // weight rows per expert: I (gate/up) or H (down)
   int E;
+  int packed;                 // weights in the packed fragment layout
 };
 
 struct CombineArgs {
@@ -57,8 +56,19 @@ struct CombineArgs {
   int T, H, k;
 };
 
-template <typename T> __global__ void route_skip_kernel(RouteArgs a);
-int route_tokens_per_block();
+struct CalibArgs {
+  const int32_t* idx;
+  const float* gate;
+  const float* a_gsp;
+  const float* a_rcr;
+  float* tau_out;       // [2]
+  int32_t* level_out;   // [2] (m, n) or null
+  int32_t* ws_rank_g;
+  int32_t* ws_rank_r;
+  float* ws_score_g;    // scores in ascending rank order
+  float* ws_score_r;
+  int T, k, N, n_target;
+};
 
 // Host launchers (return the launch status).
 hipError_t launch_route(int dtype, const RouteArgs& a, hipStream_t s);
@@ -68,5 +78,8 @@ size_t dispatch_workspace_bytes(int T, int E);
 hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs& a, int T, int k, int num_cu,
                          hipStream_t s);
 hipError_t launch_combine(int dtype, const CombineArgs& a, hipStream_t s);
+hipError_t launch_pack(int dtype, const void* src, void* dst, int E, int N, int K, hipStream_t s);
+size_t calib_workspace_bytes(int T, int k);
+hipError_t launch_calibrate(CalibArgs a, void* workspace, hipStream_t s);
 
 }  // namespace ace

@@ -1,4 +1,4 @@
-// RMSNorm + router + top-k gates + ACE skip mask, one workgroup per 16 tokens.
+// RMSNorm + router, then top-k gates + ACE skip mask (two kernels).
 //
 // Method: "ACE: Adaptive Calibration-Free Expert Skipping for MoE-based LLMs"
 // (picx.dev summary page).  h = x̄Γ is the RMSNorm output (Theoretical
@@ -11,19 +11,18 @@ namespace ace {
 
 namespace {
 
-constexpr int TB = 16;        // tokens per workgroup
+constexpr int TB = 16;        // tokens per workgroup (router kernel)
+constexpr int ECB = 32;       // experts per workgroup (router kernel)
 constexpr int NTHR = 256;     // 4 waves
 constexpr int EMAX = 256;
 
-// h for EPL consecutive hidden units of one token, rounded to the storage type.
-// The same function feeds h_out and the router's A operand, so both see the
-// same values.
-template <typename T> __device__ __forceinline__ u32x4 make_h(u32x4 xr, float inv, const float* gamma_k);
+// h for EPL consecutive hidden units of one token, rounded to the storage
+// type (gamma values passed in).  The same function feeds h_out and the
+// router's A operand, so both see the same values.
+template <typename T> __device__ __forceinline__ u32x4 make_h(u32x4 xr, float inv, const f32x4* g);
 
-template <> __device__ __forceinline__ u32x4 make_h<bf16_t>(u32x4 xr, float inv, const float* g) {
-  const f32x4 g0 = *reinterpret_cast<const f32x4*>(g);
-  const f32x4 g1 = *reinterpret_cast<const f32x4*>(g + 4);
-  float gg[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+template <> __device__ __forceinline__ u32x4 make_h<bf16_t>(u32x4 xr, float inv, const f32x4* g) {
+  float gg[8] = {g[0][0], g[0][1], g[0][2], g[0][3], g[1][0], g[1][1], g[1][2], g[1][3]};
   u32x4 out;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -34,46 +33,44 @@ template <> __device__ __forceinline__ u32x4 make_h<bf16_t>(u32x4 xr, float inv,
   return out;
 }
 
-template <> __device__ __forceinline__ u32x4 make_h<float>(u32x4 xr, float inv, const float* g) {
-  const f32x4 g0 = *reinterpret_cast<const f32x4*>(g);
+template <> __device__ __forceinline__ u32x4 make_h<float>(u32x4 xr, float inv, const f32x4* g) {
   u32x4 out;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) out[j] = __float_as_uint((__uint_as_float(xr[j]) * inv) * g0[j]);
+  for (int j = 0; j < 4; ++j) out[j] = __float_as_uint((__uint_as_float(xr[j]) * inv) * g[0][j]);
   return out;
 }
 
-template <typename T> __device__ __forceinline__ float sumsq16(u32x4 v);
-template <> __device__ __forceinline__ float sumsq16<bf16_t>(u32x4 v) {
-  float s = 0.f;
+// Operands of one router k-step for one lane: x (16 bytes), gamma, and the
+// float32 router weights of its two experts (8 values each for bf16 h, 4 for f32).
+template <typename T> struct RouterFrag {
+  static constexpr int EPL = St<T>::EPL;
+  static constexpr int NG = EPL / 4;  // float4 pieces per EPL values
+  u32x4 x;
+  f32x4 g[NG], w0[NG], w1[NG];
+  __device__ __forceinline__ void load_x(const T* xrow, const float* gamma, int k) {
+    x = ld16(xrow + k);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float a = bf16_to_f32(uint16_t(v[j] & 0xFFFFu)), b = bf16_to_f32(uint16_t(v[j] >> 16));
-    s += a * a;
-    s += b * b;
+    for (int i = 0; i < NG; ++i) g[i] = *reinterpret_cast<const f32x4*>(gamma + k + 4 * i);
   }
-  return s;
-}
-template <> __device__ __forceinline__ float sumsq16<float>(u32x4 v) {
-  float s = 0.f;
+  __device__ __forceinline__ void load(const T* xrow, const float* gamma, const float* r0, const float* r1, int k) {
+    load_x(xrow, gamma, k);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) s += __uint_as_float(v[j]) * __uint_as_float(v[j]);
-  return s;
-}
+    for (int i = 0; i < NG; ++i) {
+      w0[i] = *reinterpret_cast<const f32x4*>(r0 + k + 4 * i);
+      w1[i] = *reinterpret_cast<const f32x4*>(r1 + k + 4 * i);
+    }
+  }
+};
 
 // Router product for one 16-token x 16-expert block and one k-step.
 // bf16: each float32 router weight w is split exactly into three bf16 terms
 // (w = hi + mid + lo; 24 significant bits = 3 x 8), so the three bf16 MFMAs
 // form exact products of the bf16 h with the full float32 weight and
 // accumulate them in float32.
-template <typename T> __device__ __forceinline__ f32x4 router_step(u32x4 a, const float* wrow, bool ok, f32x4 acc);
+template <typename T> __device__ __forceinline__ f32x4 router_mma(u32x4 a, const f32x4* w, f32x4 acc);
 
-template <> __device__ __forceinline__ f32x4 router_step<bf16_t>(u32x4 a, const float* w, bool ok, f32x4 acc) {
-  f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = {0.f, 0.f, 0.f, 0.f};
-  if (ok) {
-    w0 = *reinterpret_cast<const f32x4*>(w);
-    w1 = *reinterpret_cast<const f32x4*>(w + 4);
-  }
-  float ww[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+template <> __device__ __forceinline__ f32x4 router_mma<bf16_t>(u32x4 a, const f32x4* w, f32x4 acc) {
+  float ww[8] = {w[0][0], w[0][1], w[0][2], w[0][3], w[1][0], w[1][1], w[1][2], w[1][3]};
   u32x4 hi, mid, lo;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -97,194 +94,240 @@ template <> __device__ __forceinline__ f32x4 router_step<bf16_t>(u32x4 a, const 
   return acc;
 }
 
-template <> __device__ __forceinline__ f32x4 router_step<float>(u32x4 a, const float* w, bool ok, f32x4 acc) {
-  u32x4 b = {0u, 0u, 0u, 0u};
-  if (ok) b = ld16(w);
-  return mma_step<float>(a, b, acc);
+template <> __device__ __forceinline__ f32x4 router_mma<float>(u32x4 a, const f32x4* w, f32x4 acc) {
+  return mma_step<float>(a, __builtin_bit_cast(u32x4, w[0]), acc);
+}
+
+template <typename T> __device__ __forceinline__ float sumsq16(u32x4 v);
+template <> __device__ __forceinline__ float sumsq16<bf16_t>(u32x4 v) {
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float a = bf16_to_f32(uint16_t(v[j] & 0xFFFFu)), b = bf16_to_f32(uint16_t(v[j] >> 16));
+    s += a * a;
+    s += b * b;
+  }
+  return s;
+}
+template <> __device__ __forceinline__ float sumsq16<float>(u32x4 v) {
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) s += __uint_as_float(v[j]) * __uint_as_float(v[j]);
+  return s;
 }
 
 }  // namespace
 
+// Kernel 1: RMSNorm (+ h_out) and the router product for 16 tokens x 32
+// experts.  The four waves split the hidden dimension; their partial logits
+// are summed in a fixed order, so the result does not depend on timing.
+// Loops issue the loads of step i+1 before the work of step i (explicit
+// software pipelining); token rows past T and expert rows past E read a
+// clamped valid row whose results are never stored.
 template <typename T>
-__global__ __launch_bounds__(NTHR) void route_skip_kernel(RouteArgs a) {
+__global__ __launch_bounds__(NTHR) void norm_router_kernel(RouteArgs a) {
   __shared__ float s_inv[TB];
-  __shared__ float s_logit[TB][EMAX + 1];
-  __shared__ double s_z[NTHR / 64][EMAX];
+  __shared__ float s_part[NTHR / 64][TB][ECB + 1];
 
   constexpr int EPL = St<T>::EPL;
+  constexpr int KS = 4 * EPL;
   const int w = wave_id(), l = lane_id();
   const int tok0 = blockIdx.x * TB;
-  const int H = a.H, E = a.E, k = a.k;
+  const int H = a.H, E = a.E;
   const T* x = reinterpret_cast<const T*>(a.x);
 
-  // 1. inverse RMS of each token (wave w: tokens 4w..4w+3)
-  for (int r = 0; r < 4; ++r) {
-    const int tl = w * 4 + r, t = tok0 + tl;
-    float ss = 0.f;
-    if (t < a.T) {
-      const T* row = x + int64_t(t) * H;
-      for (int j = l * EPL; j < H; j += 64 * EPL) ss += sumsq16<T>(ld16(row + j));
-    }
-    ss = wave_sum(ss);
-    if (l == 0) s_inv[tl] = 1.0f / sqrtf(ss / float(H) + a.eps);
-  }
-  __syncthreads();
-
-  // 2. h_out rows of this workgroup
+  // inverse RMS of each token (wave w: tokens 4w..4w+3)
   {
-    const int segs = H / EPL;  // 16-byte segments per row
-    for (int u = threadIdx.x; u < TB * segs; u += NTHR) {
-      const int tl = u / segs, j = (u % segs) * EPL, t = tok0 + tl;
-      if (t < a.T) {
-        const u32x4 hv = make_h<T>(ld16(x + int64_t(t) * H + j), s_inv[tl], a.gamma + j);
-        st16(reinterpret_cast<T*>(a.h_out) + int64_t(t) * H + j, hv);
-      }
-    }
-  }
-
-  // 3. logits into LDS
-  if (a.logits_in != nullptr) {
-    for (int u = threadIdx.x; u < TB * E; u += NTHR) {
-      const int tl = u / E, e = u % E, t = tok0 + tl;
-      s_logit[tl][e] = (t < a.T) ? a.logits_in[int64_t(t) * E + e] : 0.f;
-    }
-  } else {
-    const int ncb = (E + 15) / 16;  // 16-expert column blocks, round-robin over waves
-    const int q = l >> 4, r16 = l & 15;
-    const int t = tok0 + r16;
-    const bool tok_ok = t < a.T;
-    const float inv = s_inv[r16];
-    const T* xrow = x + int64_t(tok_ok ? t : 0) * H;
-    f32x4 acc[4];
+    const T* rows[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int kk = 0; kk < H; kk += 4 * EPL) {
-      const int kb = kk + q * EPL;
-      u32x4 af = {0u, 0u, 0u, 0u};
-      if (tok_ok) af = make_h<T>(ld16(xrow + kb), inv, a.gamma + kb);
+    for (int r = 0; r < 4; ++r) rows[r] = x + int64_t(min(tok0 + w * 4 + r, a.T - 1)) * H;
+    float ss[4] = {0.f, 0.f, 0.f, 0.f};
+    u32x4 cur[4], nxt[4];
+    const int step = 64 * EPL;
+    int j = l * EPL;
+    const int j0 = min(j, H - EPL);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int cb = w + 4 * c;
-        if (cb < ncb) {
-          const int e = cb * 16 + r16;
-          acc[c] = router_step<T>(af, a.w_router + int64_t(e < E ? e : 0) * H + kb, e < E, acc[c]);
-        }
+    for (int r = 0; r < 4; ++r) cur[r] = ld16(rows[r] + j0);
+    for (; j < H; j += step) {
+      const int jn = min(j + step, H - EPL);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) nxt[r] = ld16(rows[r] + jn);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ss[r] += sumsq16<T>(cur[r]);
+        cur[r] = nxt[r];
       }
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int cb = w + 4 * c;
-      const int e = cb * 16 + r16;
-      if (cb < ncb && e < E) {
-        const float b = a.bias ? a.bias[e] : 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) s_logit[4 * q + j][e] = acc[c][j] + b;
-      }
+    for (int r = 0; r < 4; ++r) {
+      const float v = wave_sum(ss[r]);
+      if (l == 0) s_inv[w * 4 + r] = 1.0f / sqrtf(v / float(H) + a.eps);
     }
   }
   __syncthreads();
 
-  if (a.logits_out != nullptr) {
-    for (int u = threadIdx.x; u < TB * E; u += NTHR) {
-      const int tl = u / E, e = u % E, t = tok0 + tl;
-      if (t < a.T) a.logits_out[int64_t(t) * E + e] = s_logit[tl][e];
+  const int q = l >> 4, r16 = l & 15;
+  const int tt = tok0 + r16;
+  const bool tok_ok = tt < a.T;
+  const int t = min(tt, a.T - 1);
+  const float inv = s_inv[r16];
+  const T* xrow = x + int64_t(t) * H;
+  T* hrow = reinterpret_cast<T*>(a.h_out) + int64_t(t) * H;
+  const bool write_h = blockIdx.y == 0 && tok_ok;
+  const bool do_router = a.logits_in == nullptr;
+  const int e0 = min(blockIdx.y * ECB + r16, E - 1), e1 = min(blockIdx.y * ECB + 16 + r16, E - 1);
+  const float* w0 = a.w_router + int64_t(e0) * H;
+  const float* w1 = a.w_router + int64_t(e1) * H;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  // the four waves split the hidden dimension: each wave's quarter also
+  // writes that quarter of h_out (blockIdx.y == 0 only)
+  const int kq = H / 4;
+  const int kbeg = w * kq, kend = kbeg + kq;
+  if (do_router) {
+    RouterFrag<T> cur, nxt;
+    cur.load(xrow, a.gamma, w0, w1, kbeg + q * EPL);
+    for (int kk = kbeg; kk < kend; kk += KS) {
+      nxt.load(xrow, a.gamma, w0, w1, min(kk + KS, kend - KS) + q * EPL);
+      const u32x4 af = make_h<T>(cur.x, inv, cur.g);
+      if (write_h) st16(hrow + kk + q * EPL, af);
+      acc0 = router_mma<T>(af, cur.w0, acc0);
+      acc1 = router_mma<T>(af, cur.w1, acc1);
+      cur = nxt;
+    }
+  } else if (blockIdx.y == 0) {
+    RouterFrag<T> cur, nxt;
+    cur.load_x(xrow, a.gamma, kbeg + q * EPL);
+    for (int kk = kbeg; kk < kend; kk += KS) {
+      nxt.load_x(xrow, a.gamma, min(kk + KS, kend - KS) + q * EPL);
+      if (write_h) st16(hrow + kk + q * EPL, make_h<T>(cur.x, inv, cur.g));
+      cur = nxt;
     }
   }
-
-  // 4. top-k, gates, skip mask: one wave per token
-  const int R = (E + 63) / 64;
-  for (int r = 0; r < 4; ++r) {
-    const int tl = w * 4 + r, t = tok0 + tl;
-    if (t >= a.T) break;
-    float v[4];
+  if (!do_router) return;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int e = l + 64 * rr;
-      v[rr] = (rr < R && e < E) ? s_logit[tl][e] : 0.f;
-    }
-    uint32_t taken = 0;
-    int my_e = 0;
-    float my_logit = 0.f, top_logit = 0.f;
-    for (int i = 0; i < k; ++i) {
-      float bv = -INFINITY;
-      int bi = 0x7FFFFFFF;
+  for (int j = 0; j < 4; ++j) {
+    s_part[w][4 * q + j][r16] = acc0[j];
+    s_part[w][4 * q + j][16 + r16] = acc1[j];
+  }
+  __syncthreads();
+  for (int u = threadIdx.x; u < TB * ECB; u += NTHR) {
+    const int tl = u / ECB, c = u % ECB, e = blockIdx.y * ECB + c, to = tok0 + tl;
+    if (to < a.T && e < E) {
+      float v = s_part[0][tl][c];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int e = l + 64 * rr;
-        if (rr < R && e < E && !((taken >> rr) & 1u)) {
-          if (v[rr] > bv || (v[rr] == bv && e < bi)) {
-            bv = v[rr];
-            bi = e;
-          }
-        }
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if ((bi & 63) == l) taken |= 1u << (bi >> 6);
-      if (l == i) {
-        my_e = bi;
-        my_logit = bv;
-      }
-      if (i == 0) top_logit = bv;
-    }
-    // softmax in float64, shifted by the top-1 logit
-    const double m = double(top_logit);
-    const double z = (l < k) ? exp(double(my_logit) - m) : 0.0;
-    double s = 0.0;
-    if (a.norm_topk) {
-      for (int i = 0; i < k; ++i) s += __shfl(z, i, 64);
-    } else {
-      for (int e = l; e < E; e += 64) s_z[w][e] = exp(double(s_logit[tl][e]) - m);
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      for (int e = 0; e < E; ++e) s += s_z[w][e];
-      __builtin_amdgcn_wave_barrier();
-    }
-    if (l < k) {
-      const float g = float(z / s);
-      bool keep = true;
-      if (l > 0) {
-        const float sg = g * a.a_gsp[my_e];
-        const float sr = g * a.a_rcr[my_e];
-        const bool lg = sg < a.tau_gsp, lr = sr < a.tau_rcr;
-        bool skip;
-        switch (a.fusion) {
-          case 1: skip = lg || lr; break;
-          case 2:
-            skip = a.tau_gsp > 0.f && a.tau_rcr > 0.f &&
-                   0.5 * (double(sg) / double(a.tau_gsp) + double(sr) / double(a.tau_rcr)) < 1.0;
-            break;
-          case 3: skip = lg; break;
-          case 4: skip = lr; break;
-          case 5: skip = g < a.tau_gsp; break;
-          default: skip = lg && lr; break;
-        }
-        keep = !skip;
-      }
-      const int64_t o = int64_t(t) * k + l;
-      a.topk_idx[o] = my_e;
-      a.topk_gate[o] = g;
-      a.keep[o] = keep ? 1 : 0;
+      for (int ww = 1; ww < NTHR / 64; ++ww) v += s_part[ww][tl][c];
+      if (a.bias) v += a.bias[e];
+      a.logits_out[int64_t(to) * E + e] = v;
     }
   }
 }
 
-int route_tokens_per_block() { return TB; }
+// Kernel 2: top-k, gates and skip mask, one wave per token.
+__global__ __launch_bounds__(NTHR) void topk_skip_kernel(RouteArgs a) {
+  __shared__ double s_z[NTHR / 64][EMAX];
+  const int w = wave_id(), l = lane_id();
+  const int t = blockIdx.x * (NTHR / 64) + w;
+  if (t >= a.T) return;
+  const int E = a.E, k = a.k;
+  const float* lrow = (a.logits_in ? a.logits_in : a.logits_out) + int64_t(t) * E;
+  const int R = (E + 63) / 64;
+  float v[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int e = l + 64 * rr;
+    v[rr] = (rr < R && e < E) ? lrow[e] : 0.f;
+  }
+  if (a.logits_in != nullptr) {
+    float* orow = a.logits_out + int64_t(t) * E;
+    for (int rr = 0; rr < R; ++rr)
+      if (l + 64 * rr < E) orow[l + 64 * rr] = v[rr];
+  }
+  uint32_t taken = 0;
+  int my_e = 0;
+  float my_logit = 0.f, top_logit = 0.f;
+  for (int i = 0; i < k; ++i) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int e = l + 64 * rr;
+      if (rr < R && e < E && !((taken >> rr) & 1u)) {
+        if (v[rr] > bv || (v[rr] == bv && e < bi)) {
+          bv = v[rr];
+          bi = e;
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == l) taken |= 1u << (bi >> 6);
+    if (l == i) {
+      my_e = bi;
+      my_logit = bv;
+    }
+    if (i == 0) top_logit = bv;
+  }
+  // softmax in float64, shifted by the top-1 logit; sums in ascending order
+  const double m = double(top_logit);
+  const double z = (l < k) ? exp(double(my_logit) - m) : 0.0;
+  double s = 0.0;
+  if (a.norm_topk) {
+    for (int i = 0; i < k; ++i) s += __shfl(z, i, 64);
+  } else {
+    for (int rr = 0; rr < R; ++rr) {
+      const int e = l + 64 * rr;
+      if (e < E) s_z[w][e] = exp(double(v[rr]) - m);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int e = 0; e < E; ++e) s += s_z[w][e];
+  }
+  if (l < k) {
+    const float g = float(z / s);
+    bool keep = true;
+    if (l > 0) {
+      const float sg = g * a.a_gsp[my_e];
+      const float sr = g * a.a_rcr[my_e];
+      const bool lg = sg < a.tau_gsp, lr = sr < a.tau_rcr;
+      bool skip;
+      switch (a.fusion) {
+        case 1: skip = lg || lr; break;
+        case 2:
+          skip = a.tau_gsp > 0.f && a.tau_rcr > 0.f &&
+                 0.5 * (double(sg) / double(a.tau_gsp) + double(sr) / double(a.tau_rcr)) < 1.0;
+          break;
+        case 3: skip = lg; break;
+        case 4: skip = lr; break;
+        case 5: skip = g < a.tau_gsp; break;
+        default: skip = lg && lr; break;
+      }
+      keep = !skip;
+    }
+    const int64_t o = int64_t(t) * k + l;
+    a.topk_idx[o] = my_e;
+    a.topk_gate[o] = g;
+    a.keep[o] = keep ? 1 : 0;
+  }
+}
 
 hipError_t launch_route(int dtype, const RouteArgs& a, hipStream_t s) {
-  const dim3 grid((a.T + TB - 1) / TB), block(NTHR);
+  const dim3 grid1((a.T + TB - 1) / TB, a.logits_in ? 1 : (a.E + ECB - 1) / ECB), block(NTHR);
   if (dtype == 1)
-    hipLaunchKernelGGL(route_skip_kernel<bf16_t>, grid, block, 0, s, a);
+    hipLaunchKernelGGL(norm_router_kernel<bf16_t>, grid1, block, 0, s, a);
   else
-    hipLaunchKernelGGL(route_skip_kernel<float>, grid, block, 0, s, a);
+    hipLaunchKernelGGL(norm_router_kernel<float>, grid1, block, 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid2((a.T + NTHR / 64 - 1) / (NTHR / 64));
+  hipLaunchKernelGGL(topk_skip_kernel, grid2, block, 0, s, a);
   return hipGetLastError();
 }
 

@@ -66,26 +66,41 @@ class AceMoeLayer:
     a_gsp/a_rcr [E] f32 tables."""
 
     def __init__(self, gamma, w_router, router_bias, w_gate, w_up, w_down, a_gsp, a_rcr, k, norm_topk=1,
-                 fusion="max", rms_eps=1e-6):
+                 fusion="max", rms_eps=1e-6, weight_layout=_lib.ACE_LAYOUT_LINEAR):
         self.gamma, self.w_router, self.router_bias = gamma, w_router, router_bias
         self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
         self.a_gsp, self.a_rcr = a_gsp, a_rcr
         self.E, self.I, self.H = w_gate.shape
         self.k, self.norm_topk, self.fusion, self.rms_eps = int(k), int(norm_topk), fusion, float(rms_eps)
         self.dtype = w_gate.dtype
+        self.weight_layout = int(weight_layout)
 
     def desc(self, T: int):
-        return _lib.make_desc(T, self.H, self.E, self.I, self.k, self.dtype, self.norm_topk, self.fusion, self.rms_eps)
+        return _lib.make_desc(T, self.H, self.E, self.I, self.k, self.dtype, self.norm_topk, self.fusion, self.rms_eps,
+                              self.weight_layout)
+
+    def packed(self, stream=None) -> "AceMoeLayer":
+        """The same layer with its expert weights copied into the packed layout
+        (moe_pack_weights); the tensors keep their shapes."""
+        if self.weight_layout == _lib.ACE_LAYOUT_PACKED:
+            return self
+        d = self.desc(1)
+        out = []
+        for which, w in ((0, self.w_gate), (0, self.w_up), (1, self.w_down)):
+            p = torch.empty_like(w)
+            _lib.moe_pack_weights(d, which, w, p, stream)
+            out.append(p)
+        return AceMoeLayer(self.gamma, self.w_router, self.router_bias, out[0], out[1], out[2], self.a_gsp, self.a_rcr,
+                           self.k, self.norm_topk, self.fusion, self.rms_eps, _lib.ACE_LAYOUT_PACKED)
 
     def buffers(self, T: int) -> LayerBuffers:
         return LayerBuffers.allocate(T, self.H, self.E, self.I, self.k, self.dtype, self.w_gate.device)
 
-    def route(self, x, tau_gsp, tau_rcr, b: LayerBuffers, logits_in=None, want_logits=True, stream=None):
+    def route(self, x, tau_gsp, tau_rcr, b: LayerBuffers, logits_in=None, stream=None):
         T = x.shape[0]
         d = self.desc(T)
-        _lib.moe_route_skip(d, x, self.gamma, self.w_router, self.router_bias, logits_in,
-                            b.logits if want_logits else None, self.a_gsp, self.a_rcr, tau_gsp, tau_rcr, b.h,
-                            b.topk_idx, b.topk_gate, b.keep, stream)
+        _lib.moe_route_skip(d, x, self.gamma, self.w_router, self.router_bias, logits_in, b.logits, self.a_gsp,
+                            self.a_rcr, tau_gsp, tau_rcr, b.h, b.topk_idx, b.topk_gate, b.keep, stream)
 
     def dispatch(self, T: int, b: LayerBuffers, stream=None):
         _lib.moe_dispatch(self.desc(T), b.topk_idx, b.topk_gate, b.keep, b.offsets, b.sorted_token, b.sorted_gate,
@@ -99,13 +114,13 @@ class AceMoeLayer:
         _lib.moe_combine(self.desc(T), b.slot_pos, b.slot_out, residual, b.y, stream)
 
     def forward(self, x, tau_gsp, tau_rcr, b: LayerBuffers | None = None, path=_lib.ACE_PATH_AUTO, logits_in=None,
-                want_logits=True, residual=None, stream=None) -> torch.Tensor:
+                residual=None, stream=None) -> torch.Tensor:
         T = x.shape[0]
         if b is None:
             b = self.buffers(T)
         if b.T < T:
             raise ValueError(f"buffers sized for {b.T} tokens, got {T}")
-        self.route(x, tau_gsp, tau_rcr, b, logits_in, want_logits, stream)
+        self.route(x, tau_gsp, tau_rcr, b, logits_in, stream)
         self.dispatch(T, b, stream)
         self.experts(T, b, path, stream)
         self.combine(T, b, residual, stream)
