@@ -27,7 +27,9 @@
  *   - T = 0 is a valid empty batch: the call returns ACE_OK and launches
  *     nothing.
  *   - Limits: 1 <= k <= min(E, 16); 1 <= E <= 256; H and I multiples of 128;
- *     T * k < 2^31.  Outside them: ACE_EUNSUPPORTED.
+ *     one expert's matrix (H*I elements) and the slot activations
+ *     (T*k*max(H, I) elements) each under 2 GiB.  Outside them:
+ *     ACE_EUNSUPPORTED.
  *   - Calls on one stream run in order; calls that share output or workspace
  *     buffers must not run concurrently on different streams.
  */
@@ -101,9 +103,9 @@ typedef struct {
 int moe_abi_version(void);
 const char* moe_last_error(void);
 
-/* Bytes of scratch that moe_dispatch needs (per-chunk counts, token masks).
- * The same workspace may then be passed to moe_expert_forward, which needs
- * none today.  Returns 0 for an invalid descriptor. */
+/* Bytes of device workspace that moe_dispatch and moe_expert_forward need
+ * (both take one; they may share it).  Calls sharing a workspace must not
+ * overlap.  Returns 0 for an invalid descriptor. */
 size_t moe_workspace_bytes(const ace_moe_desc* d);
 
 /*
@@ -155,6 +157,7 @@ ace_status moe_dispatch(const ace_moe_desc* d, const int32_t* topk_idx, const fl
  * one kept slot have their weights read.
  * In:  h [T,H] dtype (from moe_route_skip); weights as above.
  * Out: act [T*k, I] dtype (scratch rows); slot_out [T*k, H] f32.
+ * workspace: >= moe_workspace_bytes(d) bytes.
  */
 ace_status moe_expert_forward(const ace_moe_desc* d, int32_t path, const void* h, const void* w_gate,
                               const void* w_up, const void* w_down, const int32_t* expert_offsets,

@@ -105,7 +105,7 @@ def test_empty_batch_is_a_no_op():
     f = 0x1000
     assert lib.moe_route_skip(ctypes.byref(d), f, f, f, None, None, f, f, f, 0.0, 0.0, f, f, f, f, None) == 0
     assert lib.moe_dispatch(ctypes.byref(d), f, f, f, f, f, f, f, f, 1 << 20, None) == 0
-    assert lib.moe_expert_forward(ctypes.byref(d), 0, f, f, f, f, f, f, f, f, f, None, 0, None) == 0
+    assert lib.moe_expert_forward(ctypes.byref(d), 0, f, f, f, f, f, f, f, f, f, f, 1 << 20, None) == 0
     assert lib.moe_combine(ctypes.byref(d), f, f, None, f, None) == 0
     assert lib.moe_last_error().decode() == ""
 
@@ -114,7 +114,10 @@ def test_bad_path_and_events():
     m, lib = _lib()
     d = m.make_desc(4, 256, 16, 128, 4, "f32")
     f = 0x1000
-    assert lib.moe_expert_forward(ctypes.byref(d), 5, f, f, f, f, f, f, f, f, f, None, 0, None) == 1
+    assert lib.moe_expert_forward(ctypes.byref(d), 5, f, f, f, f, f, f, f, f, f, f, 1 << 20, None) == 1
+    assert lib.moe_expert_forward(ctypes.byref(d), 0, f, f, f, f, f, f, f, f, f, None, 1 << 20, None) == 1
+    assert "workspace" in lib.moe_last_error().decode()
+    assert lib.moe_expert_forward(ctypes.byref(d), 0, f, f, f, f, f, f, f, f, f, f, 16, None) == 3
     assert lib.moe_set_kernel_events(f, None) == 1
     assert lib.moe_set_kernel_events(None, None) == 0
 

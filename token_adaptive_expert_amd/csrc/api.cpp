@@ -73,7 +73,13 @@ ace_status check_desc(const ace_moe_desc* d) {
   if (d->H % 128 != 0) return fail(ACE_EUNSUPPORTED, "H=%d is not a multiple of 128", d->H);
   if (d->I % 128 != 0) return fail(ACE_EUNSUPPORTED, "I=%d is not a multiple of 128", d->I);
   if (int64_t(d->T) * d->k >= (int64_t(1) << 31)) return fail(ACE_EUNSUPPORTED, "T*k >= 2^31");
-  if (int64_t(d->T) * d->H >= (int64_t(1) << 40)) return fail(ACE_EUNSUPPORTED, "T*H too large");
+  {
+    const int64_t es = d->dtype == ACE_BF16 ? 2 : 4;
+    const int64_t lim = (int64_t(1) << 31) - 1;
+    if (int64_t(d->H) * d->I * es > lim) return fail(ACE_EUNSUPPORTED, "H*I too large for one expert");
+    if (int64_t(d->T) * d->k * std::max(d->H, d->I) * es > lim)
+      return fail(ACE_EUNSUPPORTED, "T*k*max(H,I) activations exceed 2 GiB");
+  }
   return ACE_OK;
 }
 
@@ -202,8 +208,10 @@ ace_status moe_expert_forward(const ace_moe_desc* d, int32_t path, const void* h
     REQUIRE(sorted_gate);
     REQUIRE(act);
     REQUIRE(slot_out);
-    (void)workspace;
-    (void)workspace_bytes;
+    REQUIRE(workspace);
+    if (workspace_bytes < ace::dispatch_workspace_bytes(d->T, d->E))
+      return fail(ACE_EWORKSPACE, "workspace_bytes=%zu < %zu needed", workspace_bytes,
+                  ace::dispatch_workspace_bytes(d->T, d->E));
     if (d->T == 0) return ok();
     int ncu = 0;
     st = num_cu(&ncu);
@@ -226,6 +234,7 @@ ace_status moe_expert_forward(const ace_moe_desc* d, int32_t path, const void* h
     gu.N = d->I;
     gu.E = d->E;
     gu.packed = d->weight_layout == ACE_LAYOUT_PACKED ? 1 : 0;
+    gu.A_rows = d->T;
     hipError_t e;
     if (ev0) {
       e = hipEventRecord(ev0, s);
@@ -246,6 +255,7 @@ ace_status moe_expert_forward(const ace_moe_desc* d, int32_t path, const void* h
     dn.out = slot_out;
     dn.K = d->I;
     dn.N = d->H;
+    dn.A_rows = d->T * d->k;
     if (run_dn) {
       e = ace::launch_expert(d->dtype, 1, stream_path, dn, d->T, d->k, ncu, s);
       if (e != hipSuccess) return hip_fail("down launch", e);

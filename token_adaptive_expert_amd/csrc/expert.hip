@@ -25,12 +25,26 @@ namespace ace {
 
 namespace {
 
+// Tuning knobs (compile-time; the defaults are the measured best on MI355X).
+#ifndef ACE_GROUPED_RB
+#define ACE_GROUPED_RB 4      // 16-row blocks of slot rows per grouped tile
+#endif
+#ifndef ACE_GROUPED_STAGES
+#define ACE_GROUPED_STAGES 2  // depth of the weight register ring (grouped tiles)
+#endif
+#ifndef ACE_WAVES_PER_EU
+#define ACE_WAVES_PER_EU 3    // occupancy target given to the register allocator
+#endif
+#ifndef ACE_LDS_PITCH
+#define ACE_LDS_PITCH 272     // padded LDS row pitch of the staged slot rows
+#endif
+
 constexpr int ROWB = 256;        // bytes of one row per chunk
 constexpr int NXCD = 8;          // XCDs of an MI355X; only tile placement depends on it
-constexpr int LDS_PITCH = 272;   // padded row pitch in LDS (16 B pad: conflict-free fragment reads)
+constexpr int LDS_PITCH = ACE_LDS_PITCH;
 
-template <typename T, int RB, int NW, int KIND>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+template <typename T, int RB, int NW, int KIND, int STAGES>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ACE_WAVES_PER_EU)))
 void expert_gemm_kernel(ExpertArgs a) {
   constexpr int EPL = St<T>::EPL;
   constexpr int KS = 4 * EPL;      // k values per k-step
@@ -92,7 +106,9 @@ void expert_gemm_kernel(ExpertArgs a) {
   // that tiles sharing slot rows (same m-tile) or weights (same n-block) are
   // neighbours.  The list is cut into NXCD contiguous parts, one per XCD:
   // workgroup id i runs on XCD i % NXCD (round-robin dispatch) and takes the
-  // (i / NXCD)-th tile of that XCD's part, so neighbours share one L2.
+  // (i / NXCD)-th tile of that XCD's part, so neighbours share one L2.  One
+  // tile per workgroup; the hardware dispatcher refills a compute unit as soon
+  // as one of its tiles finishes, which balances uneven per-CU bandwidth.
   const int per_xcd = (ntiles + NXCD - 1) / NXCD;
   for (int wg = blockIdx.x; wg < NXCD * per_xcd; wg += gridDim.x) {
     const int g = (wg % NXCD) * per_xcd + wg / NXCD;
@@ -112,34 +128,40 @@ void expert_gemm_kernel(ExpertArgs a) {
     const int rows = min(BM, s_off[e + 1] - row0);
     const int nrb = (rows + 15) >> 4;
 
-    // this lane's weight fragment stream for each of its two 16-row groups:
-    // k-step j of group g is at wbase[g] + j * wstep.  Linear layout: row
-    // (n0 + l%16), k offset (l/16)*EPL.  Packed layout: fragment j of the
-    // group is one contiguous 1 KB block in lane order.
-    const T* W0 = reinterpret_cast<const T*>(a.W0);
-    const T* W1 = reinterpret_cast<const T*>(a.W1);
-    const int col0 = (KIND == 0) ? nb * ROWS_PER_WG + w * 16 : nb * ROWS_PER_WG + w * 32;
+    // Weights are read with buffer loads: the expert's matrix base lives in a
+    // scalar resource descriptor, the lane part of the address is one 32-bit
+    // register and the k-step part a scalar offset.  k-step j of group g is at
+    // byte wv + ws[g] + j * wstep.  Linear layout: row n0 + l%16, k offset
+    // (l/16)*EPL.  Packed layout: fragment j of the group is one contiguous
+    // 1 KB block in lane order.  Both 16-row groups of a wave are uniform.
+    const int col0 = __builtin_amdgcn_readfirstlane((KIND == 0) ? nb * ROWS_PER_WG + w * 16
+                                                                : nb * ROWS_PER_WG + w * 32);
     const int n0[2] = {col0, (KIND == 0) ? col0 : col0 + 16};
-    const T* wm[2] = {W0, (KIND == 0) ? W1 : W0};
-    const T* wbase[2];
-    int64_t wstep;
+    const int64_t ebytes = int64_t(N) * K * int(sizeof(T));  // one expert's matrix
+    const char* wm0 = reinterpret_cast<const char*>(a.W0) + int64_t(e) * ebytes;
+    const char* wm1 = reinterpret_cast<const char*>((KIND == 0) ? a.W1 : a.W0) + int64_t(e) * ebytes;
+    const __amdgpu_buffer_rsrc_t wr0 = make_rsrc(wm0, uint32_t(ebytes));
+    const __amdgpu_buffer_rsrc_t wr1 = make_rsrc(wm1, uint32_t(ebytes));
+    int wv, ws[2], wstep;
     if (a.packed) {
-      const int64_t ksteps = K / KS;
+      const int ksteps = K / KS;
+      wv = l * 16;
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
-        wbase[g] = wm[g] + ((int64_t(e) * (N / 16) + n0[g] / 16) * ksteps) * (64 * EPL) + l * EPL;
-      wstep = 64 * EPL;
+      for (int g = 0; g < 2; ++g) ws[g] = (n0[g] / 16) * ksteps * 1024;
+      wstep = 1024;
     } else {
+      wv = (r16 * K + q * EPL) * int(sizeof(T));
 #pragma unroll
-      for (int g = 0; g < 2; ++g) wbase[g] = wm[g] + (int64_t(e) * N + n0[g] + r16) * K + q * EPL;
-      wstep = KS;
+      for (int g = 0; g < 2; ++g) ws[g] = n0[g] * K * int(sizeof(T));
+      wstep = KS * int(sizeof(T));
     }
 
-    // staged-row sources of this thread's units.  Rows past the tile's last
-    // slot row re-read that row: their MFMA output rows are never stored
-    // (an output row depends only on its own input row), and keeping every
-    // load unconditional keeps the loop body one schedulable block.
-    const T* xsrc[UPT];
+    // staged-row sources of this thread's units (byte offsets into A).  Rows
+    // past the tile's last slot row re-read that row: their MFMA output rows
+    // are never stored (an output row depends only on its own input row), and
+    // keeping every load unconditional keeps the loop body one block.
+    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.A, uint32_t(int64_t(a.A_rows) * K * int(sizeof(T))));
+    int xsrc[UPT];
     int xoff[UPT];
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
@@ -147,27 +169,28 @@ void expert_gemm_kernel(ExpertArgs a) {
       const int r = unit >> 4, seg = unit & 15;
       xoff[u] = r * LDS_PITCH + seg * 16;
       const int rr = min(r, rows - 1);
-      const int64_t src_row = (KIND == 0) ? int64_t(a.sorted_token[row0 + rr]) : int64_t(row0 + rr);
-      xsrc[u] = A + src_row * K + seg * EPL;
+      const int src_row = (KIND == 0) ? a.sorted_token[row0 + rr] : row0 + rr;
+      xsrc[u] = src_row * K * int(sizeof(T)) + seg * 16;
     }
 
     f32x4 acc[RB][2];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) acc[rb][0] = acc[rb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // weight chunks ride a three-stage register ring: while chunk c is
-    // multiplied, chunks c+1 and c+2 are in flight
+    // weight chunks ride a register ring of STAGES chunks: while chunk c is
+    // multiplied, the next STAGES-1 chunks are in flight
     u32x4 wA[2][4], wB[2][4], wC[2][4], xr[UPT];
     auto load_w = [&](u32x4 (&dst)[2][4], int c) {
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) dst[g][s] = ld16(wbase[g] + (int64_t(c) * 4 + s) * wstep);
+      for (int s = 0; s < 4; ++s) {
+        dst[0][s] = buf_ld16(wr0, wv, ws[0] + (c * 4 + s) * wstep);
+        dst[1][s] = buf_ld16(wr1, wv, ws[1] + (c * 4 + s) * wstep);
+      }
     };
     auto load_x = [&](int c) {
-      const int koff = c * KC;
+      const int koff = c * KC * int(sizeof(T));
 #pragma unroll
-      for (int u = 0; u < UPT; ++u) xr[u] = ld16(xsrc[u] + koff);
+      for (int u = 0; u < UPT; ++u) xr[u] = buf_ld16(xrs, xsrc[u], koff);
     };
     auto store_x = [&](int buf) {
 #pragma unroll
@@ -176,10 +199,10 @@ void expert_gemm_kernel(ExpertArgs a) {
     };
     // One chunk.  Loads are issued X first, then weights: the X rows must land
     // before the barrier, and the in-order completion counter then lets the
-    // weight loads of chunk c+2 stay in flight across it.
-    auto step = [&](u32x4 (&cur)[2][4], u32x4 (&nxt2)[2][4], int c) {
+    // weight loads of the later chunk stay in flight across it.
+    auto step = [&](u32x4 (&cur)[2][4], u32x4 (&ahead)[2][4], int c) {
       if (c + 1 < nch) load_x(c + 1);
-      if (c + 2 < nch) load_w(nxt2, c + 2);
+      if (c + STAGES - 1 < nch) load_w(ahead, c + STAGES - 1);
       const int buf = c & 1;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -197,13 +220,20 @@ void expert_gemm_kernel(ExpertArgs a) {
 
     load_x(0);
     load_w(wA, 0);
-    if (nch > 1) load_w(wB, 1);
+    if (STAGES == 3 && nch > 1) load_w(wB, 1);
     store_x(0);
     __syncthreads();
-    for (int c = 0; c < nch; c += 3) {
-      step(wA, wC, c);
-      if (c + 1 < nch) step(wB, wA, c + 1);
-      if (c + 2 < nch) step(wC, wB, c + 2);
+    if constexpr (STAGES == 3) {
+      for (int c = 0; c < nch; c += 3) {
+        step(wA, wC, c);
+        if (c + 1 < nch) step(wB, wA, c + 1);
+        if (c + 2 < nch) step(wC, wB, c + 2);
+      }
+    } else {
+      for (int c = 0; c < nch; c += 2) {
+        step(wA, wB, c);
+        if (c + 1 < nch) step(wB, wA, c + 1);
+      }
     }
 
     // epilogue
@@ -252,21 +282,18 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const T* __restrict__
   st16(dst + u * EPL, ld16(src + row * K + k));
 }
 
-template <typename T, int RB, int NW, int KIND>
-hipError_t launch_one(const ExpertArgs& a, int ntok, int k, int num_cu, int wg_per_cu, hipStream_t s) {
+template <typename T, int RB, int NW, int KIND, int STAGES>
+hipError_t launch_one(const ExpertArgs& a, int ntok, int k, hipStream_t s) {
   constexpr int BM = 16 * RB;
   constexpr int ROWS_PER_WG = (KIND == 0) ? NW * 16 : NW * 32;
   const int64_t slots = int64_t(ntok) * k;
   const int64_t mt_bound = (slots + BM - 1) / BM + std::min<int64_t>(a.E, slots);
   const int64_t tiles_bound = mt_bound * (a.N / ROWS_PER_WG);
-  // one tile per workgroup: the grid covers the largest possible tile count
-  // and workgroups past the actual count exit at once; the hardware
-  // dispatcher then balances the tiles over the compute units.
-  (void)num_cu;
-  (void)wg_per_cu;
+  // the grid covers the largest possible tile count (a multiple of NXCD);
+  // workgroups past the actual count exit at once
   const int64_t grid = std::max<int64_t>(NXCD, std::min<int64_t>((tiles_bound + NXCD - 1) / NXCD * NXCD,
                                                                    int64_t(1) << 30));
-  hipLaunchKernelGGL((expert_gemm_kernel<T, RB, NW, KIND>), dim3(unsigned(grid)), dim3(NW * 64), 0, s, a);
+  hipLaunchKernelGGL((expert_gemm_kernel<T, RB, NW, KIND, STAGES>), dim3(unsigned(grid)), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -287,18 +314,20 @@ hipError_t launch_pack(int dtype, const void* src, void* dst, int E, int N, int 
 
 hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs& a, int T, int k, int num_cu,
                          hipStream_t s) {
+  constexpr int G = ACE_GROUPED_RB, S = ACE_GROUPED_STAGES;
+  (void)num_cu;
   if (dtype == 1) {
     if (stream_path)
-      return kind == 0 ? launch_one<bf16_t, 1, 2, 0>(a, T, k, num_cu, 8, s)
-                       : launch_one<bf16_t, 1, 2, 1>(a, T, k, num_cu, 8, s);
-    return kind == 0 ? launch_one<bf16_t, 4, 4, 0>(a, T, k, num_cu, 2, s)
-                     : launch_one<bf16_t, 4, 4, 1>(a, T, k, num_cu, 2, s);
+      return kind == 0 ? launch_one<bf16_t, 1, 2, 0, 3>(a, T, k, s)
+                       : launch_one<bf16_t, 1, 2, 1, 3>(a, T, k, s);
+    return kind == 0 ? launch_one<bf16_t, G, 4, 0, S>(a, T, k, s)
+                     : launch_one<bf16_t, G, 4, 1, S>(a, T, k, s);
   }
   if (stream_path)
-    return kind == 0 ? launch_one<float, 1, 2, 0>(a, T, k, num_cu, 8, s)
-                     : launch_one<float, 1, 2, 1>(a, T, k, num_cu, 8, s);
-  return kind == 0 ? launch_one<float, 4, 4, 0>(a, T, k, num_cu, 2, s)
-                   : launch_one<float, 4, 4, 1>(a, T, k, num_cu, 2, s);
+    return kind == 0 ? launch_one<float, 1, 2, 0, 3>(a, T, k, s)
+                     : launch_one<float, 1, 2, 1, 3>(a, T, k, s);
+  return kind == 0 ? launch_one<float, G, 4, 0, S>(a, T, k, s)
+                   : launch_one<float, G, 4, 1, S>(a, T, k, s);
 }
 
 }  // namespace ace

@@ -46,6 +46,7 @@ struct ExpertArgs {
   int N;                      // weight rows per expert: I (gate/up) or H (down)
   int E;
   int packed;                 // weights in the packed fragment layout
+  int A_rows;                 // rows of A: T (gate/up) or T*k (down)
 };
 
 struct CombineArgs {

@@ -13,7 +13,9 @@ namespace {
 
 constexpr int TB = 16;        // tokens per workgroup (router kernel)
 constexpr int ECB = 32;       // experts per workgroup (router kernel)
-constexpr int NTHR = 256;     // 4 waves
+constexpr int RW = 16;        // waves of the router kernel (split the hidden dimension)
+constexpr int RNTHR = RW * 64;
+constexpr int NTHR = 256;     // 4 waves (top-k kernel)
 constexpr int EMAX = 256;
 
 // h for EPL consecutive hidden units of one token, rounded to the storage
@@ -119,15 +121,15 @@ template <> __device__ __forceinline__ float sumsq16<float>(u32x4 v) {
 }  // namespace
 
 // Kernel 1: RMSNorm (+ h_out) and the router product for 16 tokens x 32
-// experts.  The four waves split the hidden dimension; their partial logits
-// are summed in a fixed order, so the result does not depend on timing.
-// Loops issue the loads of step i+1 before the work of step i (explicit
-// software pipelining); token rows past T and expert rows past E read a
-// clamped valid row whose results are never stored.
+// experts.  Sixteen waves split the hidden dimension: wave w takes k-steps
+// w, w+16, w+32, ...  Their partial logits are summed in a fixed wave order,
+// so the result does not depend on timing.  Loads are issued for two
+// k-steps before either is used; token rows past T and expert rows past E
+// read a clamped valid row whose results are never stored.
 template <typename T>
-__global__ __launch_bounds__(NTHR) void norm_router_kernel(RouteArgs a) {
+__global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
   __shared__ float s_inv[TB];
-  __shared__ float s_part[NTHR / 64][TB][ECB + 1];
+  __shared__ float s_part[RW][TB][ECB + 1];
 
   constexpr int EPL = St<T>::EPL;
   constexpr int KS = 4 * EPL;
@@ -136,71 +138,64 @@ __global__ __launch_bounds__(NTHR) void norm_router_kernel(RouteArgs a) {
   const int H = a.H, E = a.E;
   const T* x = reinterpret_cast<const T*>(a.x);
 
-  // inverse RMS of each token (wave w: tokens 4w..4w+3)
+  // inverse RMS: wave w owns token tok0 + w; a row is read 8 segments of
+  // 64 lanes x 16 bytes at a time, all in flight together
   {
-    const T* rows[4];
+    const T* row = x + int64_t(min(tok0 + w, a.T - 1)) * H;
+    constexpr int SEG = 64 * EPL;
+    float ss = 0.f;
+    for (int j0 = 0; j0 < H; j0 += 8 * SEG) {
+      u32x4 v[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) rows[r] = x + int64_t(min(tok0 + w * 4 + r, a.T - 1)) * H;
-    float ss[4] = {0.f, 0.f, 0.f, 0.f};
-    u32x4 cur[4], nxt[4];
-    const int step = 64 * EPL;
-    int j = l * EPL;
-    const int j0 = min(j, H - EPL);
+      for (int b = 0; b < 8; ++b) v[b] = ld16(row + min(j0 + b * SEG + l * EPL, H - EPL));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) cur[r] = ld16(rows[r] + j0);
-    for (; j < H; j += step) {
-      const int jn = min(j + step, H - EPL);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) nxt[r] = ld16(rows[r] + jn);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        ss[r] += sumsq16<T>(cur[r]);
-        cur[r] = nxt[r];
-      }
+      for (int b = 0; b < 8; ++b)
+        if (j0 + b * SEG + l * EPL < H) ss += sumsq16<T>(v[b]);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float v = wave_sum(ss[r]);
-      if (l == 0) s_inv[w * 4 + r] = 1.0f / sqrtf(v / float(H) + a.eps);
-    }
+    ss = wave_sum(ss);
+    if (l == 0) s_inv[w] = 1.0f / sqrtf(ss / float(H) + a.eps);
   }
   __syncthreads();
 
   const int q = l >> 4, r16 = l & 15;
   const int tt = tok0 + r16;
-  const bool tok_ok = tt < a.T;
   const int t = min(tt, a.T - 1);
   const float inv = s_inv[r16];
   const T* xrow = x + int64_t(t) * H;
   T* hrow = reinterpret_cast<T*>(a.h_out) + int64_t(t) * H;
-  const bool write_h = blockIdx.y == 0 && tok_ok;
+  const bool write_h = blockIdx.y == 0 && tt < a.T;
   const bool do_router = a.logits_in == nullptr;
   const int e0 = min(blockIdx.y * ECB + r16, E - 1), e1 = min(blockIdx.y * ECB + 16 + r16, E - 1);
   const float* w0 = a.w_router + int64_t(e0) * H;
   const float* w1 = a.w_router + int64_t(e1) * H;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  // the four waves split the hidden dimension: each wave's quarter also
-  // writes that quarter of h_out (blockIdx.y == 0 only)
-  const int kq = H / 4;
-  const int kbeg = w * kq, kend = kbeg + kq;
-  if (do_router) {
-    RouterFrag<T> cur, nxt;
-    cur.load(xrow, a.gamma, w0, w1, kbeg + q * EPL);
-    for (int kk = kbeg; kk < kend; kk += KS) {
-      nxt.load(xrow, a.gamma, w0, w1, min(kk + KS, kend - KS) + q * EPL);
-      const u32x4 af = make_h<T>(cur.x, inv, cur.g);
-      if (write_h) st16(hrow + kk + q * EPL, af);
-      acc0 = router_mma<T>(af, cur.w0, acc0);
-      acc1 = router_mma<T>(af, cur.w1, acc1);
-      cur = nxt;
-    }
-  } else if (blockIdx.y == 0) {
-    RouterFrag<T> cur, nxt;
-    cur.load_x(xrow, a.gamma, kbeg + q * EPL);
-    for (int kk = kbeg; kk < kend; kk += KS) {
-      nxt.load_x(xrow, a.gamma, min(kk + KS, kend - KS) + q * EPL);
-      if (write_h) st16(hrow + kk + q * EPL, make_h<T>(cur.x, inv, cur.g));
-      cur = nxt;
+  const int nks = H / KS;
+  if (do_router || blockIdx.y == 0) {
+    for (int j0 = w; j0 < nks; j0 += 2 * RW) {
+      const int j1 = j0 + RW;
+      const int k0 = j0 * KS + q * EPL, k1 = min(j1, nks - 1) * KS + q * EPL;
+      RouterFrag<T> f0, f1;
+      if (do_router) {
+        f0.load(xrow, a.gamma, w0, w1, k0);
+        f1.load(xrow, a.gamma, w0, w1, k1);
+      } else {
+        f0.load_x(xrow, a.gamma, k0);
+        f1.load_x(xrow, a.gamma, k1);
+      }
+      const u32x4 h0 = make_h<T>(f0.x, inv, f0.g);
+      if (write_h) st16(hrow + k0, h0);
+      if (do_router) {
+        acc0 = router_mma<T>(h0, f0.w0, acc0);
+        acc1 = router_mma<T>(h0, f0.w1, acc1);
+      }
+      if (j1 < nks) {
+        const u32x4 h1 = make_h<T>(f1.x, inv, f1.g);
+        if (write_h) st16(hrow + k1, h1);
+        if (do_router) {
+          acc0 = router_mma<T>(h1, f1.w0, acc0);
+          acc1 = router_mma<T>(h1, f1.w1, acc1);
+        }
+      }
     }
   }
   if (!do_router) return;
@@ -210,12 +205,12 @@ __global__ __launch_bounds__(NTHR) void norm_router_kernel(RouteArgs a) {
     s_part[w][4 * q + j][16 + r16] = acc1[j];
   }
   __syncthreads();
-  for (int u = threadIdx.x; u < TB * ECB; u += NTHR) {
+  for (int u = threadIdx.x; u < TB * ECB; u += RNTHR) {
     const int tl = u / ECB, c = u % ECB, e = blockIdx.y * ECB + c, to = tok0 + tl;
     if (to < a.T && e < E) {
       float v = s_part[0][tl][c];
 #pragma unroll
-      for (int ww = 1; ww < NTHR / 64; ++ww) v += s_part[ww][tl][c];
+      for (int ww = 1; ww < RW; ++ww) v += s_part[ww][tl][c];
       if (a.bias) v += a.bias[e];
       a.logits_out[int64_t(to) * E + e] = v;
     }
@@ -231,11 +226,15 @@ __global__ __launch_bounds__(NTHR) void topk_skip_kernel(RouteArgs a) {
   const int E = a.E, k = a.k;
   const float* lrow = (a.logits_in ? a.logits_in : a.logits_out) + int64_t(t) * E;
   const int R = (E + 63) / 64;
-  float v[4];
+  // lane l holds experts l, l+64, ...: logits and both tables, loaded together
+  // (indices clamped so every load is in bounds)
+  float v[4], tg[4], tr[4];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
-    const int e = l + 64 * rr;
-    v[rr] = (rr < R && e < E) ? lrow[e] : 0.f;
+    const int e = min(l + 64 * rr, E - 1);
+    v[rr] = lrow[e];
+    tg[rr] = a.a_gsp[e];
+    tr[rr] = a.a_rcr[e];
   }
   if (a.logits_in != nullptr) {
     float* orow = a.logits_out + int64_t(t) * E;
@@ -290,12 +289,22 @@ __global__ __launch_bounds__(NTHR) void topk_skip_kernel(RouteArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     for (int e = 0; e < E; ++e) s += s_z[w][e];
   }
+  // table values of this lane's selected expert, from the lane that owns it
+  float ag = 0.f, ar = 0.f;
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const float gq = __shfl(tg[rr], my_e & 63, 64), rq = __shfl(tr[rr], my_e & 63, 64);
+    if ((my_e >> 6) == rr) {
+      ag = gq;
+      ar = rq;
+    }
+  }
   if (l < k) {
     const float g = float(z / s);
     bool keep = true;
     if (l > 0) {
-      const float sg = g * a.a_gsp[my_e];
-      const float sr = g * a.a_rcr[my_e];
+      const float sg = g * ag;
+      const float sr = g * ar;
       const bool lg = sg < a.tau_gsp, lr = sr < a.tau_rcr;
       bool skip;
       switch (a.fusion) {
@@ -319,11 +328,11 @@ __global__ __launch_bounds__(NTHR) void topk_skip_kernel(RouteArgs a) {
 }
 
 hipError_t launch_route(int dtype, const RouteArgs& a, hipStream_t s) {
-  const dim3 grid1((a.T + TB - 1) / TB, a.logits_in ? 1 : (a.E + ECB - 1) / ECB), block(NTHR);
+  const dim3 grid1((a.T + TB - 1) / TB, a.logits_in ? 1 : (a.E + ECB - 1) / ECB), block1(RNTHR), block(NTHR);
   if (dtype == 1)
-    hipLaunchKernelGGL(norm_router_kernel<bf16_t>, grid1, block, 0, s, a);
+    hipLaunchKernelGGL(norm_router_kernel<bf16_t>, grid1, block1, 0, s, a);
   else
-    hipLaunchKernelGGL(norm_router_kernel<float>, grid1, block, 0, s, a);
+    hipLaunchKernelGGL(norm_router_kernel<float>, grid1, block1, 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid2((a.T + NTHR / 64 - 1) / (NTHR / 64));
