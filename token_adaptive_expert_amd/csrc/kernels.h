@@ -21,6 +21,7 @@ struct RouteArgs {
   uint8_t* keep;
   int T, H, E, k, norm_topk, fusion;
   float eps;
+  int router_packed;  // w_router holds the pre-split bf16 planes (bf16 activations only)
 };
 
 struct DispatchArgs {
@@ -79,6 +80,8 @@ size_t dispatch_workspace_bytes(int T, int E);
 hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs& a, int T, int k, int num_cu,
                          hipStream_t s);
 hipError_t launch_combine(int dtype, const CombineArgs& a, hipStream_t s);
+size_t router_packed_bytes(int E, int H);
+hipError_t launch_pack_router(const float* w, void* dst, int E, int H, hipStream_t s);
 hipError_t launch_pack(int dtype, const void* src, void* dst, int E, int N, int K, hipStream_t s);
 size_t calib_workspace_bytes(int T, int k);
 hipError_t launch_calibrate(CalibArgs a, void* workspace, hipStream_t s);

@@ -71,9 +71,10 @@ template <typename T> struct RouterFrag {
 // accumulate them in float32.
 template <typename T> __device__ __forceinline__ f32x4 router_mma(u32x4 a, const f32x4* w, f32x4 acc);
 
-template <> __device__ __forceinline__ f32x4 router_mma<bf16_t>(u32x4 a, const f32x4* w, f32x4 acc) {
+// Exact three-term bf16 split of 8 float32 values: w = hi + mid + lo (each
+// term rounded to nearest even; the residuals are exact in float32).
+__device__ __forceinline__ void split3(const f32x4* w, u32x4* planes) {
   float ww[8] = {w[0][0], w[0][1], w[0][2], w[0][3], w[1][0], w[1][1], w[1][2], w[1][3]};
-  u32x4 hi, mid, lo;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     uint16_t h2[2], m2[2], l2[2];
@@ -86,14 +87,23 @@ template <> __device__ __forceinline__ f32x4 router_mma<bf16_t>(u32x4 a, const f
       const float r2 = r1 - bf16_to_f32(m2[p]);
       l2[p] = f32_to_bf16(r2);
     }
-    hi[j] = uint32_t(h2[0]) | (uint32_t(h2[1]) << 16);
-    mid[j] = uint32_t(m2[0]) | (uint32_t(m2[1]) << 16);
-    lo[j] = uint32_t(l2[0]) | (uint32_t(l2[1]) << 16);
+    planes[0][j] = uint32_t(h2[0]) | (uint32_t(h2[1]) << 16);
+    planes[1][j] = uint32_t(m2[0]) | (uint32_t(m2[1]) << 16);
+    planes[2][j] = uint32_t(l2[0]) | (uint32_t(l2[1]) << 16);
   }
-  acc = mfma_bf16(a, hi, acc);
-  acc = mfma_bf16(a, mid, acc);
-  acc = mfma_bf16(a, lo, acc);
+}
+
+__device__ __forceinline__ f32x4 mma3(u32x4 a, const u32x4* planes, f32x4 acc) {
+  acc = mfma_bf16(a, planes[0], acc);
+  acc = mfma_bf16(a, planes[1], acc);
+  acc = mfma_bf16(a, planes[2], acc);
   return acc;
+}
+
+template <> __device__ __forceinline__ f32x4 router_mma<bf16_t>(u32x4 a, const f32x4* w, f32x4 acc) {
+  u32x4 planes[3];
+  split3(w, planes);
+  return mma3(a, planes, acc);
 }
 
 template <> __device__ __forceinline__ f32x4 router_mma<float>(u32x4 a, const f32x4* w, f32x4 acc) {
@@ -170,6 +180,43 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
   const float* w1 = a.w_router + int64_t(e1) * H;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   const int nks = H / KS;
+  if constexpr (sizeof(T) == 2) {
+    if (do_router && a.router_packed) {
+      // pre-split planes: [3][CB][nks][64][16 B]; this workgroup's two
+      // 16-expert column blocks
+      const int CB = (E + 15) / 16;
+      const int cb0 = min(int(blockIdx.y) * 2, CB - 1), cb1 = min(int(blockIdx.y) * 2 + 1, CB - 1);
+      const uint8_t* wp = reinterpret_cast<const uint8_t*>(a.w_router);
+      const int64_t plane_bytes = int64_t(CB) * nks * 1024;
+      auto ldp = [&](int cb, int j, u32x4* out) {
+#pragma unroll
+        for (int p = 0; p < 3; ++p) out[p] = ld16(wp + p * plane_bytes + (int64_t(cb) * nks + j) * 1024 + l * 16);
+      };
+      for (int j0 = w; j0 < nks; j0 += 2 * RW) {
+        const int j1 = min(j0 + RW, nks - 1);
+        const int k0 = j0 * KS + q * EPL, k1 = j1 * KS + q * EPL;
+        RouterFrag<T> f0, f1;
+        u32x4 p00[3], p01[3], p10[3], p11[3];
+        f0.load_x(xrow, a.gamma, k0);
+        f1.load_x(xrow, a.gamma, k1);
+        ldp(cb0, j0, p00);
+        ldp(cb1, j0, p01);
+        ldp(cb0, j1, p10);
+        ldp(cb1, j1, p11);
+        const u32x4 h0 = make_h<T>(f0.x, inv, f0.g);
+        if (write_h) st16(hrow + k0, h0);
+        acc0 = mma3(h0, p00, acc0);
+        acc1 = mma3(h0, p01, acc1);
+        if (j0 + RW < nks) {
+          const u32x4 h1 = make_h<T>(f1.x, inv, f1.g);
+          if (write_h) st16(hrow + k1, h1);
+          acc0 = mma3(h1, p10, acc0);
+          acc1 = mma3(h1, p11, acc1);
+        }
+      }
+      goto reduce;
+    }
+  }
   if (do_router || blockIdx.y == 0) {
     for (int j0 = w; j0 < nks; j0 += 2 * RW) {
       const int j1 = j0 + RW;
@@ -199,6 +246,7 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
     }
   }
   if (!do_router) return;
+reduce:
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     s_part[w][4 * q + j][r16] = acc0[j];
@@ -325,6 +373,40 @@ __global__ __launch_bounds__(NTHR) void topk_skip_kernel(RouteArgs a) {
     a.topk_gate[o] = g;
     a.keep[o] = keep ? 1 : 0;
   }
+}
+
+// Router pre-split for bf16 activations: [3 planes][CB][H/32][64 lanes][8 bf16];
+// the unit of lane l in (plane p, column block cb, k-step j) holds plane p of
+// w_router[16*cb + l%16][32*j + 8*(l/16) .. +8] (zero for experts >= E).
+__global__ __launch_bounds__(256) void pack_router_kernel(const float* __restrict__ w, uint8_t* __restrict__ dst,
+                                                          int E, int H) {
+  const int nks = H / 32, CB = (E + 15) / 16;
+  const int64_t units = int64_t(CB) * nks * 64;
+  const int64_t u = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (u >= units) return;
+  const int l = int(u & 63);
+  const int64_t frag = u >> 6;
+  const int j = int(frag % nks), cb = int(frag / nks);
+  const int e = cb * 16 + (l & 15), k = j * 32 + (l >> 4) * 8;
+  f32x4 v[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  if (e < E) {
+    v[0] = *reinterpret_cast<const f32x4*>(w + int64_t(e) * H + k);
+    v[1] = *reinterpret_cast<const f32x4*>(w + int64_t(e) * H + k + 4);
+  }
+  u32x4 planes[3];
+  split3(v, planes);
+  const int64_t plane_bytes = units * 16;
+#pragma unroll
+  for (int p = 0; p < 3; ++p) st16(dst + p * plane_bytes + u * 16, planes[p]);
+}
+
+size_t router_packed_bytes(int E, int H) { return size_t(3) * ((E + 15) / 16) * 16 * size_t(H) * 2; }
+
+hipError_t launch_pack_router(const float* w, void* dst, int E, int H, hipStream_t s) {
+  const int64_t units = int64_t((E + 15) / 16) * (H / 32) * 64;
+  hipLaunchKernelGGL(pack_router_kernel, dim3(unsigned((units + 255) / 256)), dim3(256), 0, s, w,
+                     static_cast<uint8_t*>(dst), E, H);
+  return hipGetLastError();
 }
 
 hipError_t launch_route(int dtype, const RouteArgs& a, hipStream_t s) {

@@ -66,7 +66,8 @@ class AceMoeLayer:
     a_gsp/a_rcr [E] f32 tables."""
 
     def __init__(self, gamma, w_router, router_bias, w_gate, w_up, w_down, a_gsp, a_rcr, k, norm_topk=1,
-                 fusion="max", rms_eps=1e-6, weight_layout=_lib.ACE_LAYOUT_LINEAR):
+                 fusion="max", rms_eps=1e-6, weight_layout=_lib.ACE_LAYOUT_LINEAR,
+                 router_layout=_lib.ACE_LAYOUT_LINEAR, H=None):
         self.gamma, self.w_router, self.router_bias = gamma, w_router, router_bias
         self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
         self.a_gsp, self.a_rcr = a_gsp, a_rcr
@@ -74,24 +75,31 @@ class AceMoeLayer:
         self.k, self.norm_topk, self.fusion, self.rms_eps = int(k), int(norm_topk), fusion, float(rms_eps)
         self.dtype = w_gate.dtype
         self.weight_layout = int(weight_layout)
+        self.router_layout = int(router_layout)
 
     def desc(self, T: int):
         return _lib.make_desc(T, self.H, self.E, self.I, self.k, self.dtype, self.norm_topk, self.fusion, self.rms_eps,
-                              self.weight_layout)
+                              self.weight_layout, self.router_layout)
 
-    def packed(self, stream=None) -> "AceMoeLayer":
+    def packed(self, stream=None, router=True) -> "AceMoeLayer":
         """The same layer with its expert weights copied into the packed layout
-        (moe_pack_weights); the tensors keep their shapes."""
-        if self.weight_layout == _lib.ACE_LAYOUT_PACKED:
-            return self
+        (moe_pack_weights; the tensors keep their shapes) and, for bf16
+        layers when ``router`` is set, the router pre-split (moe_pack_router)."""
         d = self.desc(1)
-        out = []
-        for which, w in ((0, self.w_gate), (0, self.w_up), (1, self.w_down)):
-            p = torch.empty_like(w)
-            _lib.moe_pack_weights(d, which, w, p, stream)
-            out.append(p)
-        return AceMoeLayer(self.gamma, self.w_router, self.router_bias, out[0], out[1], out[2], self.a_gsp, self.a_rcr,
-                           self.k, self.norm_topk, self.fusion, self.rms_eps, _lib.ACE_LAYOUT_PACKED)
+        out = [self.w_gate, self.w_up, self.w_down]
+        if self.weight_layout != _lib.ACE_LAYOUT_PACKED:
+            out = []
+            for which, w in ((0, self.w_gate), (0, self.w_up), (1, self.w_down)):
+                p = torch.empty_like(w)
+                _lib.moe_pack_weights(d, which, w, p, stream)
+                out.append(p)
+        w_router, rl = self.w_router, self.router_layout
+        if router and self.dtype == torch.bfloat16 and rl != _lib.ACE_LAYOUT_PACKED:
+            w_router = torch.empty(_lib.moe_router_packed_bytes(d), dtype=torch.uint8, device=self.w_router.device)
+            _lib.moe_pack_router(d, self.w_router, w_router, stream)
+            rl = _lib.ACE_LAYOUT_PACKED
+        return AceMoeLayer(self.gamma, w_router, self.router_bias, out[0], out[1], out[2], self.a_gsp, self.a_rcr,
+                           self.k, self.norm_topk, self.fusion, self.rms_eps, _lib.ACE_LAYOUT_PACKED, rl)
 
     def buffers(self, T: int) -> LayerBuffers:
         return LayerBuffers.allocate(T, self.H, self.E, self.I, self.k, self.dtype, self.w_gate.device)
