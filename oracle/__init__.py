@@ -10,7 +10,8 @@ LLMs" (picx.dev summary page): the SwiGLU expert equation and RMSNorm
 factorisation (Theoretical Foundation), the GSP and RCR slot scores
 (Methodology sections 1 and 2), conservative max-fusion and the top-1 rule
 (Methodology section 3), and quantile-mapped thresholds (Efficiency Results,
-Table 6).  It is written plainly: per-token loops, float64 arithmetic, each
+Table 6), and the offline GSP and RCR tables (Methodology sections 1-2).
+It is written plainly: per-token loops, float64 arithmetic, each
 function stating the passage it follows.
 
 Pinning status of each function is listed in ``oracle/moe.py`` and
@@ -20,6 +21,8 @@ Pinning status of each function is listed in ``oracle/moe.py`` and
 from .moe import (rmsnorm, router_logits, topk_experts, topk_gates, skip_mask, silu, swiglu_expert,
                   dispatch_order, moe_layer, round_to_bf16, as_f64)
 from .thresholds import slot_scores, quantile_thresholds
+from .tables import gsp_raw, gsp_table, rcr_prototypes, rcr_raw, rcr_table, normalise
 
 __all__ = ["rmsnorm", "router_logits", "topk_experts", "topk_gates", "skip_mask", "silu", "swiglu_expert",
-           "dispatch_order", "moe_layer", "round_to_bf16", "as_f64", "slot_scores", "quantile_thresholds"]
+           "dispatch_order", "moe_layer", "round_to_bf16", "as_f64", "slot_scores", "quantile_thresholds",
+           "gsp_raw", "gsp_table", "rcr_prototypes", "rcr_raw", "rcr_table", "normalise"]
