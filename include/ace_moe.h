@@ -224,6 +224,39 @@ size_t moe_router_packed_bytes(const ace_moe_desc* d);
 ace_status moe_pack_router(const ace_moe_desc* d, const float* w_router, void* dst, void* stream);
 
 /*
+ * moe_build_tables -- the offline per-expert tables from the layer's own
+ * weights ("ACE: Adaptive Calibration-Free Expert Skipping for MoE-based
+ * LLMs", Methodology sections 1 and 2), typically once per checkpoint.
+ * With W^gate = w_gate[e]^T, W^up = w_up[e]^T (H x I), W^down = w_down[e]^T
+ * (I x H) and Gamma = diag(gamma):
+ *   GSP: a_up = |Gamma W^up|_F * |Gamma W^gate W^down|_F,
+ *        a_gate = |Gamma W^gate|_F * |Gamma W^up W^down|_F,
+ *        raw_e = sqrt(a_up * a_gate);
+ *   RCR: q_e = (w_router[e] - mean_j w_router[j]) / (RMS(that) + eps)
+ *        (prototype scale 1), raw_e = |f_e(q_e)| / (|q_e| + eps) where f_e is
+ *        the SwiGLU expert applied to q_e in the role of the normalised token,
+ *        i.e. to q_e * gamma;
+ *   both: a[e] = raw_e / (mean over experts of raw + eps).
+ * Computed on the device: the Frobenius norms through I x I Gram matrices
+ * (bf16 MFMA with exact products, float32 accumulation, float64 sums); RCR
+ * in float32 with float64 final sums.  Deterministic.
+ * In:  gamma [H] f32; w_router [E,H] f32 (plain rows); w_gate, w_up [E,I,H]
+ *      and w_down [E,H,I] of desc->dtype in the LINEAR layout (a PACKED
+ *      desc->weight_layout is rejected); eps >= 0 (1e-6 is the usual value).
+ * Out: a_gsp [E], a_rcr [E] f32 (device).  T, k, fusion and router_layout of
+ *      the descriptor are not used.
+ * workspace: moe_tables_workspace_bytes(d) bytes is the preferred size
+ *      (transposed w_down for a batch of experts, at most 512 MiB of it, plus
+ *      per-expert partials).  A smaller workspace is accepted down to the
+ *      size for batches of one expert (else ACE_EWORKSPACE): the builder then
+ *      uses the largest batch that fits.  The result does not depend on it.
+ */
+size_t moe_tables_workspace_bytes(const ace_moe_desc* d);
+ace_status moe_build_tables(const ace_moe_desc* d, float eps, const float* gamma, const float* w_router,
+                            const void* w_gate, const void* w_up, const void* w_down, float* a_gsp, float* a_rcr,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * moe_set_kernel_events -- for profiling callers: the next moe_expert_forward
  * on this thread records `start` (a hipEvent_t) on its stream just before the
  * gate/up kernel and `stop` just after it, then forgets both.  NULL clears.

@@ -131,3 +131,26 @@ def test_pack_rejects_overlap_and_bad_kind():
     assert lib.moe_pack_weights(ctypes.byref(d), 2, 0x1000, 0x100000000, None) == 1
     assert lib.moe_pack_weights(ctypes.byref(d), 0, 0x1000, 0x1000 + 64, None) == 1
     assert "overlap" in lib.moe_last_error().decode()
+
+
+def test_build_tables_validation():
+    m, lib = _lib()
+    f = 0x1000
+    d = m.make_desc(1, 2048, 128, 768, 8, "bf16")
+    pref = lib.moe_tables_workspace_bytes(ctypes.byref(d))
+    # transposed w_down for every expert (3 MiB each) fits under the 512 MiB cap
+    assert pref >= 128 * 768 * 2048 * 2
+    args = [f] * 7
+    assert lib.moe_build_tables(ctypes.byref(d), 1e-6, *args, None, 1 << 30, None) == 1
+    assert "workspace is NULL" in lib.moe_last_error().decode()
+    assert lib.moe_build_tables(ctypes.byref(d), 1e-6, None, *args[1:], f, 1 << 30, None) == 1
+    assert "gamma is NULL" in lib.moe_last_error().decode()
+    assert lib.moe_build_tables(ctypes.byref(d), -1.0, *args, f, 1 << 30, None) == 1
+    # the minimum is one expert's transposed w_down plus the per-expert partials
+    assert lib.moe_build_tables(ctypes.byref(d), 1e-6, *args, f, 768 * 2048 * 2, None) == 3
+    assert "batches of one expert" in lib.moe_last_error().decode()
+    dp = m.make_desc(1, 2048, 128, 768, 8, "bf16", weight_layout=1)
+    assert lib.moe_build_tables(ctypes.byref(dp), 1e-6, *args, f, pref, None) == 2
+    assert "LINEAR" in lib.moe_last_error().decode()
+    big = m.make_desc(1, 4096, 128, 1408, 8, "bf16")
+    assert lib.moe_tables_workspace_bytes(ctypes.byref(big)) < (512 + 64) << 20

@@ -25,7 +25,8 @@ STATUS_NAMES = {0: "ACE_OK", 1: "ACE_EINVAL", 2: "ACE_EUNSUPPORTED", 3: "ACE_EWO
 
 EXPORTS = ["moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_route_skip", "moe_dispatch",
            "moe_expert_forward", "moe_combine", "moe_calibrate_workspace_bytes", "moe_calibrate_thresholds",
-           "moe_pack_weights", "moe_router_packed_bytes", "moe_pack_router", "moe_set_kernel_events"]
+           "moe_pack_weights", "moe_router_packed_bytes", "moe_pack_router", "moe_tables_workspace_bytes",
+           "moe_build_tables", "moe_set_kernel_events"]
 
 
 class AceMoeError(RuntimeError):
@@ -93,6 +94,10 @@ def load() -> ctypes.CDLL:
     lib.moe_router_packed_bytes.argtypes = [D]
     lib.moe_pack_router.restype = ctypes.c_int
     lib.moe_pack_router.argtypes = [D, P, P, P]
+    lib.moe_tables_workspace_bytes.restype = SZ
+    lib.moe_tables_workspace_bytes.argtypes = [D]
+    lib.moe_build_tables.restype = ctypes.c_int
+    lib.moe_build_tables.argtypes = [D, F32, P, P, P, P, P, P, P, P, SZ, P]
     lib.moe_set_kernel_events.restype = ctypes.c_int
     lib.moe_set_kernel_events.argtypes = [P, P]
     _lib = lib
@@ -188,6 +193,18 @@ def moe_router_packed_bytes(desc: MoeDesc) -> int:
 
 def moe_pack_router(desc, w_router, dst, stream=None):
     _check(load().moe_pack_router(ctypes.byref(desc), _ptr(w_router), _ptr(dst), _stream(stream)), "moe_pack_router")
+
+
+def moe_tables_workspace_bytes(desc: MoeDesc) -> int:
+    return int(load().moe_tables_workspace_bytes(ctypes.byref(desc)))
+
+
+def moe_build_tables(desc, eps, gamma, w_router, w_gate, w_up, w_down, a_gsp, a_rcr, workspace,
+                     workspace_bytes=None, stream=None):
+    nbytes = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    _check(load().moe_build_tables(ctypes.byref(desc), float(eps), _ptr(gamma), _ptr(w_router), _ptr(w_gate),
+                                   _ptr(w_up), _ptr(w_down), _ptr(a_gsp), _ptr(a_rcr), _ptr(workspace), int(nbytes),
+                                   _stream(stream)), "moe_build_tables")
 
 
 def moe_set_kernel_events(start, stop):

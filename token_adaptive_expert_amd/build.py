@@ -18,7 +18,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libace_moe.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.cpp", "route.hip", "dispatch.hip", "expert.hip", "combine.hip", "calibrate.hip"]
+SOURCES = ["api.cpp", "route.hip", "dispatch.hip", "expert.hip", "combine.hip", "calibrate.hip", "tables.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

@@ -387,6 +387,52 @@ ace_status moe_pack_router(const ace_moe_desc* d, const float* w_router, void* d
   }
 }
 
+size_t moe_tables_workspace_bytes(const ace_moe_desc* d) {
+  if (check_desc(d) != ACE_OK) return 0;
+  return ace::tables_workspace_bytes(d->E, d->H, d->I, d->dtype, false);
+}
+
+ace_status moe_build_tables(const ace_moe_desc* d, float eps, const float* gamma, const float* w_router,
+                            const void* w_gate, const void* w_up, const void* w_down, float* a_gsp, float* a_rcr,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    ace_status st = check_desc(d);
+    if (st != ACE_OK) return st;
+    if (d->weight_layout != ACE_LAYOUT_LINEAR)
+      return fail(ACE_EUNSUPPORTED, "moe_build_tables reads expert weights in the LINEAR layout");
+    if (!(eps >= 0.f)) return fail(ACE_EINVAL, "eps must be >= 0");
+    REQUIRE(gamma);
+    REQUIRE(w_router);
+    REQUIRE(w_gate);
+    REQUIRE(w_up);
+    REQUIRE(w_down);
+    REQUIRE(a_gsp);
+    REQUIRE(a_rcr);
+    REQUIRE(workspace);
+    const size_t need = ace::tables_workspace_bytes(d->E, d->H, d->I, d->dtype, true);
+    if (workspace_bytes < need)
+      return fail(ACE_EWORKSPACE, "workspace_bytes=%zu < %zu needed (batches of one expert)", workspace_bytes,
+                  need);
+    ace::TablesArgs a{};
+    a.gamma = gamma;
+    a.w_router = w_router;
+    a.w_gate = w_gate;
+    a.w_up = w_up;
+    a.w_down = w_down;
+    a.a_gsp = a_gsp;
+    a.a_rcr = a_rcr;
+    a.E = d->E;
+    a.H = d->H;
+    a.I = d->I;
+    a.eps = eps;
+    hipError_t e = ace::launch_tables(d->dtype, a, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("tables launch", e);
+    return ok();
+  } catch (...) {
+    return fail(ACE_EHIP, "unexpected host exception in moe_build_tables");
+  }
+}
+
 ace_status moe_set_kernel_events(void* start, void* stop) {
   if ((start == nullptr) != (stop == nullptr)) return fail(ACE_EINVAL, "start and stop must both be set or both NULL");
   g_ev_start = static_cast<hipEvent_t>(start);

@@ -88,6 +88,29 @@ template <> __device__ __forceinline__ f32x4 mma_step<float>(u32x4 a, u32x4 b, f
   return c;
 }
 
+// Exact three-term bf16 split of 8 float32 values: v = hi + mid + lo, each
+// term rounded to nearest even.  24 significant bits = 3 x 8, and each residual
+// is exact in float32, so bf16 MFMAs against the three planes form exact
+// float32 products.  planes[p] holds term p of the 8 values, packed in order.
+__device__ __forceinline__ void split3_f8(const float (&ww)[8], u32x4* planes) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint16_t h2[2], m2[2], l2[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const float v = ww[2 * j + p];
+      h2[p] = f32_to_bf16(v);
+      const float r1 = v - bf16_to_f32(h2[p]);
+      m2[p] = f32_to_bf16(r1);
+      const float r2 = r1 - bf16_to_f32(m2[p]);
+      l2[p] = f32_to_bf16(r2);
+    }
+    planes[0][j] = uint32_t(h2[0]) | (uint32_t(h2[1]) << 16);
+    planes[1][j] = uint32_t(m2[0]) | (uint32_t(m2[1]) << 16);
+    planes[2][j] = uint32_t(l2[0]) | (uint32_t(l2[1]) << 16);
+  }
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 }  // namespace ace

@@ -72,6 +72,28 @@ struct CalibArgs {
   int T, k, N, n_target;
 };
 
+struct TablesArgs {
+  const float* gamma;     // [H]
+  const float* w_router;  // [E, H] f32
+  const void* w_gate;     // [E, I, H] dtype (linear layout)
+  const void* w_up;       // [E, I, H]
+  const void* w_down;     // [E, H, I]
+  float* a_gsp;           // [E] out
+  float* a_rcr;           // [E] out
+  int E, H, I;
+  float eps;
+  // workspace regions, set by launch_tables
+  void* ws_wdT;
+  double* ws_part;
+  float* ws_mean;
+  float* ws_x;
+  float* ws_qnorm;
+  float* ws_v;
+  double* ws_opart;
+  double* ws_raw_gsp;
+  double* ws_raw_rcr;
+};
+
 // Host launchers (return the launch status).
 hipError_t launch_route(int dtype, const RouteArgs& a, hipStream_t s);
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
@@ -85,5 +107,9 @@ hipError_t launch_pack_router(const float* w, void* dst, int E, int H, hipStream
 hipError_t launch_pack(int dtype, const void* src, void* dst, int E, int N, int K, hipStream_t s);
 size_t calib_workspace_bytes(int T, int k);
 hipError_t launch_calibrate(CalibArgs a, void* workspace, hipStream_t s);
+// minimum: the smallest workspace (Gram batches of one expert); else the preferred size.
+size_t tables_workspace_bytes(int E, int H, int I, int dtype, bool minimum);
+// Uses the largest Gram batch that workspace_bytes holds.
+hipError_t launch_tables(int dtype, TablesArgs a, void* workspace, size_t workspace_bytes, hipStream_t s);
 
 }  // namespace ace

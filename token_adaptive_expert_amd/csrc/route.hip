@@ -71,26 +71,10 @@ template <typename T> struct RouterFrag {
 // accumulate them in float32.
 template <typename T> __device__ __forceinline__ f32x4 router_mma(u32x4 a, const f32x4* w, f32x4 acc);
 
-// Exact three-term bf16 split of 8 float32 values: w = hi + mid + lo (each
-// term rounded to nearest even; the residuals are exact in float32).
+// Exact three-term bf16 split of the 8 float32 weights of one k-step.
 __device__ __forceinline__ void split3(const f32x4* w, u32x4* planes) {
-  float ww[8] = {w[0][0], w[0][1], w[0][2], w[0][3], w[1][0], w[1][1], w[1][2], w[1][3]};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint16_t h2[2], m2[2], l2[2];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const float v = ww[2 * j + p];
-      h2[p] = f32_to_bf16(v);
-      const float r1 = v - bf16_to_f32(h2[p]);
-      m2[p] = f32_to_bf16(r1);
-      const float r2 = r1 - bf16_to_f32(m2[p]);
-      l2[p] = f32_to_bf16(r2);
-    }
-    planes[0][j] = uint32_t(h2[0]) | (uint32_t(h2[1]) << 16);
-    planes[1][j] = uint32_t(m2[0]) | (uint32_t(m2[1]) << 16);
-    planes[2][j] = uint32_t(l2[0]) | (uint32_t(l2[1]) << 16);
-  }
+  const float ww[8] = {w[0][0], w[0][1], w[0][2], w[0][3], w[1][0], w[1][1], w[1][2], w[1][3]};
+  split3_f8(ww, planes);
 }
 
 __device__ __forceinline__ f32x4 mma3(u32x4 a, const u32x4* planes, f32x4 acc) {

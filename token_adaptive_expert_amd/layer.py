@@ -133,3 +133,20 @@ class AceMoeLayer:
         self.experts(T, b, path, stream)
         self.combine(T, b, residual, stream)
         return b.y[:T]
+
+
+def build_tables(gamma, w_router, w_gate, w_up, w_down, eps=1e-6, workspace=None, stream=None):
+    """A^GSP and A^RCR [E] f32 of one layer from its weights (moe_build_tables).
+    Weights in the LINEAR layout on one device; ``workspace`` (uint8 tensor)
+    defaults to the preferred size."""
+    E, I, H = w_gate.shape
+    d = _lib.make_desc(1, H, E, I, 1, w_gate.dtype)
+    if workspace is None:
+        n = _lib.moe_tables_workspace_bytes(d)
+        if n == 0:
+            raise _lib.AceMoeError(_lib.ACE_EINVAL, "moe_tables_workspace_bytes", _lib.moe_last_error())
+        workspace = torch.empty(n, dtype=torch.uint8, device=w_gate.device)
+    a_gsp = torch.empty(E, dtype=torch.float32, device=w_gate.device)
+    a_rcr = torch.empty(E, dtype=torch.float32, device=w_gate.device)
+    _lib.moe_build_tables(d, eps, gamma, w_router, w_gate, w_up, w_down, a_gsp, a_rcr, workspace, None, stream)
+    return a_gsp, a_rcr
