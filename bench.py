@@ -40,6 +40,7 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-tables", action="store_true", help="skip timing the offline table builder")
     p.add_argument("--cpu-tokens", type=int, default=1024, help="tokens in the oracle's timed sample")
     p.add_argument("--path", type=int, default=0, help="0 auto, 1 grouped, 2 stream")
     p.add_argument("--layout", choices=["packed", "linear"], default="packed",
@@ -184,6 +185,40 @@ class Bench:
         return out
 
 
+def tables_build(B, reps=5):
+    """Time moe_build_tables (A^GSP and A^RCR of the layer from its weights,
+    done once per checkpoint) on the generated layer's linear weights.
+    Gram MFMA work per expert: the 128x128 upper-triangular tiles of D, G_g and
+    G_u, the last two with the gamma^2-scaled operand as three exact bf16
+    planes (7 MFMA passes per tile); useful work counts each Gram once."""
+    torch, ace, S, P = B.torch, B.ace, B.S, B.P
+    d = ace.make_desc(1, S.H, S.E, S.I, 1, "bf16")
+    ws = torch.empty(ace.moe_tables_workspace_bytes(d), dtype=torch.uint8, device=B.dev)
+    args = (P["gamma"], P["w_router"], P["w_gate"], P["w_up"], P["w_down"])
+    ace.build_tables(*args, workspace=ws)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        g, r = ace.build_tables(*args, workspace=ws)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    nbk = S.I // 128
+    tiles = nbk * (nbk + 1) // 2
+    executed = S.E * tiles * 128 * 128 * S.H * 2 * 7
+    useful = S.E * 3 * S.I * (S.I + 1) // 2 * S.H * 2
+    weight_bytes = S.E * 3 * S.H * S.I * 2
+    return {"ms": round(ms, 4), "experts": S.E,
+            "mfma_tflop_executed": round(executed / 1e12, 4),
+            "executed_tflops": round(executed / (ms * 1e-3) / 1e12, 1),
+            "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 1),
+            "mfma_frac_whole_build": round(executed / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+            "weight_bytes": weight_bytes,
+            "a_gsp_range": [round(float(g.min()), 4), round(float(g.max()), 4)],
+            "a_rcr_range": [round(float(r.min()), 4), round(float(r.max()), 4)]}
+
+
 def cpu_baseline(L, S, tau, ntok, min_seconds=10.0, max_passes=20):
     """The oracle, as it stands, over the first `ntok` tokens of the batch,
     repeated until at least `min_seconds` of host time (at most `max_passes`)."""
@@ -285,6 +320,8 @@ def main():
         res["decode_us_per_layer"] = {str(m): round(v["us"], 2) for m, v in dec.items()}
         res["decode_detail"] = {str(m): {k2: (round(v2, 4) if isinstance(v2, float) else v2) for k2, v2 in v.items()}
                                 for m, v in dec.items()}
+    if not args.no_tables:
+        res["tables_build"] = tables_build(B)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(B.L, S, head["tau"], args.cpu_tokens)
     print(json.dumps(res), flush=True)

@@ -46,6 +46,23 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Wave64 sum through DPP row shifts (inclusive scan within each row of 16
+// lanes) and the four row totals read from lanes 15, 31, 47, 63, added in
+// that order; every lane gets the result.  No LDS round trips.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+#define ACE_DPP_ADD(CTRL) \
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false))
+  ACE_DPP_ADD(0x111);
+  ACE_DPP_ADD(0x112);
+  ACE_DPP_ADD(0x114);
+  ACE_DPP_ADD(0x118);
+#undef ACE_DPP_ADD
+  const int b = __float_as_int(v);
+  return ((__int_as_float(__builtin_amdgcn_readlane(b, 15)) + __int_as_float(__builtin_amdgcn_readlane(b, 31))) +
+          __int_as_float(__builtin_amdgcn_readlane(b, 47))) +
+         __int_as_float(__builtin_amdgcn_readlane(b, 63));
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 

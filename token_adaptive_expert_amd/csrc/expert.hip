@@ -43,6 +43,62 @@ constexpr int ROWB = 256;        // bytes of one row per chunk
 constexpr int NXCD = 8;          // XCDs of an MI355X; only tile placement depends on it
 constexpr int LDS_PITCH = ACE_LDS_PITCH;
 
+// Tile list of the dispatched slots (wave 0 writes it to LDS): expert e has
+// ceil(n_e / BM) m-tiles; s_pref = exclusive prefix of those counts over the
+// experts (s_pref[E] = total), s_off = expert_offsets.
+template <int BM>
+__device__ __forceinline__ void build_tile_list(const ExpertArgs& a, int32_t* s_pref, int32_t* s_off) {
+  if (wave_id() != 0) return;
+  const int l = lane_id(), E = a.E;
+  int cnt[4], loc = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = l * 4 + j;
+    int c = 0;
+    if (e < E) {
+      const int o0 = a.offsets[e], o1 = a.offsets[e + 1];
+      s_off[e] = o0;
+      c = (o1 - o0 + BM - 1) / BM;
+    }
+    cnt[j] = c;
+    loc += c;
+  }
+  int inc = loc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(inc, o, 64);
+    if (l >= o) inc += v;
+  }
+  int run = inc - loc;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = l * 4 + j;
+    if (e < E) s_pref[e] = run;
+    run += cnt[j];
+  }
+  if (l == 63) s_pref[E] = inc;
+  if (l == 0) s_off[E] = a.offsets[E];
+}
+
+// Tile g of the expert-major list (expert, then n-block, then the expert's
+// m-tiles): its expert, n-block, first sorted row and row count.
+__device__ __forceinline__ void find_tile(int g, int nb_count, int BM, int E, const int32_t* s_pref,
+                                          const int32_t* s_off, int& e, int& nb, int& row0, int& rows) {
+  // expert e owns tiles [nb_count*s_pref[e], nb_count*s_pref[e+1])
+  int lo = 0, hi = E;  // invariant: nb_count*s_pref[lo] <= g < nb_count*s_pref[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (nb_count * s_pref[mid] <= g) lo = mid; else hi = mid;
+  }
+  e = lo;
+  const int mt_e = s_pref[e + 1] - s_pref[e];
+  const int local = g - nb_count * s_pref[e];
+  nb = local / mt_e;
+  const int mtl = local - nb * mt_e;
+  row0 = s_off[e] + mtl * BM;
+  rows = min(BM, s_off[e + 1] - row0);
+}
+
 template <typename T, int RB, int NW, int KIND, int STAGES>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ACE_WAVES_PER_EU)))
 void expert_gemm_kernel(ExpertArgs a) {
@@ -65,37 +121,7 @@ void expert_gemm_kernel(ExpertArgs a) {
   const int nch = K / KC;
   const int nb_count = N / ROWS_PER_WG;
 
-  // tile list: per-expert m-tile counts, exclusive prefix (wave 0)
-  if (w == 0) {
-    int cnt[4], loc = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = l * 4 + j;
-      int c = 0;
-      if (e < E) {
-        const int o0 = a.offsets[e], o1 = a.offsets[e + 1];
-        s_off[e] = o0;
-        c = (o1 - o0 + BM - 1) / BM;
-      }
-      cnt[j] = c;
-      loc += c;
-    }
-    int inc = loc;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(inc, o, 64);
-      if (l >= o) inc += v;
-    }
-    int run = inc - loc;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = l * 4 + j;
-      if (e < E) s_pref[e] = run;
-      run += cnt[j];
-    }
-    if (l == 63) s_pref[E] = inc;
-    if (l == 0) s_off[E] = a.offsets[E];
-  }
+  build_tile_list<BM>(a, s_pref, s_off);
   __syncthreads();
 
   const int total_mt = s_pref[E];
@@ -113,19 +139,8 @@ void expert_gemm_kernel(ExpertArgs a) {
   for (int wg = blockIdx.x; wg < NXCD * per_xcd; wg += gridDim.x) {
     const int g = (wg % NXCD) * per_xcd + wg / NXCD;
     if (g >= ntiles) continue;
-    // expert of tile g: expert e owns tiles [nb_count*s_pref[e], nb_count*s_pref[e+1])
-    int lo = 0, hi = E;  // invariant: nb_count*s_pref[lo] <= g < nb_count*s_pref[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (nb_count * s_pref[mid] <= g) lo = mid; else hi = mid;
-    }
-    const int e = lo;
-    const int mt_e = s_pref[e + 1] - s_pref[e];
-    const int local = g - nb_count * s_pref[e];
-    const int nb = local / mt_e;
-    const int mtl = local - nb * mt_e;
-    const int row0 = s_off[e] + mtl * BM;
-    const int rows = min(BM, s_off[e + 1] - row0);
+    int e, nb, row0, rows;
+    find_tile(g, nb_count, BM, E, s_pref, s_off, e, nb, row0, rows);
     const int nrb = (rows + 15) >> 4;
 
     // Weights are read with buffer loads: the expert's matrix base lives in a
@@ -261,6 +276,151 @@ void expert_gemm_kernel(ExpertArgs a) {
   }
 }
 
+// Small-batch ("stream") path: split-K inside the workgroup.  A tile is one
+// expert, up to 16 of its slot rows and 32 weight rows (gate/up: 16 gate and
+// the 16 up rows of the same intermediate units; down: 32 output columns).
+// Its SK_NW waves take interleaved k-steps (wave w: w, w+SK_NW, ...) and
+// issue all weight and slot-row loads of up to SK_NBK k-steps at once, so
+// that with few rows per expert the weight stream is limited by bandwidth,
+// not by one wave's loads in flight.  The waves' partial sums meet in LDS
+// and are added in wave order (deterministic), then SiLU(gate)*up or the
+// gate scale is applied.  Slot rows are read straight from global memory
+// (they are few and stay in L2).
+constexpr int SK_NW = 8;
+
+template <typename T, int KIND, int SK_NBK>
+__global__ __launch_bounds__(SK_NW * 64) void expert_splitk_kernel(ExpertArgs a) {
+  constexpr int EPL = St<T>::EPL;
+  constexpr int KS = 4 * EPL;
+  constexpr int BM = 16;
+  constexpr int COLS = (KIND == 0) ? 16 : 32;  // output columns per tile
+  __shared__ int32_t s_pref[257];
+  __shared__ int32_t s_off[257];
+  __shared__ float s_red[SK_NW][2][16][17];
+
+  const int w = wave_id(), l = lane_id(), tid = threadIdx.x;
+  const int q = l >> 4, r16 = l & 15;
+  const int E = a.E, K = a.K, N = a.N;
+  const int nb_count = N / COLS;
+  const int nk = K / KS;
+  const int nkw = w < nk ? (nk - 1 - w) / SK_NW + 1 : 0;  // this wave's k-steps
+
+  build_tile_list<BM>(a, s_pref, s_off);
+  __syncthreads();
+  const int ntiles = s_pref[E] * nb_count;
+  const int per_xcd = (ntiles + NXCD - 1) / NXCD;
+  for (int wg = blockIdx.x; wg < NXCD * per_xcd; wg += gridDim.x) {
+    const int g = (wg % NXCD) * per_xcd + wg / NXCD;
+    if (g >= ntiles) continue;
+    int e, nb, row0, rows;
+    find_tile(g, nb_count, BM, E, s_pref, s_off, e, nb, row0, rows);
+    const int col0 = nb * COLS;
+    const int n0[2] = {col0, (KIND == 0) ? col0 : col0 + 16};
+    const int64_t ebytes = int64_t(N) * K * int(sizeof(T));
+    const char* wm0 = reinterpret_cast<const char*>(a.W0) + int64_t(e) * ebytes;
+    const char* wm1 = reinterpret_cast<const char*>((KIND == 0) ? a.W1 : a.W0) + int64_t(e) * ebytes;
+    const __amdgpu_buffer_rsrc_t wr0 = make_rsrc(wm0, uint32_t(ebytes));
+    const __amdgpu_buffer_rsrc_t wr1 = make_rsrc(wm1, uint32_t(ebytes));
+    int wv, ws[2], wstep;
+    if (a.packed) {
+      wv = l * 16;
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) ws[gg] = (n0[gg] / 16) * nk * 1024;
+      wstep = 1024;
+    } else {
+      wv = (r16 * K + q * EPL) * int(sizeof(T));
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) ws[gg] = n0[gg] * K * int(sizeof(T));
+      wstep = KS * int(sizeof(T));
+    }
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    if (nkw > 0) {
+      // weight loads of the first batch go out before the slot row is known
+      u32x4 wa[SK_NBK], wb[SK_NBK], xa[SK_NBK];
+      auto load_w = [&](int i0) {
+#pragma unroll
+        for (int b = 0; b < SK_NBK; ++b) {
+          const int j = w + SK_NW * min(i0 + b, nkw - 1);
+          wa[b] = buf_ld16(wr0, wv, ws[0] + j * wstep);
+          wb[b] = buf_ld16(wr1, wv, ws[1] + j * wstep);
+        }
+      };
+      load_w(0);
+      // slot row of this lane; lanes past the tile's last row get an offset
+      // beyond the buffer, so their loads return zero without memory traffic
+      const int rr = min(r16, rows - 1);
+      const int src_row = (KIND == 0) ? a.sorted_token[row0 + rr] : row0 + rr;
+      const uint32_t xbytes = uint32_t(int64_t(a.A_rows) * K * int(sizeof(T)));
+      const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.A, xbytes);
+      const int xv = r16 < rows ? (src_row * K + q * EPL) * int(sizeof(T)) : int(0x7FFFFFF0u);
+      for (int i0 = 0; i0 < nkw; i0 += SK_NBK) {
+        if (i0 > 0) load_w(i0);
+#pragma unroll
+        for (int b = 0; b < SK_NBK; ++b) {
+          const int j = w + SK_NW * min(i0 + b, nkw - 1);
+          xa[b] = buf_ld16(xrs, xv, j * KS * int(sizeof(T)));
+        }
+#pragma unroll
+        for (int b = 0; b < SK_NBK; ++b) {
+          if (i0 + b < nkw) {
+            acc0 = mma_step<T>(xa[b], wa[b], acc0);
+            acc1 = mma_step<T>(xa[b], wb[b], acc1);
+          }
+        }
+      }
+    }
+    // lane (q, r16) holds rows 4q..4q+3 of weight column r16 in each group
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s_red[w][0][4 * q + j][r16] = acc0[j];
+      s_red[w][1][4 * q + j][r16] = acc1[j];
+    }
+    __syncthreads();
+    if (tid < 256) {
+      const int row = tid >> 4, c = tid & 15;
+      if (row < rows) {
+        float v0 = s_red[0][0][row][c], v1 = s_red[0][1][row][c];
+#pragma unroll
+        for (int ww = 1; ww < SK_NW; ++ww) {
+          v0 += s_red[ww][0][row][c];
+          v1 += s_red[ww][1][row][c];
+        }
+        const int64_t p = row0 + row;
+        if (KIND == 0) {
+          reinterpret_cast<T*>(a.out)[p * N + col0 + c] = St<T>::from_f32(silu(v0) * v1);
+        } else {
+          const float gt = a.sorted_gate[p];
+          float* o = reinterpret_cast<float*>(a.out) + p * N + col0 + c;
+          o[0] = gt * v0;
+          o[16] = gt * v1;
+        }
+      }
+    }
+    __syncthreads();  // s_red is reused by the next tile of this workgroup
+  }
+}
+
+// The tile count is known only on the device; the grid covers the host-side
+// bound but at most SK_WG_PER_CU workgroups per compute unit, which loop over
+// the tiles (workgroups past the last tile exit after the tile-list prologue,
+// so an uncapped worst-case grid would mostly pay that prologue).  k-steps
+// per load batch: 8 for gate/up (K = H), 4 for down (K = I; fewer registers,
+// more resident workgroups).
+constexpr int SK_WG_PER_CU = 8;
+
+template <typename T, int KIND>
+hipError_t launch_splitk(const ExpertArgs& a, int ntok, int k, int num_cu, hipStream_t s) {
+  constexpr int COLS = (KIND == 0) ? 16 : 32;
+  const int64_t slots = int64_t(ntok) * k;
+  const int64_t mt_bound = (slots + 15) / 16 + std::min<int64_t>(a.E, slots);
+  const int64_t tiles_bound = mt_bound * (a.N / COLS);
+  const int64_t cap = int64_t(std::max(num_cu, 1)) * SK_WG_PER_CU;
+  const int64_t grid = std::max<int64_t>(NXCD, (std::min(tiles_bound, cap) + NXCD - 1) / NXCD * NXCD);
+  hipLaunchKernelGGL((expert_splitk_kernel<T, KIND, KIND == 0 ? 8 : 4>), dim3(unsigned(grid)), dim3(SK_NW * 64), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
 // Packed weight layout: [E][N/16][K/KS][64 lanes][16 bytes], where the
 // 16-byte unit of lane l in fragment (e, n-group, k-step j) holds row
 // n-group*16 + l%16, k values j*KS + (l/16)*EPL .. +EPL of the linear
@@ -315,17 +475,14 @@ hipError_t launch_pack(int dtype, const void* src, void* dst, int E, int N, int 
 hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs& a, int T, int k, int num_cu,
                          hipStream_t s) {
   constexpr int G = ACE_GROUPED_RB, S = ACE_GROUPED_STAGES;
-  (void)num_cu;
   if (dtype == 1) {
     if (stream_path)
-      return kind == 0 ? launch_one<bf16_t, 1, 2, 0, 3>(a, T, k, s)
-                       : launch_one<bf16_t, 1, 2, 1, 3>(a, T, k, s);
+      return kind == 0 ? launch_splitk<bf16_t, 0>(a, T, k, num_cu, s) : launch_splitk<bf16_t, 1>(a, T, k, num_cu, s);
     return kind == 0 ? launch_one<bf16_t, G, 4, 0, S>(a, T, k, s)
                      : launch_one<bf16_t, G, 4, 1, S>(a, T, k, s);
   }
   if (stream_path)
-    return kind == 0 ? launch_one<float, 1, 2, 0, 3>(a, T, k, s)
-                     : launch_one<float, 1, 2, 1, 3>(a, T, k, s);
+    return kind == 0 ? launch_splitk<float, 0>(a, T, k, num_cu, s) : launch_splitk<float, 1>(a, T, k, num_cu, s);
   return kind == 0 ? launch_one<float, G, 4, 0, S>(a, T, k, s)
                    : launch_one<float, G, 4, 1, S>(a, T, k, s);
 }

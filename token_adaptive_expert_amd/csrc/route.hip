@@ -12,11 +12,11 @@ namespace ace {
 namespace {
 
 constexpr int TB = 16;        // tokens per workgroup (router kernel)
-constexpr int ECB = 32;       // experts per workgroup (router kernel)
 constexpr int RW = 16;        // waves of the router kernel (split the hidden dimension)
 constexpr int RNTHR = RW * 64;
 constexpr int NTHR = 256;     // 4 waves (top-k kernel)
 constexpr int EMAX = 256;
+constexpr int NARROW_HMAX = 8192;  // hidden size limit of the small-batch router variant
 
 // h for EPL consecutive hidden units of one token, rounded to the storage
 // type (gamma values passed in).  The same function feeds h_out and the
@@ -114,16 +114,21 @@ template <> __device__ __forceinline__ float sumsq16<float>(u32x4 v) {
 
 }  // namespace
 
-// Kernel 1: RMSNorm (+ h_out) and the router product for 16 tokens x 32
+// Kernel 1: RMSNorm (+ h_out) and the router product for 16 tokens x 16*NCB
 // experts.  Sixteen waves split the hidden dimension: wave w takes k-steps
 // w, w+16, w+32, ...  Their partial logits are summed in a fixed wave order,
-// so the result does not depend on timing.  Loads are issued for two
-// k-steps before either is used; token rows past T and expert rows past E
-// read a clamped valid row whose results are never stored.
-template <typename T>
+// so a logit does not depend on timing, on NCB or on the batch size.  Token
+// rows past T and expert rows past E read a clamped valid row whose results
+// are never stored.  For small batches (NCB = 1: more workgroups share the
+// pre-split router planes) the first batch of a wave's weight and x loads is
+// issued before the RMS prologue, so that the two latencies overlap.
+template <typename T, int NCB>
 __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
+  constexpr int ECBW = 16 * NCB;          // experts per workgroup
+  constexpr int NBK = NCB == 1 ? 4 : 2;   // k-steps per wave per load batch (pre-split planes)
   __shared__ float s_inv[TB];
-  __shared__ float s_part[RW][TB][ECB + 1];
+  __shared__ float s_part[RW][TB][ECBW + 1];
+  __shared__ __attribute__((aligned(16))) float s_gam[NCB == 1 ? NARROW_HMAX : 4];
 
   constexpr int EPL = St<T>::EPL;
   constexpr int KS = 4 * EPL;
@@ -131,6 +136,50 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
   const int tok0 = blockIdx.x * TB;
   const int H = a.H, E = a.E;
   const T* x = reinterpret_cast<const T*>(a.x);
+  const int q = l >> 4, r16 = l & 15;
+  const int tt = tok0 + r16;
+  const int t = min(tt, a.T - 1);
+  const T* xrow = x + int64_t(t) * H;
+  T* hrow = reinterpret_cast<T*>(a.h_out) + int64_t(t) * H;
+  const bool write_h = blockIdx.y == 0 && tt < a.T;
+  const bool do_router = a.logits_in == nullptr;
+  const int nks = H / KS;
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+
+  // pre-split planes: [3][CB][nks][64][16 B]; this workgroup's column blocks
+  const bool packed = sizeof(T) == 2 && do_router && a.router_packed;
+  const int CB = (E + 15) / 16;
+  int cb[NCB];
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) cb[c] = min(int(blockIdx.y) * NCB + c, CB - 1);
+  const uint8_t* wp = reinterpret_cast<const uint8_t*>(a.w_router);
+  const int64_t plane_bytes = int64_t(CB) * nks * 1024;
+  const int nki = w < nks ? (nks - 1 - w) / RW + 1 : 0;  // this wave's k-steps
+  u32x4 pl[NBK][NCB][3];
+  u32x4 px[NBK];
+  auto issue = [&](int i0) {
+#pragma unroll
+    for (int b = 0; b < NBK; ++b) {
+      const int j = w + RW * min(i0 + b, nki - 1);
+      px[b] = ld16(xrow + j * KS + q * EPL);
+#pragma unroll
+      for (int c = 0; c < NCB; ++c)
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+          pl[b][c][p] = ld16(wp + p * plane_bytes + (int64_t(cb[c]) * nks + j) * 1024 + l * 16);
+    }
+  };
+  constexpr bool EARLY = NCB == 1;  // registers allow the early batch only with one column block
+  if (EARLY && packed && nki > 0) issue(0);
+  // router bias of this thread's output (read after the last barrier)
+  float bias_v = 0.f;
+  if (do_router && a.bias != nullptr && threadIdx.x < TB * ECBW)
+    bias_v = a.bias[min(int(blockIdx.y) * ECBW + int(threadIdx.x) % ECBW, E - 1)];
+  if constexpr (EARLY) {
+    // gamma into LDS (H <= NARROW_HMAX on this path), read back after the barrier
+    for (int h = threadIdx.x * 4; h < H; h += RNTHR * 4)
+      *reinterpret_cast<f32x4*>(&s_gam[h]) = *reinterpret_cast<const f32x4*>(a.gamma + h);
+  }
 
   // inverse RMS: wave w owns token tok0 + w; a row is read 8 segments of
   // 64 lanes x 16 bytes at a time, all in flight together
@@ -146,85 +195,63 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
       for (int b = 0; b < 8; ++b)
         if (j0 + b * SEG + l * EPL < H) ss += sumsq16<T>(v[b]);
     }
-    ss = wave_sum(ss);
+    ss = wave_sum_dpp(ss);
     if (l == 0) s_inv[w] = 1.0f / sqrtf(ss / float(H) + a.eps);
   }
   __syncthreads();
-
-  const int q = l >> 4, r16 = l & 15;
-  const int tt = tok0 + r16;
-  const int t = min(tt, a.T - 1);
   const float inv = s_inv[r16];
-  const T* xrow = x + int64_t(t) * H;
-  T* hrow = reinterpret_cast<T*>(a.h_out) + int64_t(t) * H;
-  const bool write_h = blockIdx.y == 0 && tt < a.T;
-  const bool do_router = a.logits_in == nullptr;
-  const int e0 = min(blockIdx.y * ECB + r16, E - 1), e1 = min(blockIdx.y * ECB + 16 + r16, E - 1);
-  const float* w0 = a.w_router + int64_t(e0) * H;
-  const float* w1 = a.w_router + int64_t(e1) * H;
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  const int nks = H / KS;
+
   if constexpr (sizeof(T) == 2) {
-    if (do_router && a.router_packed) {
-      // pre-split planes: [3][CB][nks][64][16 B]; this workgroup's two
-      // 16-expert column blocks
-      const int CB = (E + 15) / 16;
-      const int cb0 = min(int(blockIdx.y) * 2, CB - 1), cb1 = min(int(blockIdx.y) * 2 + 1, CB - 1);
-      const uint8_t* wp = reinterpret_cast<const uint8_t*>(a.w_router);
-      const int64_t plane_bytes = int64_t(CB) * nks * 1024;
-      auto ldp = [&](int cb, int j, u32x4* out) {
+    if (packed) {
+      for (int i0 = 0; i0 < nki; i0 += NBK) {
+        if (i0 > 0 || !EARLY) issue(i0);
 #pragma unroll
-        for (int p = 0; p < 3; ++p) out[p] = ld16(wp + p * plane_bytes + (int64_t(cb) * nks + j) * 1024 + l * 16);
-      };
-      for (int j0 = w; j0 < nks; j0 += 2 * RW) {
-        const int j1 = min(j0 + RW, nks - 1);
-        const int k0 = j0 * KS + q * EPL, k1 = j1 * KS + q * EPL;
-        RouterFrag<T> f0, f1;
-        u32x4 p00[3], p01[3], p10[3], p11[3];
-        f0.load_x(xrow, a.gamma, k0);
-        f1.load_x(xrow, a.gamma, k1);
-        ldp(cb0, j0, p00);
-        ldp(cb1, j0, p01);
-        ldp(cb0, j1, p10);
-        ldp(cb1, j1, p11);
-        const u32x4 h0 = make_h<T>(f0.x, inv, f0.g);
-        if (write_h) st16(hrow + k0, h0);
-        acc0 = mma3(h0, p00, acc0);
-        acc1 = mma3(h0, p01, acc1);
-        if (j0 + RW < nks) {
-          const u32x4 h1 = make_h<T>(f1.x, inv, f1.g);
-          if (write_h) st16(hrow + k1, h1);
-          acc0 = mma3(h1, p10, acc0);
-          acc1 = mma3(h1, p11, acc1);
+        for (int b = 0; b < NBK; ++b) {
+          if (i0 + b < nki) {
+            const int k0 = (w + RW * (i0 + b)) * KS + q * EPL;
+            const float* gp = EARLY ? s_gam + k0 : a.gamma + k0;
+            f32x4 g[2];
+            g[0] = *reinterpret_cast<const f32x4*>(gp);
+            g[1] = *reinterpret_cast<const f32x4*>(gp + 4);
+            const u32x4 h = make_h<T>(px[b], inv, g);
+            if (write_h) st16(hrow + k0, h);
+#pragma unroll
+            for (int c = 0; c < NCB; ++c) acc[c] = mma3(h, pl[b][c], acc[c]);
+          }
         }
       }
       goto reduce;
     }
   }
-  if (do_router || blockIdx.y == 0) {
-    for (int j0 = w; j0 < nks; j0 += 2 * RW) {
-      const int j1 = j0 + RW;
-      const int k0 = j0 * KS + q * EPL, k1 = min(j1, nks - 1) * KS + q * EPL;
-      RouterFrag<T> f0, f1;
-      if (do_router) {
-        f0.load(xrow, a.gamma, w0, w1, k0);
-        f1.load(xrow, a.gamma, w0, w1, k1);
-      } else {
-        f0.load_x(xrow, a.gamma, k0);
-        f1.load_x(xrow, a.gamma, k1);
-      }
-      const u32x4 h0 = make_h<T>(f0.x, inv, f0.g);
-      if (write_h) st16(hrow + k0, h0);
-      if (do_router) {
-        acc0 = router_mma<T>(h0, f0.w0, acc0);
-        acc1 = router_mma<T>(h0, f0.w1, acc1);
-      }
-      if (j1 < nks) {
-        const u32x4 h1 = make_h<T>(f1.x, inv, f1.g);
-        if (write_h) st16(hrow + k1, h1);
+  if constexpr (NCB == 2) {
+    const int e0 = min(blockIdx.y * ECBW + r16, E - 1), e1 = min(blockIdx.y * ECBW + 16 + r16, E - 1);
+    const float* w0 = a.w_router + int64_t(e0) * H;
+    const float* w1 = a.w_router + int64_t(e1) * H;
+    if (do_router || blockIdx.y == 0) {
+      for (int j0 = w; j0 < nks; j0 += 2 * RW) {
+        const int j1 = j0 + RW;
+        const int k0 = j0 * KS + q * EPL, k1 = min(j1, nks - 1) * KS + q * EPL;
+        RouterFrag<T> f0, f1;
         if (do_router) {
-          acc0 = router_mma<T>(h1, f1.w0, acc0);
-          acc1 = router_mma<T>(h1, f1.w1, acc1);
+          f0.load(xrow, a.gamma, w0, w1, k0);
+          f1.load(xrow, a.gamma, w0, w1, k1);
+        } else {
+          f0.load_x(xrow, a.gamma, k0);
+          f1.load_x(xrow, a.gamma, k1);
+        }
+        const u32x4 h0 = make_h<T>(f0.x, inv, f0.g);
+        if (write_h) st16(hrow + k0, h0);
+        if (do_router) {
+          acc[0] = router_mma<T>(h0, f0.w0, acc[0]);
+          acc[1] = router_mma<T>(h0, f0.w1, acc[1]);
+        }
+        if (j1 < nks) {
+          const u32x4 h1 = make_h<T>(f1.x, inv, f1.g);
+          if (write_h) st16(hrow + k1, h1);
+          if (do_router) {
+            acc[0] = router_mma<T>(h1, f1.w0, acc[0]);
+            acc[1] = router_mma<T>(h1, f1.w1, acc[1]);
+          }
         }
       }
     }
@@ -232,111 +259,131 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
   if (!do_router) return;
 reduce:
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    s_part[w][4 * q + j][r16] = acc0[j];
-    s_part[w][4 * q + j][16 + r16] = acc1[j];
-  }
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) s_part[w][4 * q + j][16 * c + r16] = acc[c][j];
   __syncthreads();
-  for (int u = threadIdx.x; u < TB * ECB; u += RNTHR) {
-    const int tl = u / ECB, c = u % ECB, e = blockIdx.y * ECB + c, to = tok0 + tl;
+  static_assert(TB * ECBW <= RNTHR, "one output per thread");
+  if (threadIdx.x < TB * ECBW) {
+    const int u = threadIdx.x;
+    const int tl = u / ECBW, c = u % ECBW, e = blockIdx.y * ECBW + c, to = tok0 + tl;
     if (to < a.T && e < E) {
       float v = s_part[0][tl][c];
 #pragma unroll
       for (int ww = 1; ww < RW; ++ww) v += s_part[ww][tl][c];
-      if (a.bias) v += a.bias[e];
+      if (a.bias) v += bias_v;
       a.logits_out[int64_t(to) * E + e] = v;
     }
   }
 }
 
-// Kernel 2: top-k, gates and skip mask, one wave per token.
+// Wave-wide max / min through DPP row shifts (within rows of 16 lanes) and
+// a combine of the four row results read from lanes 15, 31, 47 and 63; every
+// lane gets the result.  No LDS round trips on the dependency chain.
+template <int CTRL> __device__ __forceinline__ int dpp_shr(int v, int ident) {
+  return __builtin_amdgcn_update_dpp(ident, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+  const int ni = __float_as_int(-INFINITY);
+  v = fmaxf(v, __int_as_float(dpp_shr<0x111>(__float_as_int(v), ni)));
+  v = fmaxf(v, __int_as_float(dpp_shr<0x112>(__float_as_int(v), ni)));
+  v = fmaxf(v, __int_as_float(dpp_shr<0x114>(__float_as_int(v), ni)));
+  v = fmaxf(v, __int_as_float(dpp_shr<0x118>(__float_as_int(v), ni)));
+  const int b = __float_as_int(v);
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 15)), __int_as_float(__builtin_amdgcn_readlane(b, 31))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 47)), __int_as_float(__builtin_amdgcn_readlane(b, 63))));
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+  constexpr int big = 0x7FFFFFFF;
+  v = min(v, dpp_shr<0x111>(v, big));
+  v = min(v, dpp_shr<0x112>(v, big));
+  v = min(v, dpp_shr<0x114>(v, big));
+  v = min(v, dpp_shr<0x118>(v, big));
+  return min(min(__builtin_amdgcn_readlane(v, 15), __builtin_amdgcn_readlane(v, 31)),
+             min(__builtin_amdgcn_readlane(v, 47), __builtin_amdgcn_readlane(v, 63)));
+}
+
+// Kernel 2: top-k, gates and skip mask, one wave per token.  k rounds of
+// arg-max: the wave-wide largest remaining logit, then the lowest expert
+// index among the lanes holding it (order: value descending, index
+// ascending).
 __global__ __launch_bounds__(NTHR) void topk_skip_kernel(RouteArgs a) {
-  __shared__ double s_z[NTHR / 64][EMAX];
+  constexpr int NWV = NTHR / 64;
+  __shared__ float s_tg[EMAX], s_tr[EMAX];
+  __shared__ double s_z[NWV][EMAX];
   const int w = wave_id(), l = lane_id();
-  const int t = blockIdx.x * (NTHR / 64) + w;
-  if (t >= a.T) return;
+  const int t_raw = blockIdx.x * NWV + w;
+  const bool valid = t_raw < a.T;
+  const int t = min(t_raw, a.T - 1);
   const int E = a.E, k = a.k;
-  const float* lrow = (a.logits_in ? a.logits_in : a.logits_out) + int64_t(t) * E;
   const int R = (E + 63) / 64;
-  // lane l holds experts l, l+64, ...: logits and both tables, loaded together
-  // (indices clamped so every load is in bounds)
-  float v[4], tg[4], tr[4];
+  const float* lrow = (a.logits_in ? a.logits_in : a.logits_out) + int64_t(t) * E;
+  // lane l holds experts l, l+64, ... (indices clamped: every load in bounds)
+  float v[4];
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int e = min(l + 64 * rr, E - 1);
-    v[rr] = lrow[e];
-    tg[rr] = a.a_gsp[e];
-    tr[rr] = a.a_rcr[e];
+  for (int rr = 0; rr < 4; ++rr) v[rr] = lrow[min(l + 64 * rr, E - 1)];
+  {
+    // tables, shared by the workgroup's tokens (entries >= E are never read)
+    const int e = min(int(threadIdx.x), E - 1);
+    s_tg[threadIdx.x] = a.a_gsp[e];
+    s_tr[threadIdx.x] = a.a_rcr[e];
   }
-  if (a.logits_in != nullptr) {
+  if (valid && a.logits_in != nullptr) {
     float* orow = a.logits_out + int64_t(t) * E;
-    for (int rr = 0; rr < R; ++rr)
-      if (l + 64 * rr < E) orow[l + 64 * rr] = v[rr];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      if (rr < R && l + 64 * rr < E) orow[l + 64 * rr] = v[rr];
   }
-  uint32_t taken = 0;
+  uint32_t avail = 0;  // bit rr: value rr of this lane is a real, not yet taken expert
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr)
+    if (rr < R && l + 64 * rr < E) avail |= 1u << rr;
   int my_e = 0;
   float my_logit = 0.f, top_logit = 0.f;
   for (int i = 0; i < k; ++i) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+    // this lane's candidate: largest available value, lowest index on ties
+    float cv = -INFINITY;
+    int ce = 0x7FFFFFFF;
+    int crr = -1;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      if (((avail >> rr) & 1u) && (crr < 0 || v[rr] > cv)) {
+        cv = v[rr];
+        ce = l + 64 * rr;
+        crr = rr;
+      }
+    }
+    const float m = wave_max_f(cv);
+    const int be = wave_min_i(crr >= 0 && cv == m ? ce : 0x7FFFFFFF);
+    if (ce == be) avail &= ~(1u << crr);
+    if (l == i) {
+      my_e = be;
+      my_logit = m;
+    }
+    if (i == 0) top_logit = m;
+  }
+  // softmax in float64, shifted by the top-1 logit; sums in ascending order
+  const double mx = double(top_logit);
+  const double z = (l < k) ? exp(double(my_logit) - mx) : 0.0;
+  if (a.norm_topk) {
+    if (l < k) s_z[w][l] = z;
+  } else {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int e = l + 64 * rr;
-      if (rr < R && e < E && !((taken >> rr) & 1u)) {
-        if (v[rr] > bv || (v[rr] == bv && e < bi)) {
-          bv = v[rr];
-          bi = e;
-        }
-      }
+      if (rr < R && e < E) s_z[w][e] = exp(double(v[rr]) - mx);
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == l) taken |= 1u << (bi >> 6);
-    if (l == i) {
-      my_e = bi;
-      my_logit = bv;
-    }
-    if (i == 0) top_logit = bv;
   }
-  // softmax in float64, shifted by the top-1 logit; sums in ascending order
-  const double m = double(top_logit);
-  const double z = (l < k) ? exp(double(my_logit) - m) : 0.0;
+  __syncthreads();
   double s = 0.0;
-  if (a.norm_topk) {
-    for (int i = 0; i < k; ++i) s += __shfl(z, i, 64);
-  } else {
-    for (int rr = 0; rr < R; ++rr) {
-      const int e = l + 64 * rr;
-      if (e < E) s_z[w][e] = exp(double(v[rr]) - m);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (int e = 0; e < E; ++e) s += s_z[w][e];
-  }
-  // table values of this lane's selected expert, from the lane that owns it
-  float ag = 0.f, ar = 0.f;
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const float gq = __shfl(tg[rr], my_e & 63, 64), rq = __shfl(tr[rr], my_e & 63, 64);
-    if ((my_e >> 6) == rr) {
-      ag = gq;
-      ar = rq;
-    }
-  }
-  if (l < k) {
+  const int nsum = a.norm_topk ? k : E;
+  for (int i = 0; i < nsum; ++i) s += s_z[w][i];
+  if (valid && l < k) {
     const float g = float(z / s);
     bool keep = true;
     if (l > 0) {
-      const float sg = g * ag;
-      const float sr = g * ar;
+      const float sg = g * s_tg[my_e];
+      const float sr = g * s_tr[my_e];
       const bool lg = sg < a.tau_gsp, lr = sr < a.tau_rcr;
       bool skip;
       switch (a.fusion) {
@@ -394,11 +441,21 @@ hipError_t launch_pack_router(const float* w, void* dst, int E, int H, hipStream
 }
 
 hipError_t launch_route(int dtype, const RouteArgs& a, hipStream_t s) {
-  const dim3 grid1((a.T + TB - 1) / TB, a.logits_in ? 1 : (a.E + ECB - 1) / ECB), block1(RNTHR), block(NTHR);
-  if (dtype == 1)
-    hipLaunchKernelGGL(norm_router_kernel<bf16_t>, grid1, block1, 0, s, a);
-  else
-    hipLaunchKernelGGL(norm_router_kernel<float>, grid1, block1, 0, s, a);
+  static_assert(NTHR == EMAX, "the top-k kernel loads one table entry per thread");
+  const dim3 block1(RNTHR), block(NTHR);
+  const unsigned gx = unsigned((a.T + TB - 1) / TB);
+  // small batches with the pre-split router: one 16-expert column block per
+  // workgroup, so that more workgroups share the router weights
+  const bool narrow = dtype == 1 && a.router_packed && a.logits_in == nullptr && gx <= 8 && a.H <= NARROW_HMAX;
+  if (narrow) {
+    hipLaunchKernelGGL((norm_router_kernel<bf16_t, 1>), dim3(gx, unsigned((a.E + 15) / 16)), block1, 0, s, a);
+  } else {
+    const dim3 grid1(gx, a.logits_in ? 1 : unsigned((a.E + 31) / 32));
+    if (dtype == 1)
+      hipLaunchKernelGGL((norm_router_kernel<bf16_t, 2>), grid1, block1, 0, s, a);
+    else
+      hipLaunchKernelGGL((norm_router_kernel<float, 2>), grid1, block1, 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid2((a.T + NTHR / 64 - 1) / (NTHR / 64));
