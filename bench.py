@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-tables", action="store_true", help="skip timing the offline table builder")
+    p.add_argument("--no-stack", action="store_true", help="skip the 48-layer stack")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the GLM-4.5-Air-shaped layer, the T=32768 run and the dense GEMM ceiling")
     p.add_argument("--cpu-tokens", type=int, default=1024, help="tokens in the oracle's timed sample")
     p.add_argument("--path", type=int, default=0, help="0 auto, 1 grouped, 2 stream")
     p.add_argument("--layout", choices=["packed", "linear"], default="packed",
@@ -185,6 +188,124 @@ class Bench:
         return out
 
 
+def timed(torch, fn, steps, warmup):
+    """Mean ms of fn(i) over `steps` calls after `warmup`, HIP events on the current stream."""
+    for i in range(warmup):
+        fn(i)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        fn(warmup + i)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def layer_roof(S, T, U, n_kept, ms):
+    """Algorithmic bytes and flops of one layer forward (executed slots and
+    active experts only) and the fractions of the HBM and MFMA peaks."""
+    b = U * 3 * S.H * S.I * 2 + S.E * S.H * 4 + T * S.H * 4 + 8 * S.E
+    f = n_kept * 6 * S.H * S.I + 2 * T * S.H * S.E
+    t = ms * 1e-3
+    return {"alg_bytes": b, "alg_flops": f, "hbm_frac": round(b / t / (HBM_PEAK_GBS * 1e9), 4),
+            "mfma_frac": round(f / t / (BF16_PEAK_TFLOPS * 1e12), 4),
+            "roof_us": round(max(b / (HBM_PEAK_GBS * 1e9), f / (BF16_PEAK_TFLOPS * 1e12)) * 1e6, 1)}
+
+
+def extra_prefill(B, name, S, T, rate, steps, warmup, P=None, layer=None):
+    """Whole-layer prefill of another workload (weights drawn on the device),
+    thresholds by on-device quantile mapping on the batch itself, plus the
+    gate/up kernel alone."""
+    torch, ace = B.torch, B.ace
+    from workloads.device import make_layer_device, make_tokens_device
+    if layer is None:
+        P = make_layer_device(S, B.dev, seed=0)
+        layer = ace.AceMoeLayer(P["gamma"], P["w_router"], P["router_bias"], P["w_gate"], P["w_up"],
+                                P["w_down"], P["a_gsp"], P["a_rcr"], S.k, S.norm_topk, "max",
+                                S.rms_eps).packed()
+        del P["w_gate"], P["w_up"], P["w_down"]
+    x = make_tokens_device(S, B.dev, seed=0, step=7, T=T) if T != S.T else P["x"]
+    b = layer.buffers(T)
+    layer.route(x, 0.0, 0.0, b)
+    d = layer.desc(T)
+    ws = torch.empty(ace.moe_calibrate_workspace_bytes(d), dtype=torch.uint8, device=B.dev)
+    tau_t = torch.zeros(2, dtype=torch.float32, device=B.dev)
+    ace.moe_calibrate_thresholds(d, b.topk_idx, b.topk_gate, layer.a_gsp, layer.a_rcr, rate, tau_t, None, ws)
+    tg, tr = [float(v) for v in tau_t.cpu()]
+    ms = timed(torch, lambda i: layer.forward(x, tg, tr, b), steps, warmup)
+    gu = timed(torch, lambda i: layer.experts(T, b, ace.ACE_STAGE_GATEUP), steps, 2)
+    off = b.offsets.cpu().numpy().astype(np.int64)
+    n_kept, U = int(off[-1]), int((np.diff(off) > 0).sum())
+    gu_flops = n_kept * 4 * S.H * S.I
+    gu_bytes = U * 2 * S.H * S.I * 2 + T * S.H * 2 + n_kept * S.I * 2
+    out = {"workload": name, "T": T, "H": S.H, "E": S.E, "I": S.I, "k": S.k, "skip_target": rate,
+           "skip_realized": round(1 - n_kept / (T * S.k), 5), "active_experts": U, "n_kept": n_kept,
+           "tokens_per_s": round(T / (ms * 1e-3), 1), "us_per_layer": round(ms * 1e3, 2),
+           "gateup_us": round(gu * 1e3, 2), "gateup_tflops": round(gu_flops / (gu * 1e-3) / 1e12, 1),
+           "gateup_GBs": round(gu_bytes / (gu * 1e-3) / 1e9, 1)}
+    out.update(layer_roof(S, T, U, n_kept, ms))
+    return out
+
+
+def dense_gemm_ceiling(B, M=32768, reps=10):
+    """bf16 dense GEMM of the gate/up shape (K = H, N = 2I) through torch
+    (hipBLASLt): a measured MFMA ceiling beside the datasheet peak."""
+    torch, S = B.torch, B.S
+    a = torch.randn(M, S.H, device=B.dev, dtype=torch.bfloat16)
+    w = torch.randn(2 * S.I, S.H, device=B.dev, dtype=torch.bfloat16)
+    wt = w.t().contiguous()
+    ms = timed(torch, lambda i: torch.matmul(a, wt), reps, 3)
+    return round(2 * M * S.H * 2 * S.I / (ms * 1e-3) / 1e12, 1)
+
+
+def stack48(B, decode_steps=128, M=8):
+    """48 independent Qwen3-30B-A3B-shaped layers (each with its own Zipf(1.1)
+    router prior; 58 GB of bf16 expert weights) with the residual stream:
+    per-layer thresholds by on-device quantile mapping at 60% on the layers'
+    own prefill inputs, then the 1024-token prefill and decode steps of 8
+    fresh tokens, each step one HIP graph replay of all 48 layers."""
+    torch, ace = B.torch, B.ace
+    import workloads
+    from workloads.device import make_layer_device, make_tokens_device
+    S = workloads.CONFIGS["stack48_layer"]
+    layers, x0 = [], None
+    for l in range(workloads.STACK_LAYERS):
+        P = make_layer_device(S, B.dev, seed=0, layer=l, with_x=(l == 0))
+        if l == 0:
+            x0 = P["x"]
+        layers.append(ace.AceMoeLayer(P["gamma"], P["w_router"], P["router_bias"], P["w_gate"], P["w_up"],
+                                      P["w_down"], P["a_gsp"], P["a_rcr"], S.k, S.norm_topk, "max",
+                                      S.rms_eps).packed())
+        del P
+    st = ace.AceMoeStack(layers)
+    st.calibrate(x0, 0.6)
+    bufs = st.buffers(S.T)
+    pre_ms = timed(torch, lambda i: st.forward(x0, bufs), 5, 1)
+    g, x_in, _ = st.capture(M)
+    xs = make_tokens_device(S, B.dev, seed=0, step=1000, T=decode_steps * M).view(decode_steps, M, S.H)
+
+    def step(i):
+        x_in.copy_(xs[i % decode_steps])
+        g.replay()
+
+    dec_ms = timed(torch, step, decode_steps, 8)
+    nl = len(layers)
+    skip = [1 - n / (S.T * S.k) for n in st.kept]
+    out = {"workload": "48 qwen3_30b_a3b-shaped layers, Zipf(1.1) router priors, residual stream, 60% skip",
+           "layers": nl, "weights_GB": round(nl * 3 * S.E * S.H * S.I * 2 / 1e9, 1),
+           "prefill_tokens": S.T, "prefill_ms": round(pre_ms, 3),
+           "prefill_tokens_per_s": round(S.T / (pre_ms * 1e-3), 1),
+           "prefill_us_per_layer": round(pre_ms * 1e3 / nl, 2),
+           "decode_M": M, "decode_steps": decode_steps, "decode_ms_per_step": round(dec_ms, 4),
+           "decode_us_per_layer": round(dec_ms * 1e3 / nl, 2),
+           "decode_tokens_per_s": round(M / (dec_ms * 1e-3), 1),
+           "calibration_skip_min_max": [round(min(skip), 5), round(max(skip), 5)]}
+    del st, layers, g, bufs
+    torch.cuda.empty_cache()
+    return out
+
+
 def tables_build(B, reps=5):
     """Time moe_build_tables (A^GSP and A^RCR of the layer from its weights,
     done once per checkpoint) on the generated layer's linear weights.
@@ -320,6 +441,16 @@ def main():
         res["decode_us_per_layer"] = {str(m): round(v["us"], 2) for m, v in dec.items()}
         res["decode_detail"] = {str(m): {k2: (round(v2, 4) if isinstance(v2, float) else v2) for k2, v2 in v.items()}
                                 for m, v in dec.items()}
+    if not args.no_extra:
+        import workloads
+        res["glm45_air_shape_prefill"] = extra_prefill(B, "glm45_air_shape MoE layer prefill (Zipf router prior)",
+                                                       workloads.CONFIGS["glm45_air_shape"], 4096, 0.5,
+                                                       max(10, args.steps // 2), 3)
+        res["mfma_bound_T32768"] = extra_prefill(B, "qwen3_30b_a3b layer at T=32768 (MFMA-bound supplement)", S,
+                                                 32768, args.skip, 10, 2, P=B.P, layer=B.layers[0])
+        res["dense_gemm_ceiling_tflops"] = dense_gemm_ceiling(B)
+    if not args.no_stack:
+        res["stack48"] = stack48(B)
     if not args.no_tables:
         res["tables_build"] = tables_build(B)
     if not args.no_cpu_baseline:

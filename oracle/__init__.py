@@ -19,10 +19,10 @@ Pinning status of each function is listed in ``oracle/moe.py`` and
 ``-m "not gpu"`` test; none is "parity unpinned".
 """
 from .moe import (rmsnorm, router_logits, topk_experts, topk_gates, skip_mask, silu, swiglu_expert,
-                  dispatch_order, moe_layer, round_to_bf16, as_f64)
+                  dispatch_order, moe_layer, round_to_bf16, as_f64, store)
 from .thresholds import slot_scores, quantile_thresholds
 from .tables import gsp_raw, gsp_table, rcr_prototypes, rcr_raw, rcr_table, normalise
 
 __all__ = ["rmsnorm", "router_logits", "topk_experts", "topk_gates", "skip_mask", "silu", "swiglu_expert",
-           "dispatch_order", "moe_layer", "round_to_bf16", "as_f64", "slot_scores", "quantile_thresholds",
+           "dispatch_order", "moe_layer", "round_to_bf16", "as_f64", "store", "slot_scores", "quantile_thresholds",
            "gsp_raw", "gsp_table", "rcr_prototypes", "rcr_raw", "rcr_table", "normalise"]

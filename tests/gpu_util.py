@@ -25,14 +25,21 @@ def oracle_thresholds(L: dict, rate: float):
 
 
 class GpuLayer:
-    def __init__(self, L: dict, device, fusion="max", norm_topk=None):
+    """The HIP path on one layer.  ``P``: the layer's device tensors when they
+    were drawn on the device (else copied from L); ``packed``: run with the
+    packed expert weights and pre-split router, the configuration bench.py
+    times."""
+
+    def __init__(self, L: dict, device, fusion="max", norm_topk=None, P=None, packed=False):
         S = L["shape"]
         self.S = S
-        self.P = layer_to_torch(L, device)
+        self.P = layer_to_torch(L, device) if P is None else P
         P = self.P
         self.layer = ace.AceMoeLayer(P["gamma"], P["w_router"], P["router_bias"], P["w_gate"], P["w_up"],
                                      P["w_down"], P["a_gsp"], P["a_rcr"], S.k,
                                      S.norm_topk if norm_topk is None else norm_topk, fusion, S.rms_eps)
+        if packed:
+            self.layer = self.layer.packed()
 
     def run(self, tau_g, tau_r, path=ace.ACE_PATH_AUTO, logits_in=None, x=None, residual=None) -> dict:
         x = self.P["x"] if x is None else x
