@@ -10,7 +10,9 @@ LLMs" (picx.dev summary page): the SwiGLU expert equation and RMSNorm
 factorisation (Theoretical Foundation), the GSP and RCR slot scores
 (Methodology sections 1 and 2), conservative max-fusion and the top-1 rule
 (Methodology section 3), and quantile-mapped thresholds (Efficiency Results,
-Table 6), and the offline GSP and RCR tables (Methodology sections 1-2).
+Table 6), and the offline GSP and RCR tables (Methodology sections 1-2); and
+the batch-level decode expert-pool cap of the ExFold listing page (abstract,
+Tables 1, 5 and 6), without its folding.
 It is written plainly: per-token loops, float64 arithmetic, each
 function stating the passage it follows.
 
@@ -22,7 +24,9 @@ from .moe import (rmsnorm, router_logits, topk_experts, topk_gates, skip_mask, s
                   dispatch_order, moe_layer, round_to_bf16, as_f64, store)
 from .thresholds import slot_scores, quantile_thresholds
 from .tables import gsp_raw, gsp_table, rcr_prototypes, rcr_raw, rcr_table, normalise
+from .pool import pool_scores, expert_pool, cap_expert_pool
 
 __all__ = ["rmsnorm", "router_logits", "topk_experts", "topk_gates", "skip_mask", "silu", "swiglu_expert",
            "dispatch_order", "moe_layer", "round_to_bf16", "as_f64", "store", "slot_scores", "quantile_thresholds",
-           "gsp_raw", "gsp_table", "rcr_prototypes", "rcr_raw", "rcr_table", "normalise"]
+           "gsp_raw", "gsp_table", "rcr_prototypes", "rcr_raw", "rcr_table", "normalise", "pool_scores",
+           "expert_pool", "cap_expert_pool"]
