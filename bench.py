@@ -172,7 +172,30 @@ class Bench:
         n_kept, U = self.counts(bufs)
         return dict(tau=tau, ms=ms, gateup_ms=gu, down_ms=dn, n_kept=n_kept, U=U)
 
+    def graph_ms(self, x, tau, layers, reps=50):
+        """Mean ms of one replay of a HIP graph holding one forward of each
+        layer in `layers` (the rotated copies) on batch x."""
+        torch = self.torch
+        bufs = [lay.buffers(x.shape[0]) for lay in layers]
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for lay, b in zip(layers, bufs):
+                lay.forward(x, tau[0], tau[1], b)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for lay, b in zip(layers, bufs):
+                lay.forward(x, tau[0], tau[1], b)
+        ms = timed(torch, lambda i: g.replay(), reps, 3)
+        return ms, bufs[-1]
+
     def decode(self, tau):
+        """Decode steps of M fresh tokens, thresholds from the prefill
+        calibration.  Primary: all rotated layers in one HIP graph (per-layer
+        time = replay time / layers), as a decode loop runs; also eager
+        back-to-back launches."""
         torch, workloads = self.torch, self.workloads
         from workloads.torch_io import to_torch
         out = {}
@@ -181,10 +204,29 @@ class Bench:
             Sd = workloads.CONFIGS["qwen3_30b_a3b_decode"].with_tokens(M)
             x = to_torch(workloads.make_tokens(Sd, seed=0, step=1), self.dev)
             ms, bufs = self.run_steps(x, tau, max(self.args.steps, 50), self.args.warmup, 0)
+            gms, _ = self.graph_ms(x, tau, self.layers)
+            gms /= len(self.layers)
             n_kept, U = self.counts(bufs)
             wbytes = U * 3 * S.H * S.I * 2
-            out[M] = dict(us=ms * 1e3, U=U, n_kept=n_kept, retained_weight_MB=wbytes / 1e6,
-                          hbm_frac=(wbytes / (ms * 1e-3)) / (HBM_PEAK_GBS * 1e9))
+            out[M] = dict(us=gms * 1e3, eager_us=ms * 1e3, U=U, n_kept=n_kept, retained_weight_MB=wbytes / 1e6,
+                          hbm_frac=(wbytes / (gms * 1e-3)) / (HBM_PEAK_GBS * 1e9))
+        return out
+
+    def decode_pool(self, tau, pools=(16, 32), Ms=(8, 32, 64)):
+        """Decode with the batch-level expert-pool cap m (graph replays)."""
+        workloads = self.workloads
+        from workloads.torch_io import to_torch
+        out = {}
+        for m in pools:
+            layers = [lay.with_pool(m) for lay in self.layers]
+            row = {}
+            for M in Ms:
+                Sd = workloads.CONFIGS["qwen3_30b_a3b_decode"].with_tokens(M)
+                x = to_torch(workloads.make_tokens(Sd, seed=0, step=1), self.dev)
+                gms, b = self.graph_ms(x, tau, layers)
+                n_kept, U = self.counts(b)
+                row[str(M)] = {"us": round(gms * 1e3 / len(layers), 2), "U": U, "n_kept": n_kept}
+            out[f"pool_{m}"] = row
         return out
 
 
@@ -439,6 +481,8 @@ def main():
     if not args.no_decode:
         dec = B.decode(head["tau"])
         res["decode_us_per_layer"] = {str(m): round(v["us"], 2) for m, v in dec.items()}
+        res["decode_eager_us_per_layer"] = {str(m): round(v["eager_us"], 2) for m, v in dec.items()}
+        res["decode_pool"] = B.decode_pool(head["tau"])
         res["decode_detail"] = {str(m): {k2: (round(v2, 4) if isinstance(v2, float) else v2) for k2, v2 in v.items()}
                                 for m, v in dec.items()}
     if not args.no_extra:

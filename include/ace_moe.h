@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define ACE_MOE_ABI_VERSION 1
+#define ACE_MOE_ABI_VERSION 2
 
 typedef enum {
   ACE_OK = 0,
@@ -101,6 +101,8 @@ typedef struct {
   int32_t router_layout; /* ACE_LAYOUT_LINEAR: w_router is float32 [E, H];
                             ACE_LAYOUT_PACKED (bf16 only): the planes made by
                             moe_pack_router */
+  int32_t expert_pool;   /* 0: off.  m >= 1: batch-level expert-pool cap in
+                            moe_dispatch (see there); T*k <= 8192 */
 } ace_moe_desc;
 
 int moe_abi_version(void);
@@ -145,6 +147,15 @@ ace_status moe_route_skip(const ace_moe_desc* d, const void* x, const float* gam
  *      sorted_token [T*k] i32 and sorted_gate [T*k] f32, first n_kept
  *      entries valid; slot_pos [T*k] i32: the sorted row of slot (t,i), or
  *      -1 when the slot is skipped.
+ * Expert-pool cap (desc->expert_pool = m >= 1; decode batches): the batch's
+ * retained experts are every expert that is some token's top-1, plus, up to
+ * m experts in all, the others with the largest S_e = sum of the gates of
+ * the kept slots routed to e (float32, slot order), lower index first on
+ * ties; kept slots of other experts are skipped as well (slot_pos -1,
+ * nothing folded or renormalised).  Reading of the decode pool of "ExFold:
+ * Unified Expert Folding for Training-Free MoE Prefill-Decode Acceleration"
+ * (abstract; Tables 1, 5, 6) without its folding.  The keep array is not
+ * modified: slot_pos >= 0 marks the slots that run.
  * workspace: >= moe_workspace_bytes(d) bytes of device memory.
  */
 ace_status moe_dispatch(const ace_moe_desc* d, const int32_t* topk_idx, const float* topk_gate, const uint8_t* keep,

@@ -30,6 +30,8 @@ import math
 
 import numpy as np
 
+from .pool import cap_expert_pool
+
 
 def as_f64(a: np.ndarray) -> np.ndarray:
     """Values of a stored tensor as float64.  uint16 arrays hold bf16 bit patterns
@@ -216,7 +218,7 @@ class _ExpertCache:
 
 def moe_layer(x, gamma, w_router, router_bias, w_gate, w_up, w_down, a_gsp, a_rcr,
               tau_gsp: float, tau_rcr: float, k: int, norm_topk: bool = True, rms_eps: float = 1e-6,
-              dtype: str = "f32", logits=None, tokens=None, fusion: str = "max") -> dict:
+              dtype: str = "f32", logits=None, tokens=None, fusion: str = "max", expert_pool: int = 0) -> dict:
     """Forward of one routed SwiGLU MoE layer with ACE slot skipping.
 
     y_t = Σ over kept slots i (ascending) of g_{t,i}·f_{e_i}(x_t); no residual.
@@ -224,7 +226,9 @@ def moe_layer(x, gamma, w_router, router_bias, w_gate, w_up, w_down, a_gsp, a_rc
     that routing can be shared with another implementation.  ``tokens``
     restricts the expert computation to those token rows (y of other rows is
     left as NaN).  Returns h, logits, idx, gate, keep, y (float64) and the
-    per-slot gated outputs ``slot_out[(t, i)]``."""
+    per-slot gated outputs ``slot_out[(t, i)]``.  ``expert_pool`` = m >= 1
+    applies the batch-level expert-pool cap (``oracle.pool``) after the skip
+    rule; the returned keep is the capped mask."""
     h = rmsnorm(x, gamma, rms_eps, dtype)
     T = h.shape[0]
     E = np.asarray(w_router).shape[0]
@@ -237,6 +241,8 @@ def moe_layer(x, gamma, w_router, router_bias, w_gate, w_up, w_down, a_gsp, a_rc
         idx[t] = topk_experts(logits[t], k)
         gate[t] = topk_gates(logits[t], idx[t], norm_topk)
     keep = skip_mask(idx, gate, a_gsp, a_rcr, tau_gsp, tau_rcr, fusion)
+    if expert_pool:
+        keep = cap_expert_pool(idx, gate, keep, E, expert_pool)
     experts = _ExpertCache(w_gate, w_up, w_down)
     rows = range(T) if tokens is None else [int(t) for t in tokens]
     y = np.full((T, h.shape[1]), np.nan)

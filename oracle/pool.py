@@ -11,9 +11,10 @@ Readings where the page is silent (also listed in the design notes):
   * S_e = the sum of the gates of the batch's kept slots routed to e,
     accumulated in float32 in slot order (t ascending, then i), the same
     precision and order as the kernel, since it decides an integer ranking;
-  * every expert that is some token's top-1 is retained (the ACE rule keeps
-    top-1 slots), so the pool holds max(m, #distinct top-1 experts) experts:
-    top-1 experts first, then by S_e descending, lower index first on ties;
+  * every expert that is some token's top-1 (slot 0) is retained (the ACE
+    rule keeps top-1 slots), so the pool can exceed m when the batch has more
+    distinct top-1 experts; the remaining places go to the other experts that
+    have a kept slot, by S_e descending, lower index first on ties;
   * a kept slot whose expert is outside the pool is skipped; nothing is
     folded or renormalised.
 
@@ -39,13 +40,19 @@ def pool_scores(idx: np.ndarray, gate: np.ndarray, keep: np.ndarray, E: int) -> 
 
 
 def expert_pool(idx: np.ndarray, gate: np.ndarray, keep: np.ndarray, E: int, m: int) -> np.ndarray:
-    """Boolean [E]: the retained experts."""
+    """Boolean [E]: the retained experts.  Every top-1 expert (slot 0 of some
+    token), then, while the pool holds fewer than m experts, the other
+    experts with a kept slot by S_e descending, lower index first."""
     S = pool_scores(idx, gate, keep, E)
+    keep = np.asarray(keep, dtype=bool)
     top1 = set(int(e) for e in idx[:, 0]) if idx.shape[0] else set()
-    order = sorted(range(E), key=lambda e: (e not in top1, -float(S[e]), e))
-    size = max(int(m), len(top1))
+    active = set(int(e) for e in np.asarray(idx)[keep])
+    others = sorted((e for e in active if e not in top1), key=lambda e: (-float(S[e]), e))
     pool = np.zeros(E, dtype=bool)
-    pool[order[:size]] = True
+    for e in top1:
+        pool[e] = True
+    for e in others[:max(int(m) - len(top1), 0)]:
+        pool[e] = True
     return pool
 
 

@@ -30,14 +30,15 @@ class GpuLayer:
     packed expert weights and pre-split router, the configuration bench.py
     times."""
 
-    def __init__(self, L: dict, device, fusion="max", norm_topk=None, P=None, packed=False):
+    def __init__(self, L: dict, device, fusion="max", norm_topk=None, P=None, packed=False, expert_pool=0):
         S = L["shape"]
         self.S = S
         self.P = layer_to_torch(L, device) if P is None else P
         P = self.P
         self.layer = ace.AceMoeLayer(P["gamma"], P["w_router"], P["router_bias"], P["w_gate"], P["w_up"],
                                      P["w_down"], P["a_gsp"], P["a_rcr"], S.k,
-                                     S.norm_topk if norm_topk is None else norm_topk, fusion, S.rms_eps)
+                                     S.norm_topk if norm_topk is None else norm_topk, fusion, S.rms_eps,
+                                     expert_pool=expert_pool)
         if packed:
             self.layer = self.layer.packed()
 

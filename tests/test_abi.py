@@ -35,13 +35,13 @@ def test_library_exports_every_declared_symbol():
     for f in header_functions():
         assert hasattr(lib, f), f
     assert set(header_functions()) <= set(m._lib.EXPORTS)
-    assert m.moe_abi_version() == 1
+    assert m.moe_abi_version() == 2
 
 
 def test_desc_layout_matches_header():
     m, _ = _lib()
-    # eleven 4-byte fields, no padding
-    assert ctypes.sizeof(m.MoeDesc) == 44
+    # twelve 4-byte fields, no padding
+    assert ctypes.sizeof(m.MoeDesc) == 48
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -58,11 +58,13 @@ def test_desc_layout_matches_header():
     (dict(weight_layout=3), 1, "weight_layout=3"),
     (dict(router_layout=2), 1, "router_layout=2"),
     (dict(router_layout=1, dtype=0), 2, "router_layout=PACKED"),
+    (dict(expert_pool=-1), 1, "expert_pool=-1"),
+    (dict(expert_pool=4, T=2049), 2, "expert_pool needs T*k <= 8192"),
 ])
 def test_bad_descriptors_are_rejected_before_launch(kw, status, needle):
     m, lib = _lib()
     base = dict(T=8, H=256, E=16, I=128, k=4, dtype=1, norm_topk=1, fusion=0, rms_eps=1e-6, weight_layout=0,
-                router_layout=0)
+                router_layout=0, expert_pool=0)
     base.update(kw)
     d = m.MoeDesc(**base)
     fake = 0x1000  # never dereferenced: validation fails first

@@ -274,6 +274,37 @@ def test_qwen3_decode_steps(qwen, dev, M):
         assert rel_l2(values(gp["y"]), ref["y"]) <= TOL["bf16"]
 
 
+# ---------------------------------------------------------------- decode expert-pool cap
+@pytest.mark.parametrize("M,pool", [(1, 1), (4, 2), (8, 4), (8, 16), (32, 8), (32, 40), (64, 16), (64, 300)])
+def test_decode_expert_pool(qwen, dev, M, pool):
+    """Batch-level expert-pool cap in moe_dispatch against oracle.cap_expert_pool:
+    the GPU routes with the oracle's own logits (logits_in); which slots run,
+    the dispatch order and y must match."""
+    L, tg, tr = qwen
+    S = workloads.CONFIGS["qwen3_30b_a3b_decode"].with_tokens(M)
+    x = workloads.make_tokens(S, seed=0, step=2)
+    Ld = dict(L, x=x, shape=S)
+    h = oracle.rmsnorm(x, L["gamma"], S.rms_eps, S.dtype)
+    lg = oracle.router_logits(h, L["w_router"], L["router_bias"])
+    ref = oracle.moe_layer(x, L["gamma"], L["w_router"], L["router_bias"], L["w_gate"], L["w_up"], L["w_down"],
+                           L["a_gsp"], L["a_rcr"], tg, tr, S.k, S.norm_topk, S.rms_eps, S.dtype, logits=lg,
+                           expert_pool=pool)
+    for packed in (False, True):
+        gl = GpuLayer(Ld, dev, packed=packed, expert_pool=pool)
+        g = gl.run(tg, tr, logits_in=lg)
+        assert np.array_equal(g["topk_idx"], ref["idx"])
+        assert np.array_equal(g["slot_pos"] >= 0, ref["keep"]), "capped keep differs"
+        off, tok, slot, pos = oracle.dispatch_order(ref["idx"], ref["keep"], S.E)
+        n = int(off[-1])
+        assert np.array_equal(g["offsets"], off)
+        assert np.array_equal(g["sorted_token"][:n], tok)
+        assert np.array_equal(g["slot_pos"], pos)
+        assert np.array_equal(g["sorted_gate"][:n].view(np.uint32), ref["gate"][tok, slot].view(np.uint32))
+        assert rel_l2(values(g["y"]), ref["y"]) <= TOL["bf16"]
+        U = int((np.diff(off) > 0).sum())
+        assert U <= max(pool, len(set(ref["idx"][:, 0].tolist())))
+
+
 # ---------------------------------------------------------------- on-device quantile mapping
 def _calibrate(gl, g, rate, dev):
     S = gl.S

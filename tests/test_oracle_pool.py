@@ -30,28 +30,32 @@ def test_hand_case():
     # equal scores: the lower index wins
     gate2 = np.array([[0.6, 0.4], [0.6, 0.4]], dtype=np.float32)
     assert oracle.expert_pool(idx, gate2, keep, 5, 3).tolist() == [True, True, False, True, False]
+    # a top-1 expert counts even when its slot is not kept; experts without a
+    # kept slot never take a place
+    keep2 = np.array([[False, True], [True, False]])
+    assert oracle.expert_pool(idx, gate, keep2, 5, 3).tolist() == [True, True, False, True, False]
 
 
 def test_brute_force_best_pool():
-    """Among all pools of the allowed size that contain every top-1 expert,
-    the chosen one maximises the retained gate mass (float32 scores); the
-    kept slots are exactly those inside it."""
+    """Among all pools made of every top-1 expert plus the allowed number of
+    other experts with a kept slot, the chosen one maximises the retained
+    gate mass (float32 scores), lower indices first on equal mass; the kept
+    slots are exactly those inside it."""
     rng = np.random.default_rng(3)
-    for trial in range(30):
+    for trial in range(40):
         T, E, k = int(rng.integers(1, 5)), int(rng.integers(3, 8)), 2
         idx, gate, keep = _batch(rng, T, E, k)
         m = int(rng.integers(1, E + 1))
         S = oracle.pool_scores(idx, gate, keep, E)
         top1 = set(idx[:, 0].tolist())
-        size = max(m, len(top1))
+        cands = sorted(set(idx[keep].tolist()) - top1)
+        extra = min(max(m - len(top1), 0), len(cands))
         best = None
-        for c in itertools.combinations(range(E), size):
-            if not top1 <= set(c):
-                continue
+        for c in itertools.combinations(cands, extra):
             mass = sum(float(S[e]) for e in c)
-            key = (mass, [-e for e in sorted(c)])
+            key = (mass, [-e for e in c])
             if best is None or key > best[0]:
-                best = (key, set(c))
+                best = (key, set(c) | top1)
         pool = oracle.expert_pool(idx, gate, keep, E, m)
         assert set(np.flatnonzero(pool).tolist()) == best[1]
         new = oracle.cap_expert_pool(idx, gate, keep, E, m)

@@ -39,14 +39,14 @@ class MoeDesc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("dtype", ctypes.c_int32), ("norm_topk", ctypes.c_int32),
                 ("fusion", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("weight_layout", ctypes.c_int32),
-                ("router_layout", ctypes.c_int32)]
+                ("router_layout", ctypes.c_int32), ("expert_pool", ctypes.c_int32)]
 
 
 ACE_LAYOUT_LINEAR, ACE_LAYOUT_PACKED = 0, 1
 
 
 def make_desc(T, H, E, I, k, dtype, norm_topk=1, fusion="max", rms_eps=1e-6, weight_layout=0,
-              router_layout=0) -> MoeDesc:
+              router_layout=0, expert_pool=0) -> MoeDesc:
     if isinstance(dtype, torch.dtype):
         dtype = {torch.float32: ACE_F32, torch.bfloat16: ACE_BF16}[dtype]
     elif isinstance(dtype, str):
@@ -54,7 +54,7 @@ def make_desc(T, H, E, I, k, dtype, norm_topk=1, fusion="max", rms_eps=1e-6, wei
     if isinstance(fusion, str):
         fusion = FUSION[fusion]
     return MoeDesc(int(T), int(H), int(E), int(I), int(k), int(dtype), int(norm_topk), int(fusion), float(rms_eps),
-                   int(weight_layout), int(router_layout))
+                   int(weight_layout), int(router_layout), int(expert_pool))
 
 
 _lib = None

@@ -72,6 +72,9 @@ ace_status check_desc(const ace_moe_desc* d) {
     return fail(ACE_EINVAL, "router_layout=%d is not an ace_weight_layout", d->router_layout);
   if (d->router_layout == ACE_LAYOUT_PACKED && d->dtype != ACE_BF16)
     return fail(ACE_EUNSUPPORTED, "router_layout=PACKED needs bf16 activations");
+  if (d->expert_pool < 0) return fail(ACE_EINVAL, "expert_pool=%d must be >= 0", d->expert_pool);
+  if (d->expert_pool > 0 && int64_t(d->T) * d->k > 8192)
+    return fail(ACE_EUNSUPPORTED, "expert_pool needs T*k <= 8192 (got %lld)", (long long)(int64_t(d->T) * d->k));
   if (d->E > 256) return fail(ACE_EUNSUPPORTED, "E=%d > 256", d->E);
   if (d->k > 16 || d->k > d->E) return fail(ACE_EUNSUPPORTED, "k=%d must be <= min(E, 16)", d->k);
   if (d->H % 128 != 0) return fail(ACE_EUNSUPPORTED, "H=%d is not a multiple of 128", d->H);
@@ -184,6 +187,7 @@ ace_status moe_dispatch(const ace_moe_desc* d, const int32_t* topk_idx, const fl
     a.T = d->T;
     a.E = d->E;
     a.k = d->k;
+    a.pool = d->expert_pool;
     hipError_t e = ace::launch_dispatch(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail("dispatch launch", e);
     return ok();

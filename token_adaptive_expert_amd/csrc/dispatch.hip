@@ -17,6 +17,19 @@
 //      its wave's running row for that expert + the popcount of the mask bits
 //      of lower lanes.
 // Every result is a function of the inputs alone, independent of timing.
+//
+// With the batch-level expert-pool cap (POOL), step 3 keeps each kept slot's
+// row (and expert) in LDS instead of writing it; then
+//   4. per expert, S_e = the sum of its kept gates in row order (= slot
+//      order), the number of experts that are some token's top-1, and the
+//      rank of every other active expert by (S_e descending, index
+//      ascending) among the compacted list of such experts; retained = top-1
+//      expert or rank < m - #top-1; new offsets from the retained counts;
+//   5. every slot's final row = its expert's new offset + its row inside the
+//      expert's segment (unchanged: a retained expert keeps all its slots).
+// Reading of the decode expert pool of "ExFold: Unified Expert Folding for
+// Training-Free MoE Prefill-Decode Acceleration" (abstract; Tables 1, 5, 6),
+// without the folding of excluded experts.
 #include "kernels.h"
 
 namespace ace {
@@ -25,6 +38,7 @@ namespace {
 constexpr int NW = 16;
 constexpr int NTHR = NW * 64;
 constexpr int EMAX = 256;
+constexpr int POOL_SLOTS = 8192;  // slots (T*k) the pool variant keeps in LDS
 
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -50,11 +64,42 @@ __device__ __forceinline__ SlotVals load_slot(const DispatchArgs& a, int64_t s, 
 }
 }  // namespace
 
+// Exclusive scan of one int per thread over the workgroup (thread order);
+// returns the exclusive prefix, total in *total.  Contains barriers: every
+// thread of the workgroup must call it.
+__device__ __forceinline__ int block_excl_scan(int v, int32_t* s_wsum, int* total) {
+  const int w = wave_id(), l = lane_id();
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(inc, o, 64);
+    if (l >= o) inc += u;
+  }
+  if (l == 63) s_wsum[w] = inc;
+  __syncthreads();
+  int base = 0, all = 0;
+  for (int ww = 0; ww < NW; ++ww) {
+    if (ww < w) base += s_wsum[ww];
+    all += s_wsum[ww];
+  }
+  __syncthreads();
+  *total = all;
+  return base + inc - v;
+}
+
+template <bool POOL>
 __global__ __launch_bounds__(NTHR) void dispatch_kernel(DispatchArgs a) {
   __shared__ uint32_t s_bits[NW][EMAX][2];
   __shared__ int32_t s_run[NW][EMAX];
   __shared__ int32_t s_off[EMAX + 1];
   __shared__ int32_t s_wsum[NTHR / 64];
+  // pool variant only
+  __shared__ int32_t s_pos[POOL ? POOL_SLOTS : 1];  // (row << 8) | expert, or -1
+  __shared__ float s_sg[POOL ? POOL_SLOTS : 1];     // gates by pre-cap row
+  __shared__ float s_S[POOL ? EMAX : 1];
+  __shared__ int32_t s_flag[POOL ? EMAX : 1];       // bit 0: top-1 expert; bit 1: retained
+  __shared__ int32_t s_list[POOL ? EMAX : 1];
+  __shared__ int32_t s_noff[POOL ? EMAX : 1];
   const int w = wave_id(), l = lane_id(), tid = threadIdx.x;
   const int E = a.E, k = a.k;
   const int64_t nslots = int64_t(a.T) * k;
@@ -62,15 +107,19 @@ __global__ __launch_bounds__(NTHR) void dispatch_kernel(DispatchArgs a) {
   const int cpw = (nchunks + NW - 1) / NW;
   const int c0 = w * cpw, c1 = min(nchunks, c0 + cpw);
 
-  // 1. per-wave expert counts
+  // 1. per-wave expert counts (and, with the pool, the top-1 experts)
   for (int e = l; e < E; e += 64) s_run[w][e] = 0;
-  wave_sync_lds();
+  if (POOL && tid < EMAX) s_flag[tid] = 0;
+  __syncthreads();
   if (c0 < c1) {
     SlotVals cur = load_slot(a, int64_t(c0) * 64 + l, nslots, false);
     for (int c = c0; c < c1; ++c) {
       const SlotVals nxt = load_slot(a, int64_t(min(c + 1, c1 - 1)) * 64 + l, nslots, false);
       const int64_t s = int64_t(c) * 64 + l;
-      if (s < nslots && cur.kept && unsigned(cur.e) < unsigned(E)) atomicAdd(&s_run[w][cur.e], 1);
+      if (s < nslots && unsigned(cur.e) < unsigned(E)) {
+        if (cur.kept) atomicAdd(&s_run[w][cur.e], 1);
+        if (POOL && s % k == 0) s_flag[cur.e] = 1;  // top-1 expert (kept or not)
+      }
       cur = nxt;
     }
   }
@@ -85,27 +134,21 @@ __global__ __launch_bounds__(NTHR) void dispatch_kernel(DispatchArgs a) {
       tot += v;
     }
   }
-  int inc = tot;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(inc, o, 64);
-    if (l >= o) inc += v;
-  }
-  if (l == 63) s_wsum[w] = inc;
-  __syncthreads();
+  int all = 0;
+  const int excl = block_excl_scan(tot, s_wsum, &all);
   if (tid < E) {
-    int base = 0;
-    for (int ww = 0; ww < w; ++ww) base += s_wsum[ww];
-    const int excl = base + inc - tot;
     s_off[tid] = excl;
-    a.offsets[tid] = excl;
-    if (tid == E - 1) a.offsets[E] = excl + tot;
+    if (!POOL) a.offsets[tid] = excl;
+  }
+  if (tid == 0) {
+    s_off[E] = all;
+    if (!POOL) a.offsets[E] = all;
   }
   __syncthreads();
   for (int e = l; e < E; e += 64) s_run[w][e] += s_off[e];
   wave_sync_lds();
 
-  // 3. scatter, chunk by chunk in slot order
+  // 3. rows, chunk by chunk in slot order
   if (c0 < c1) {
     const uint64_t below = (uint64_t(1) << l) - 1u;
     SlotVals cur = load_slot(a, int64_t(c0) * 64 + l, nslots, true);
@@ -124,17 +167,74 @@ __global__ __launch_bounds__(NTHR) void dispatch_kernel(DispatchArgs a) {
         if (live) {
           const uint64_t m = uint64_t(s_bits[w][cur.e][0]) | (uint64_t(s_bits[w][cur.e][1]) << 32);
           const int pos = s_run[w][cur.e] + __popcll(m & below);
-          a.sorted_token[pos] = int(s / k);
-          a.sorted_gate[pos] = cur.g;
-          a.slot_pos[s] = pos;
+          if (POOL) {
+            s_pos[s] = (pos << 8) | cur.e;
+            s_sg[pos] = cur.g;
+          } else {
+            a.sorted_token[pos] = int(s / k);
+            a.sorted_gate[pos] = cur.g;
+            a.slot_pos[s] = pos;
+          }
         } else {
-          a.slot_pos[s] = -1;
+          if (POOL) s_pos[s] = -1;
+          else a.slot_pos[s] = -1;
         }
       }
       wave_sync_lds();
       for (int e = l; e < E; e += 64) s_run[w][e] += __popc(s_bits[w][e][0]) + __popc(s_bits[w][e][1]);
       wave_sync_lds();
       cur = nxt;
+    }
+  }
+  if constexpr (POOL) {
+    __syncthreads();
+    // 4. pool: scores, top-1 count, candidate ranks, retained experts
+    const bool is_e = tid < E;
+    const int n_e = is_e ? s_off[tid + 1] - s_off[tid] : 0;
+    const bool top1 = is_e && (s_flag[tid] & 1);
+    float S = 0.f;
+    for (int p = 0; p < n_e; ++p) S += s_sg[s_off[tid] + p];
+    if (is_e) s_S[tid] = S;
+    const bool cand = is_e && n_e > 0 && !top1;
+    int n_top1 = 0, n_cand = 0;
+    const int ctop = block_excl_scan(top1 ? 1 : 0, s_wsum, &n_top1);
+    (void)ctop;
+    const int cpos = block_excl_scan(cand ? 1 : 0, s_wsum, &n_cand);
+    if (cand) s_list[cpos] = tid;
+    __syncthreads();
+    const int budget = max(a.pool - n_top1, 0);
+    bool keep_e = top1;
+    if (cand && budget > 0) {
+      int rank = 0;
+      for (int j = 0; j < n_cand; ++j) {
+        const int e2 = s_list[j];
+        const float S2 = s_S[e2];
+        rank += (S2 > S || (S2 == S && e2 < tid)) ? 1 : 0;
+      }
+      keep_e = rank < budget;
+    }
+    if (is_e) s_flag[tid] = keep_e ? 2 : 0;
+    int kept_all = 0;
+    const int nexcl = block_excl_scan(keep_e ? n_e : 0, s_wsum, &kept_all);
+    if (is_e) {
+      s_noff[tid] = nexcl;
+      a.offsets[tid] = nexcl;
+    }
+    if (tid == 0) a.offsets[E] = kept_all;
+    __syncthreads();
+    // 5. final rows
+    for (int64_t s = tid; s < nslots; s += NTHR) {
+      const int v = s_pos[s];
+      int out = -1;
+      if (v >= 0) {
+        const int e = v & 255, row = v >> 8;
+        if (s_flag[e] & 2) {
+          out = s_noff[e] + (row - s_off[e]);
+          a.sorted_token[out] = int(s / k);
+          a.sorted_gate[out] = s_sg[row];
+        }
+      }
+      a.slot_pos[s] = out;
     }
   }
 }
@@ -146,7 +246,10 @@ size_t dispatch_workspace_bytes(int T, int E) {
 }
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(NTHR), 0, s, a);
+  if (a.pool > 0)
+    hipLaunchKernelGGL(dispatch_kernel<true>, dim3(1), dim3(NTHR), 0, s, a);
+  else
+    hipLaunchKernelGGL(dispatch_kernel<false>, dim3(1), dim3(NTHR), 0, s, a);
   return hipGetLastError();
 }
 

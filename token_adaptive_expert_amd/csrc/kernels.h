@@ -33,6 +33,7 @@ struct DispatchArgs {
   float* sorted_gate;
   int32_t* slot_pos;
   int T, E, k;
+  int pool;  // 0: off; m >= 1: batch-level expert-pool cap (T*k <= 8192)
 };
 
 struct ExpertArgs {

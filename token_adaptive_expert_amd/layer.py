@@ -6,6 +6,7 @@ buffers (torch) and calls moe_route_skip -> moe_dispatch -> moe_expert_forward
 """
 from __future__ import annotations
 
+import copy
 import dataclasses
 
 import torch
@@ -67,7 +68,7 @@ class AceMoeLayer:
 
     def __init__(self, gamma, w_router, router_bias, w_gate, w_up, w_down, a_gsp, a_rcr, k, norm_topk=1,
                  fusion="max", rms_eps=1e-6, weight_layout=_lib.ACE_LAYOUT_LINEAR,
-                 router_layout=_lib.ACE_LAYOUT_LINEAR, H=None):
+                 router_layout=_lib.ACE_LAYOUT_LINEAR, H=None, expert_pool=0):
         self.gamma, self.w_router, self.router_bias = gamma, w_router, router_bias
         self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
         self.a_gsp, self.a_rcr = a_gsp, a_rcr
@@ -76,10 +77,11 @@ class AceMoeLayer:
         self.dtype = w_gate.dtype
         self.weight_layout = int(weight_layout)
         self.router_layout = int(router_layout)
+        self.expert_pool = int(expert_pool)  # 0: off; m: batch-level expert-pool cap in dispatch
 
     def desc(self, T: int):
         return _lib.make_desc(T, self.H, self.E, self.I, self.k, self.dtype, self.norm_topk, self.fusion, self.rms_eps,
-                              self.weight_layout, self.router_layout)
+                              self.weight_layout, self.router_layout, self.expert_pool)
 
     def packed(self, stream=None, router=True) -> "AceMoeLayer":
         """The same layer with its expert weights copied into the packed layout
@@ -99,7 +101,15 @@ class AceMoeLayer:
             _lib.moe_pack_router(d, self.w_router, w_router, stream)
             rl = _lib.ACE_LAYOUT_PACKED
         return AceMoeLayer(self.gamma, w_router, self.router_bias, out[0], out[1], out[2], self.a_gsp, self.a_rcr,
-                           self.k, self.norm_topk, self.fusion, self.rms_eps, _lib.ACE_LAYOUT_PACKED, rl)
+                           self.k, self.norm_topk, self.fusion, self.rms_eps, _lib.ACE_LAYOUT_PACKED, rl,
+                           expert_pool=self.expert_pool)
+
+    def with_pool(self, m: int) -> "AceMoeLayer":
+        """The same layer (same tensors) with the batch-level expert-pool cap m
+        (0: off) applied in dispatch."""
+        out = copy.copy(self)
+        out.expert_pool = int(m)
+        return out
 
     def buffers(self, T: int) -> LayerBuffers:
         return LayerBuffers.allocate(T, self.H, self.E, self.I, self.k, self.dtype, self.w_gate.device)
