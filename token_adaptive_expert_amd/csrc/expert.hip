@@ -100,7 +100,7 @@ __device__ __forceinline__ void find_tile(int g, int nb_count, int BM, int E, co
 }
 
 template <typename T, int RB, int NW, int KIND, int STAGES>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ACE_WAVES_PER_EU)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB <= 2 ? 4 : ACE_WAVES_PER_EU)))
 void expert_gemm_kernel(ExpertArgs a) {
   constexpr int EPL = St<T>::EPL;
   constexpr int KS = 4 * EPL;      // k values per k-step
@@ -171,6 +171,21 @@ void expert_gemm_kernel(ExpertArgs a) {
       wstep = KS * int(sizeof(T));
     }
 
+    // weight chunks ride a register ring of STAGES chunks: while chunk c is
+    // multiplied, the next STAGES-1 chunks are in flight.  The first chunks'
+    // loads go out before the slot rows' sources are read (they depend only
+    // on the tile), so the tile's start pays one memory latency, not two.
+    u32x4 wA[2][4], wB[2][4], wC[2][4];
+    auto load_w = [&](u32x4 (&dst)[2][4], int c) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        dst[0][s] = buf_ld16(wr0, wv, ws[0] + (c * 4 + s) * wstep);
+        dst[1][s] = buf_ld16(wr1, wv, ws[1] + (c * 4 + s) * wstep);
+      }
+    };
+    load_w(wA, 0);
+    if (STAGES == 3 && nch > 1) load_w(wB, 1);
+
     // staged-row sources of this thread's units (byte offsets into A).  Rows
     // past the tile's last slot row re-read that row: their MFMA output rows
     // are never stored (an output row depends only on its own input row), and
@@ -192,16 +207,7 @@ void expert_gemm_kernel(ExpertArgs a) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) acc[rb][0] = acc[rb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // weight chunks ride a register ring of STAGES chunks: while chunk c is
-    // multiplied, the next STAGES-1 chunks are in flight
-    u32x4 wA[2][4], wB[2][4], wC[2][4], xr[UPT];
-    auto load_w = [&](u32x4 (&dst)[2][4], int c) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        dst[0][s] = buf_ld16(wr0, wv, ws[0] + (c * 4 + s) * wstep);
-        dst[1][s] = buf_ld16(wr1, wv, ws[1] + (c * 4 + s) * wstep);
-      }
-    };
+    u32x4 xr[UPT];
     auto load_x = [&](int c) {
       const int koff = c * KC * int(sizeof(T));
 #pragma unroll
@@ -234,8 +240,6 @@ void expert_gemm_kernel(ExpertArgs a) {
     };
 
     load_x(0);
-    load_w(wA, 0);
-    if (STAGES == 3 && nch > 1) load_w(wB, 1);
     store_x(0);
     __syncthreads();
     if constexpr (STAGES == 3) {
@@ -475,9 +479,14 @@ hipError_t launch_pack(int dtype, const void* src, void* dst, int E, int N, int 
 hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs& a, int T, int k, int num_cu,
                          hipStream_t s) {
   constexpr int G = ACE_GROUPED_RB, S = ACE_GROUPED_STAGES;
+  // moderate batches (up to 64 routed slots per expert on average before
+  // skipping): 32-row tiles, more of them, less padding
+  const bool small_rb = int64_t(T) * k <= int64_t(64) * a.E && G > 2;
   if (dtype == 1) {
     if (stream_path)
       return kind == 0 ? launch_splitk<bf16_t, 0>(a, T, k, num_cu, s) : launch_splitk<bf16_t, 1>(a, T, k, num_cu, s);
+    if (small_rb)
+      return kind == 0 ? launch_one<bf16_t, 2, 4, 0, S>(a, T, k, s) : launch_one<bf16_t, 2, 4, 1, S>(a, T, k, s);
     return kind == 0 ? launch_one<bf16_t, G, 4, 0, S>(a, T, k, s)
                      : launch_one<bf16_t, G, 4, 1, S>(a, T, k, s);
   }
