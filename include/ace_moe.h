@@ -10,7 +10,9 @@
  * sections 1-3), never skipping the top-1 slot.
  *
  * Conventions shared by every entry point
- *   - Tensor pointers are DEVICE pointers, row-major, owned by the caller.
+ *   - Tensor pointers are DEVICE pointers, row-major, owned by the caller,
+ *     16-byte aligned (torch allocations are); a misaligned pointer is
+ *     rejected with ACE_EINVAL naming it.
  *     The library never allocates, frees or synchronises; every call only
  *     enqueues kernels on `stream` (a hipStream_t, NULL = default stream).
  *   - Activations (x, h, act, y) and expert weights use desc->dtype
@@ -143,6 +145,9 @@ ace_status moe_route_skip(const ace_moe_desc* d, const void* x, const float* gam
  * moe_dispatch -- group the kept slots by expert ("expert dispatch" on the
  * article page about ACE).  Deterministic: within an expert, slots follow
  * token order; no floating-point atomics are used.
+ * In:  topk_idx [T,k] (each row k distinct experts, as moe_route_skip
+ *      writes them; rows with a repeated expert give unspecified results),
+ *      topk_gate [T,k], keep [T,k].
  * Out: expert_offsets [E+1] i32 (segment starts; [E] = n_kept);
  *      sorted_token [T*k] i32 and sorted_gate [T*k] f32, first n_kept
  *      entries valid; slot_pos [T*k] i32: the sorted row of slot (t,i), or

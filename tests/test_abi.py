@@ -156,3 +156,17 @@ def test_build_tables_validation():
     assert "LINEAR" in lib.moe_last_error().decode()
     big = m.make_desc(1, 4096, 128, 1408, 8, "bf16")
     assert lib.moe_tables_workspace_bytes(ctypes.byref(big)) < (512 + 64) << 20
+
+
+def test_misaligned_pointers_rejected():
+    m, lib = _lib()
+    d = m.make_desc(8, 256, 16, 128, 4, "bf16")
+    f = 0x1000
+    st = lib.moe_route_skip(ctypes.byref(d), f + 4, f, f, None, None, f, f, f, 0.0, 0.0, f, f, f, f, None)
+    assert st == 1 and "x is not 16-byte aligned" in lib.moe_last_error().decode()
+    st = lib.moe_route_skip(ctypes.byref(d), f, f, f, f + 8, None, f, f, f, 0.0, 0.0, f, f, f, f, None)
+    assert st == 1 and "router_bias is not 16-byte aligned" in lib.moe_last_error().decode()
+    st = lib.moe_dispatch(ctypes.byref(d), f, f, f + 1, f, f, f, f, f, 1 << 20, None)
+    assert st == 1 and "keep is not 16-byte aligned" in lib.moe_last_error().decode()
+    st = lib.moe_combine(ctypes.byref(d), f, f, f + 2, f, None)
+    assert st == 1 and "residual is not 16-byte aligned" in lib.moe_last_error().decode()

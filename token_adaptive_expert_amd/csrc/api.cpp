@@ -90,8 +90,18 @@ ace_status check_desc(const ace_moe_desc* d) {
   return ACE_OK;
 }
 
-#define REQUIRE(p) \
-  if ((p) == nullptr) return fail(ACE_EINVAL, "%s is NULL", #p)
+// Device pointers: required ones must be non-NULL; all must be 16-byte
+// aligned (the kernels use 16-byte vector loads and stores).
+#define REQUIRE(p)                                                                                     \
+  do {                                                                                                 \
+    if ((p) == nullptr) return fail(ACE_EINVAL, "%s is NULL", #p);                                     \
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return fail(ACE_EINVAL, "%s is not 16-byte aligned", #p); \
+  } while (0)
+#define ALIGNED_OR_NULL(p)                                                                           \
+  do {                                                                                               \
+    if ((p) != nullptr && reinterpret_cast<uintptr_t>(p) % 16 != 0)                                  \
+      return fail(ACE_EINVAL, "%s is not 16-byte aligned", #p);                                      \
+  } while (0)
 
 }  // namespace
 
@@ -118,6 +128,8 @@ ace_status moe_route_skip(const ace_moe_desc* d, const void* x, const float* gam
     if (logits_in == nullptr) REQUIRE(w_router);
     REQUIRE(logits_out);
     if (logits_in == logits_out) return fail(ACE_EINVAL, "logits_in and logits_out must not alias");
+    ALIGNED_OR_NULL(router_bias);
+    ALIGNED_OR_NULL(logits_in);
     REQUIRE(a_gsp);
     REQUIRE(a_rcr);
     REQUIRE(h_out);
@@ -287,6 +299,7 @@ ace_status moe_combine(const ace_moe_desc* d, const int32_t* slot_pos, const flo
     ace::CombineArgs a;
     a.slot_pos = slot_pos;
     a.slot_out = slot_out;
+    ALIGNED_OR_NULL(residual);
     a.residual = residual;
     a.y = y;
     a.T = d->T;
@@ -334,6 +347,7 @@ ace_status moe_calibrate_thresholds(const ace_moe_desc* d, const int32_t* topk_i
     a.a_gsp = a_gsp;
     a.a_rcr = a_rcr;
     a.tau_out = tau_out;
+    ALIGNED_OR_NULL(level_out);
     a.level_out = level_out;
     a.T = d->T;
     a.k = d->k;

@@ -35,6 +35,12 @@ namespace {
 #ifndef ACE_WAVES_PER_EU
 #define ACE_WAVES_PER_EU 3    // occupancy target given to the register allocator
 #endif
+#ifndef ACE_GATEUP_NW
+#define ACE_GATEUP_NW 4       // waves per grouped gate/up tile (16 intermediate units each)
+#endif
+#ifndef ACE_DOWN_NW
+#define ACE_DOWN_NW 4         // waves per grouped down tile (32 output columns each)
+#endif
 #ifndef ACE_LDS_PITCH
 #define ACE_LDS_PITCH 272     // padded LDS row pitch of the staged slot rows
 #endif
@@ -485,10 +491,11 @@ hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs
   if (dtype == 1) {
     if (stream_path)
       return kind == 0 ? launch_splitk<bf16_t, 0>(a, T, k, num_cu, s) : launch_splitk<bf16_t, 1>(a, T, k, num_cu, s);
+    constexpr int NG = ACE_GATEUP_NW, ND = ACE_DOWN_NW;
     if (small_rb)
-      return kind == 0 ? launch_one<bf16_t, 2, 4, 0, S>(a, T, k, s) : launch_one<bf16_t, 2, 4, 1, S>(a, T, k, s);
-    return kind == 0 ? launch_one<bf16_t, G, 4, 0, S>(a, T, k, s)
-                     : launch_one<bf16_t, G, 4, 1, S>(a, T, k, s);
+      return kind == 0 ? launch_one<bf16_t, 2, NG, 0, S>(a, T, k, s) : launch_one<bf16_t, 2, ND, 1, S>(a, T, k, s);
+    return kind == 0 ? launch_one<bf16_t, G, NG, 0, S>(a, T, k, s)
+                     : launch_one<bf16_t, G, ND, 1, S>(a, T, k, s);
   }
   if (stream_path)
     return kind == 0 ? launch_splitk<float, 0>(a, T, k, num_cu, s) : launch_splitk<float, 1>(a, T, k, num_cu, s);
