@@ -41,6 +41,10 @@ namespace {
 #ifndef ACE_DOWN_NW
 #define ACE_DOWN_NW 4         // waves per grouped down tile (32 output columns each)
 #endif
+#ifndef ACE_XCD_COLUMNS
+#define ACE_XCD_COLUMNS 1     // (expert, n-block) columns dealt round-robin over the XCDs: 0 never,
+                              // 1 for the down projection (measured faster there), 2 for both kinds
+#endif
 #ifndef ACE_LDS_PITCH
 #define ACE_LDS_PITCH 272     // padded LDS row pitch of the staged slot rows
 #endif
@@ -105,6 +109,71 @@ __device__ __forceinline__ void find_tile(int g, int nb_count, int BM, int E, co
   rows = min(BM, s_off[e + 1] - row0);
 }
 
+// Column-dealt tile list for one XCD.  A column is one (expert, n-block) pair
+// with all of the expert's m-tiles; column c = e*nbc + nb goes to XCD c % 8,
+// so a heavily loaded expert's columns spread over every XCD while each
+// column's m-tiles (which reuse its weights) stay on one XCD's L2.  Wave 0
+// writes s_pref[e] = exclusive prefix over experts of this XCD's tiles of
+// expert e (its columns on the XCD times its m-tiles); s_off = expert_offsets.
+template <int BM>
+__device__ __forceinline__ int xcd_cols(int e, int x, int nbc) {
+  const int r0 = (x - (e * nbc) % NXCD + NXCD) % NXCD;  // first n-block of expert e on XCD x
+  return r0 < nbc ? (nbc - 1 - r0) / NXCD + 1 : 0;
+}
+
+template <int BM>
+__device__ __forceinline__ void build_xcd_tile_list(const ExpertArgs& a, int x, int nbc, int32_t* s_pref,
+                                                    int32_t* s_off) {
+  if (wave_id() != 0) return;
+  const int l = lane_id(), E = a.E;
+  int cnt[4], loc = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = l * 4 + j;
+    int c = 0;
+    if (e < E) {
+      const int o0 = a.offsets[e], o1 = a.offsets[e + 1];
+      s_off[e] = o0;
+      c = (o1 - o0 + BM - 1) / BM * xcd_cols<BM>(e, x, nbc);
+    }
+    cnt[j] = c;
+    loc += c;
+  }
+  int inc = loc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(inc, o, 64);
+    if (l >= o) inc += v;
+  }
+  int run = inc - loc;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = l * 4 + j;
+    if (e < E) s_pref[e] = run;
+    run += cnt[j];
+  }
+  if (l == 63) s_pref[E] = inc;
+  if (l == 0) s_off[E] = a.offsets[E];
+}
+
+// The j-th tile of XCD x's list: expert, n-block, first sorted row, row count.
+template <int BM>
+__device__ __forceinline__ void find_xcd_tile(int j, int x, int nbc, int E, const int32_t* s_pref,
+                                              const int32_t* s_off, int& e, int& nb, int& row0, int& rows) {
+  int lo = 0, hi = E;  // invariant: s_pref[lo] <= j < s_pref[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_pref[mid] <= j) lo = mid; else hi = mid;
+  }
+  e = lo;
+  const int mt_e = (s_off[e + 1] - s_off[e] + BM - 1) / BM;
+  const int local = j - s_pref[e];
+  const int ck = local / mt_e, mtl = local - ck * mt_e;
+  nb = (x - (e * nbc) % NXCD + NXCD) % NXCD + NXCD * ck;
+  row0 = s_off[e] + mtl * BM;
+  rows = min(BM, s_off[e + 1] - row0);
+}
+
 template <typename T, int RB, int NW, int KIND, int STAGES>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB <= 2 ? 4 : ACE_WAVES_PER_EU)))
 void expert_gemm_kernel(ExpertArgs a) {
@@ -127,26 +196,35 @@ void expert_gemm_kernel(ExpertArgs a) {
   const int nch = K / KC;
   const int nb_count = N / ROWS_PER_WG;
 
-  build_tile_list<BM>(a, s_pref, s_off);
+  constexpr bool COLS = ACE_XCD_COLUMNS == 2 || (ACE_XCD_COLUMNS == 1 && KIND == 1);
+  const int xcd = int(blockIdx.x % NXCD);
+  if (COLS)
+    build_xcd_tile_list<BM>(a, xcd, nb_count, s_pref, s_off);
+  else
+    build_tile_list<BM>(a, s_pref, s_off);
   __syncthreads();
 
-  const int total_mt = s_pref[E];
-  const int ntiles = total_mt * nb_count;
-  const T* A = reinterpret_cast<const T*>(a.A);
+  const int ntiles = COLS ? s_pref[E] : s_pref[E] * nb_count;  // this XCD's / all tiles
 
-  // Tile order: expert-major, then n-block, then the expert's m-tiles, so
-  // that tiles sharing slot rows (same m-tile) or weights (same n-block) are
-  // neighbours.  The list is cut into NXCD contiguous parts, one per XCD:
-  // workgroup id i runs on XCD i % NXCD (round-robin dispatch) and takes the
-  // (i / NXCD)-th tile of that XCD's part, so neighbours share one L2.  One
+  // Tile placement: workgroup id i runs on XCD i % NXCD (round-robin
+  // dispatch) and takes the (i / NXCD)-th tile of that XCD's list.  With
+  // column dealing (the down projection by default) an XCD's list holds every
+  // 8th (expert, n-block) column, each column's m-tiles consecutive, so every
+  // XCD streams a share of every expert and a column's weights are reused
+  // from one L2.  Otherwise (gate/up) the expert-major list is cut into NXCD
+  // contiguous parts, so that the n-blocks of one m-tile share its slot rows.  One
   // tile per workgroup; the hardware dispatcher refills a compute unit as soon
   // as one of its tiles finishes, which balances uneven per-CU bandwidth.
-  const int per_xcd = (ntiles + NXCD - 1) / NXCD;
+  const int per_xcd = COLS ? ntiles : (ntiles + NXCD - 1) / NXCD;
   for (int wg = blockIdx.x; wg < NXCD * per_xcd; wg += gridDim.x) {
-    const int g = (wg % NXCD) * per_xcd + wg / NXCD;
-    if (g >= ntiles) continue;
     int e, nb, row0, rows;
-    find_tile(g, nb_count, BM, E, s_pref, s_off, e, nb, row0, rows);
+    if (COLS) {
+      find_xcd_tile<BM>(wg / NXCD, xcd, nb_count, E, s_pref, s_off, e, nb, row0, rows);
+    } else {
+      const int g = (wg % NXCD) * per_xcd + wg / NXCD;
+      if (g >= ntiles) continue;
+      find_tile(g, nb_count, BM, E, s_pref, s_off, e, nb, row0, rows);
+    }
     const int nrb = (rows + 15) >> 4;
 
     // Weights are read with buffer loads: the expert's matrix base lives in a
@@ -458,11 +536,12 @@ hipError_t launch_one(const ExpertArgs& a, int ntok, int k, hipStream_t s) {
   constexpr int ROWS_PER_WG = (KIND == 0) ? NW * 16 : NW * 32;
   const int64_t slots = int64_t(ntok) * k;
   const int64_t mt_bound = (slots + BM - 1) / BM + std::min<int64_t>(a.E, slots);
-  const int64_t tiles_bound = mt_bound * (a.N / ROWS_PER_WG);
-  // the grid covers the largest possible tile count (a multiple of NXCD);
-  // workgroups past the actual count exit at once
-  const int64_t grid = std::max<int64_t>(NXCD, std::min<int64_t>((tiles_bound + NXCD - 1) / NXCD * NXCD,
-                                                                   int64_t(1) << 30));
+  const int64_t nbc = a.N / ROWS_PER_WG;
+  // the grid covers the largest possible tile count of any XCD (times NXCD);
+  // workgroups past their XCD's actual count exit at once
+  constexpr bool COLS = ACE_XCD_COLUMNS == 2 || (ACE_XCD_COLUMNS == 1 && KIND == 1);
+  const int64_t per_xcd_bound = COLS ? (nbc + NXCD - 1) / NXCD * mt_bound : (mt_bound * nbc + NXCD - 1) / NXCD;
+  const int64_t grid = std::max<int64_t>(NXCD, std::min<int64_t>(per_xcd_bound * NXCD, int64_t(1) << 30));
   hipLaunchKernelGGL((expert_gemm_kernel<T, RB, NW, KIND, STAGES>), dim3(unsigned(grid)), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
