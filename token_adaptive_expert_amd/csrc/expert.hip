@@ -175,7 +175,8 @@ __device__ __forceinline__ void find_xcd_tile(int j, int x, int nbc, int E, cons
 }
 
 template <typename T, int RB, int NW, int KIND, int STAGES>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB <= 2 ? 4 : ACE_WAVES_PER_EU)))
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(RB <= 2 ? 4 : (RB >= 8 ? 2 : ACE_WAVES_PER_EU))))
 void expert_gemm_kernel(ExpertArgs a) {
   constexpr int EPL = St<T>::EPL;
   constexpr int KS = 4 * EPL;      // k values per k-step
@@ -565,12 +566,18 @@ hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs
                          hipStream_t s) {
   constexpr int G = ACE_GROUPED_RB, S = ACE_GROUPED_STAGES;
   // moderate batches (up to 64 routed slots per expert on average before
-  // skipping): 32-row tiles, more of them, less padding
+  // skipping): 32-row tiles, more of them, less padding.  Very large batches
+  // (at least 512 slots per expert): 128-row tiles of 8 waves, which halve
+  // the L2 traffic per MFMA when the GEMMs become compute-bound.
   const bool small_rb = int64_t(T) * k <= int64_t(64) * a.E && G > 2;
+  // (the 8-wave down tile covers 256 output columns: H must be a multiple of 256)
+  const bool big_rb = int64_t(T) * k >= int64_t(512) * a.E && a.N % (kind == 0 ? 128 : 256) == 0;
   if (dtype == 1) {
     if (stream_path)
       return kind == 0 ? launch_splitk<bf16_t, 0>(a, T, k, num_cu, s) : launch_splitk<bf16_t, 1>(a, T, k, num_cu, s);
     constexpr int NG = ACE_GATEUP_NW, ND = ACE_DOWN_NW;
+    if (big_rb)
+      return kind == 0 ? launch_one<bf16_t, 8, 8, 0, 2>(a, T, k, s) : launch_one<bf16_t, 8, 8, 1, 2>(a, T, k, s);
     if (small_rb)
       return kind == 0 ? launch_one<bf16_t, 2, NG, 0, S>(a, T, k, s) : launch_one<bf16_t, 2, ND, 1, S>(a, T, k, s);
     return kind == 0 ? launch_one<bf16_t, G, NG, 0, S>(a, T, k, s)
