@@ -195,6 +195,24 @@ ace_status moe_combine(const ace_moe_desc* d, const int32_t* slot_pos, const flo
                        void* y, void* stream);
 
 /*
+ * moe_forward -- the whole layer in one call: moe_route_skip, moe_dispatch,
+ * moe_expert_forward (path) and moe_combine with the arguments of those four
+ * calls (same meanings, layouts and outputs; residual may be NULL).  For
+ * decode-sized batches (1 <= T <= 8, desc->expert_pool = 0, logits_in NULL,
+ * path AUTO or STREAM) the top-k, gates, skip rule and dispatch run inside
+ * the gate/up kernel's workgroups (two fewer dependent launches); every
+ * output is bit-identical to the four separate calls.  All arguments are
+ * validated before anything is launched.
+ */
+ace_status moe_forward(const ace_moe_desc* d, int32_t path, const void* x, const float* gamma, const float* w_router,
+                       const float* router_bias, const float* logits_in, float* logits_out, const float* a_gsp,
+                       const float* a_rcr, float tau_gsp, float tau_rcr, const void* w_gate, const void* w_up,
+                       const void* w_down, const void* residual, void* h_out, int32_t* topk_idx, float* topk_gate,
+                       uint8_t* keep, int32_t* expert_offsets, int32_t* sorted_token, float* sorted_gate,
+                       int32_t* slot_pos, void* act, float* slot_out, void* y, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
  * moe_calibrate_thresholds -- per-layer thresholds (tau_gsp, tau_rcr) by
  * quantile mapping (Efficiency Results, Table 6) for a target skip rate over
  * all T*k routed slots, matched to the given batch's own routing.

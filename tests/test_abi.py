@@ -170,3 +170,23 @@ def test_misaligned_pointers_rejected():
     assert st == 1 and "keep is not 16-byte aligned" in lib.moe_last_error().decode()
     st = lib.moe_combine(ctypes.byref(d), f, f, f + 2, f, None)
     assert st == 1 and "residual is not 16-byte aligned" in lib.moe_last_error().decode()
+
+
+def test_forward_validates_before_launch():
+    m, lib = _lib()
+    d = m.make_desc(4, 256, 16, 128, 4, "bf16")
+    f = 0x1000
+    args = [f] * 6 + [f, f]  # x..a_rcr (logits_in NULL handled below)
+    # y NULL
+    st = lib.moe_forward(ctypes.byref(d), 0, f, f, f, None, None, f, f, f, 0.0, 0.0, f, f, f, None, f, f, f, f, f, f,
+                         f, f, f, f, None, f, 1 << 20, None)
+    assert st == 1 and "y is NULL" in lib.moe_last_error().decode()
+    st = lib.moe_forward(ctypes.byref(d), 7, f, f, f, None, None, f, f, f, 0.0, 0.0, f, f, f, None, f, f, f, f, f, f,
+                         f, f, f, f, f, f, 1 << 20, None)
+    assert st == 1 and "path=7" in lib.moe_last_error().decode()
+    st = lib.moe_forward(ctypes.byref(d), 0, f, f, f, None, None, f, f, f, 0.0, 0.0, f, f, f, None, f, f, f, f, f, f,
+                         f, f, f, f, f, f, 16, None)
+    assert st == 3
+    d0 = m.make_desc(0, 256, 16, 128, 4, "bf16")
+    assert lib.moe_forward(ctypes.byref(d0), 0, f, f, f, None, None, f, f, f, 0.0, 0.0, f, f, f, None, f, f, f, f, f,
+                           f, f, f, f, f, f, f, 1 << 20, None) == 0

@@ -278,6 +278,49 @@ def test_qwen3_decode_steps(qwen, dev, M):
         assert rel_l2(values(gp["y"]), ref["y"]) <= TOL["bf16"]
 
 
+# ---------------------------------------------------------------- fused small-batch forward
+def _fused_vs_steps(layer, x, tg, tr, residual):
+    M = x.shape[0]
+    b1, b2 = layer.buffers(M), layer.buffers(M)
+    for b in (b1, b2):
+        for t in (b.act, b.slot_out, b.sorted_token, b.sorted_gate, b.slot_pos, b.offsets, b.y, b.topk_idx):
+            if t.is_floating_point():
+                t.fill_(float("nan"))
+            else:
+                t.fill_(-7)
+    layer.forward(x, tg, tr, b1, residual=residual)
+    layer.forward_steps(x, tg, tr, b2, residual=residual)
+    torch.cuda.synchronize()
+    n = int(b1.offsets[-1].item())
+    assert n == int(b2.offsets[-1].item())
+    for name in ("h", "logits", "topk_idx", "topk_gate", "keep", "offsets", "slot_pos", "y"):
+        a1, a2 = getattr(b1, name), getattr(b2, name)
+        assert torch.equal(a1.view(torch.uint8), a2.view(torch.uint8)), name
+    for name in ("sorted_token", "sorted_gate", "act", "slot_out"):
+        a1, a2 = getattr(b1, name)[:n], getattr(b2, name)[:n]
+        assert torch.equal(a1.view(torch.uint8), a2.view(torch.uint8)), name
+
+
+@pytest.mark.parametrize("M", [1, 3, 8])
+@pytest.mark.parametrize("packed", [False, True])
+def test_fused_forward_matches_steps(qwen, dev, M, packed):
+    """moe_forward at decode sizes (top-k, gates, skip rule and dispatch inside
+    the gate/up workgroups) equals the four step calls bit for bit."""
+    L, tg, tr = qwen
+    S = workloads.CONFIGS["qwen3_30b_a3b_decode"].with_tokens(M)
+    Ld = dict(L, x=workloads.make_tokens(S, seed=0, step=3), shape=S)
+    gl = GpuLayer(Ld, dev, packed=packed)
+    _fused_vs_steps(gl.layer, gl.P["x"], float(tg), float(tr), gl.P["x"])
+
+
+@pytest.mark.parametrize("fusion", ["max", "min", "mean", "score"])
+def test_fused_forward_matches_steps_f32(tiny, dev, fusion):
+    L, tg, tr = tiny
+    gl = GpuLayer(L, dev, fusion=fusion)
+    x = gl.P["x"][:6].contiguous()
+    _fused_vs_steps(gl.layer, x, float(tg), float(tr), None)
+
+
 # ---------------------------------------------------------------- decode expert-pool cap
 @pytest.mark.parametrize("M,pool", [(1, 1), (4, 2), (8, 4), (8, 16), (32, 8), (32, 40), (64, 16), (64, 300)])
 def test_decode_expert_pool(qwen, dev, M, pool):

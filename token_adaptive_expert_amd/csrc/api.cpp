@@ -92,6 +92,13 @@ ace_status check_desc(const ace_moe_desc* d) {
 
 // Device pointers: required ones must be non-NULL; all must be 16-byte
 // aligned (the kernels use 16-byte vector loads and stores).
+// Largest batch that moe_forward runs through the fused small-batch kernel
+// (at most ace::FUSED_TMAX).
+#ifndef ACE_FUSED_TOKENS
+#define ACE_FUSED_TOKENS 8
+#endif
+static_assert(ACE_FUSED_TOKENS <= ace::FUSED_TMAX, "fused kernel: one wave per token");
+
 #define REQUIRE(p)                                                                                     \
   do {                                                                                                 \
     if ((p) == nullptr) return fail(ACE_EINVAL, "%s is NULL", #p);                                     \
@@ -402,6 +409,141 @@ ace_status moe_pack_router(const ace_moe_desc* d, const float* w_router, void* d
     return ok();
   } catch (...) {
     return fail(ACE_EHIP, "unexpected host exception in moe_pack_router");
+  }
+}
+
+ace_status moe_forward(const ace_moe_desc* d, int32_t path, const void* x, const float* gamma, const float* w_router,
+                       const float* router_bias, const float* logits_in, float* logits_out, const float* a_gsp,
+                       const float* a_rcr, float tau_gsp, float tau_rcr, const void* w_gate, const void* w_up,
+                       const void* w_down, const void* residual, void* h_out, int32_t* topk_idx, float* topk_gate,
+                       uint8_t* keep, int32_t* expert_offsets, int32_t* sorted_token, float* sorted_gate,
+                       int32_t* slot_pos, void* act, float* slot_out, void* y, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  try {
+    ace_status st = check_desc(d);
+    if (st != ACE_OK) return st;
+    if (path < ACE_PATH_AUTO || path > ACE_PATH_STREAM) return fail(ACE_EINVAL, "path=%d is not an ace_path", path);
+    // every argument is checked before anything is launched
+    REQUIRE(x);
+    REQUIRE(gamma);
+    if (logits_in == nullptr) REQUIRE(w_router);
+    REQUIRE(logits_out);
+    if (logits_in == logits_out) return fail(ACE_EINVAL, "logits_in and logits_out must not alias");
+    ALIGNED_OR_NULL(router_bias);
+    ALIGNED_OR_NULL(logits_in);
+    ALIGNED_OR_NULL(residual);
+    REQUIRE(a_gsp);
+    REQUIRE(a_rcr);
+    REQUIRE(w_gate);
+    REQUIRE(w_up);
+    REQUIRE(w_down);
+    REQUIRE(h_out);
+    REQUIRE(topk_idx);
+    REQUIRE(topk_gate);
+    REQUIRE(keep);
+    REQUIRE(expert_offsets);
+    REQUIRE(sorted_token);
+    REQUIRE(sorted_gate);
+    REQUIRE(slot_pos);
+    REQUIRE(act);
+    REQUIRE(slot_out);
+    REQUIRE(y);
+    REQUIRE(workspace);
+    if (!(tau_gsp >= 0.f) || !(tau_rcr >= 0.f))
+      return fail(ACE_EINVAL, "thresholds must be >= 0 (got %g, %g)", double(tau_gsp), double(tau_rcr));
+    const size_t need = ace::dispatch_workspace_bytes(std::max(d->T, 1), d->E);
+    if (workspace_bytes < need) return fail(ACE_EWORKSPACE, "workspace_bytes=%zu < %zu needed", workspace_bytes, need);
+    if (d->T == 0) return ok();
+    const bool fused = d->T <= ACE_FUSED_TOKENS && d->expert_pool == 0 && logits_in == nullptr &&
+                       path != ACE_PATH_GROUPED;
+    if (!fused) {
+      st = moe_route_skip(d, x, gamma, w_router, router_bias, logits_in, logits_out, a_gsp, a_rcr, tau_gsp, tau_rcr,
+                          h_out, topk_idx, topk_gate, keep, stream);
+      if (st != ACE_OK) return st;
+      st = moe_dispatch(d, topk_idx, topk_gate, keep, expert_offsets, sorted_token, sorted_gate, slot_pos, workspace,
+                        workspace_bytes, stream);
+      if (st != ACE_OK) return st;
+      st = moe_expert_forward(d, path, h_out, w_gate, w_up, w_down, expert_offsets, sorted_token, sorted_gate, act,
+                              slot_out, workspace, workspace_bytes, stream);
+      if (st != ACE_OK) return st;
+      return moe_combine(d, slot_pos, slot_out, residual, y, stream);
+    }
+    int ncu = 0;
+    st = num_cu(&ncu);
+    if (st != ACE_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ace::RouteArgs r{};
+    r.x = x;
+    r.gamma = gamma;
+    r.w_router = w_router;
+    r.bias = router_bias;
+    r.logits_in = nullptr;
+    r.logits_out = logits_out;
+    r.h_out = h_out;
+    r.T = d->T;
+    r.H = d->H;
+    r.E = d->E;
+    r.k = d->k;
+    r.eps = d->rms_eps;
+    r.router_packed = d->router_layout == ACE_LAYOUT_PACKED ? 1 : 0;
+    hipError_t e = ace::launch_route(d->dtype, r, s, false);
+    if (e != hipSuccess) return hip_fail("router launch", e);
+    ace::FusedArgs f{};
+    f.g.A = h_out;
+    f.g.W0 = w_gate;
+    f.g.W1 = w_up;
+    f.g.out = act;
+    f.g.K = d->H;
+    f.g.N = d->I;
+    f.g.E = d->E;
+    f.g.packed = d->weight_layout == ACE_LAYOUT_PACKED ? 1 : 0;
+    f.g.A_rows = d->T;
+    f.logits = logits_out;
+    f.a_gsp = a_gsp;
+    f.a_rcr = a_rcr;
+    f.tau_gsp = tau_gsp;
+    f.tau_rcr = tau_rcr;
+    f.T = d->T;
+    f.k = d->k;
+    f.norm_topk = d->norm_topk;
+    f.fusion = d->fusion;
+    f.topk_idx = topk_idx;
+    f.topk_gate = topk_gate;
+    f.keep = keep;
+    f.offsets = expert_offsets;
+    f.sorted_token = sorted_token;
+    f.sorted_gate = sorted_gate;
+    f.slot_pos = slot_pos;
+    e = ace::launch_fused_gateup(d->dtype, f, ncu, s);
+    if (e != hipSuccess) return hip_fail("fused gate/up launch", e);
+    ace::ExpertArgs dn{};
+    dn.A = act;
+    dn.W0 = w_down;
+    dn.W1 = nullptr;
+    dn.offsets = expert_offsets;
+    dn.sorted_token = sorted_token;
+    dn.sorted_gate = sorted_gate;
+    dn.out = slot_out;
+    dn.K = d->I;
+    dn.N = d->H;
+    dn.E = d->E;
+    dn.packed = f.g.packed;
+    dn.A_rows = d->T * d->k;
+    e = ace::launch_expert(d->dtype, 1, true, dn, d->T, d->k, ncu, s);
+    if (e != hipSuccess) return hip_fail("down launch", e);
+    ace::CombineArgs c{};
+    c.slot_pos = slot_pos;
+    c.slot_out = slot_out;
+    c.residual = residual;
+    c.y = y;
+    c.T = d->T;
+    c.H = d->H;
+    c.k = d->k;
+    e = ace::launch_combine(d->dtype, c, s);
+    if (e != hipSuccess) return hip_fail("combine launch", e);
+    return ok();
+  } catch (...) {
+    return fail(ACE_EHIP, "unexpected host exception in moe_forward");
   }
 }
 

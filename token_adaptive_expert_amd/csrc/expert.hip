@@ -20,6 +20,7 @@
 // kept slot produce no tile, so their weights are never read) and takes the
 // tile of its index.
 #include "kernels.h"
+#include "topk.h"
 
 namespace ace {
 
@@ -51,6 +52,7 @@ namespace {
 
 constexpr int ROWB = 256;        // bytes of one row per chunk
 constexpr int NXCD = 8;          // XCDs of an MI355X; only tile placement depends on it
+constexpr int EMAX_EXP = 256;    // largest expert count
 constexpr int LDS_PITCH = ACE_LDS_PITCH;
 
 // Tile list of the dispatched slots (wave 0 writes it to LDS): expert e has
@@ -495,7 +497,10 @@ __global__ __launch_bounds__(SK_NW * 64) void expert_splitk_kernel(ExpertArgs a)
 // so an uncapped worst-case grid would mostly pay that prologue).  k-steps
 // per load batch: 8 for gate/up (K = H), 4 for down (K = I; fewer registers,
 // more resident workgroups).
-constexpr int SK_WG_PER_CU = 8;
+#ifndef ACE_SK_WG_PER_CU
+#define ACE_SK_WG_PER_CU 2      // grid cap per CU of the split-K kernel (measured best for decode)
+#endif
+constexpr int SK_WG_PER_CU = ACE_SK_WG_PER_CU;
 
 template <typename T, int KIND>
 hipError_t launch_splitk(const ExpertArgs& a, int ntok, int k, int num_cu, hipStream_t s) {
@@ -508,6 +513,214 @@ hipError_t launch_splitk(const ExpertArgs& a, int ntok, int k, int num_cu, hipSt
   hipLaunchKernelGGL((expert_splitk_kernel<T, KIND, KIND == 0 ? 8 : 4>), dim3(unsigned(grid)), dim3(SK_NW * 64), 0,
                      s, a);
   return hipGetLastError();
+}
+
+// Fused small-batch gate/up (decode, T <= FUSED_TMAX): instead of reading
+// the outputs of a separate top-k kernel and a dispatch kernel, every
+// workgroup derives them from the router logits in LDS (a few hundred slots
+// at most): wave t runs topk_slots for token t (the same code and bits as
+// the routing kernel); kept (expert, token) pairs set bit t of a per-expert
+// token mask, so expert e's count is the mask's popcount and slot (t, i)'s
+// row is offset[e] + popcount(mask[e] below bit t) (token order, as in
+// moe_dispatch); then the split-K tiles run as in expert_splitk_kernel.
+// Workgroup 0 writes topk_idx, topk_gate, keep, expert_offsets,
+// sorted_token, sorted_gate and slot_pos for the later kernels (down
+// projection, combine) and the caller.  Saves two dependent launches.
+template <typename T>
+__global__ __launch_bounds__(SK_NW * 64) void expert_splitk_fused_kernel(FusedArgs f) {
+  constexpr int EPL = St<T>::EPL;
+  constexpr int KS = 4 * EPL;
+  constexpr int BM = 16;
+  constexpr int COLS = 16;
+  constexpr int SK_NBK = 8;
+  constexpr int MAXS = FUSED_TMAX * 16;
+  static_assert(SK_NW >= FUSED_TMAX, "one wave per token");
+  __shared__ float s_tg[EMAX_EXP], s_tr[EMAX_EXP];
+  __shared__ double s_z[FUSED_TMAX][EMAX_EXP];
+  __shared__ int32_t s_idx[MAXS];
+  __shared__ float s_gate[MAXS];
+  __shared__ uint8_t s_keep[MAXS];
+  __shared__ uint32_t s_mask[EMAX_EXP];
+  __shared__ int32_t s_pref[EMAX_EXP + 1];
+  __shared__ int32_t s_off[EMAX_EXP + 1];
+  __shared__ int32_t s_tok[MAXS];
+  __shared__ int32_t s_wsum[SK_NW];
+  __shared__ float s_red[SK_NW][2][16][17];
+  const ExpertArgs& a = f.g;
+  const int w = wave_id(), l = lane_id(), tid = threadIdx.x;
+  const int q = l >> 4, r16 = l & 15;
+  const int E = a.E, K = a.K, N = a.N, k = f.k, Tn = f.T;
+  const int nslots = Tn * k;
+  const bool writer = blockIdx.x == 0;
+
+  // 1. tables, masks, logits of token w
+  for (int e = tid; e < EMAX_EXP; e += SK_NW * 64) {
+    const int ec = min(e, E - 1);
+    s_tg[e] = f.a_gsp[ec];
+    s_tr[e] = f.a_rcr[ec];
+    s_mask[e] = 0u;
+  }
+  float v[4];
+  const int tw = min(w, Tn - 1);
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) v[rr] = f.logits[int64_t(tw) * E + min(l + 64 * rr, E - 1)];
+  __syncthreads();
+  // 2. top-k, gates, skip decision: wave t for token t
+  if (w < Tn) {
+    const TopkParams p{E, k, f.norm_topk, f.fusion, f.tau_gsp, f.tau_rcr};
+    int my_e;
+    float g;
+    bool kp;
+    topk_slots(v, p, s_tg, s_tr, s_z[w], my_e, g, kp);
+    if (l < k) {
+      const int sidx = w * k + l;
+      s_idx[sidx] = my_e;
+      s_gate[sidx] = g;
+      s_keep[sidx] = kp ? 1 : 0;
+      if (kp) atomicOr(&s_mask[my_e], 1u << w);
+      if (writer) {
+        f.topk_idx[sidx] = my_e;
+        f.topk_gate[sidx] = g;
+        f.keep[sidx] = kp ? 1 : 0;
+      }
+    }
+  }
+  __syncthreads();
+  // 3. expert offsets and m-tile prefix (thread e owns expert e; waves 0..3)
+  {
+    const int e = tid;
+    const int cnt = e < E ? __popc(s_mask[e]) : 0;
+    const int mt = (cnt + BM - 1) / BM;
+    // two exclusive scans in one pass (rows, m-tiles) over the first 4 waves
+    int inc_c = cnt, inc_m = mt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int vc = __shfl_up(inc_c, o, 64), vm = __shfl_up(inc_m, o, 64);
+      if (l >= o) {
+        inc_c += vc;
+        inc_m += vm;
+      }
+    }
+    if (l == 63) s_wsum[w] = (inc_c << 16) | inc_m;  // both < 2^15 here
+    __syncthreads();
+    int base_c = 0, base_m = 0, all_c = 0, all_m = 0;
+    for (int ww = 0; ww < SK_NW; ++ww) {
+      const int sv = s_wsum[ww];
+      if (ww < w) {
+        base_c += sv >> 16;
+        base_m += sv & 0xFFFF;
+      }
+      all_c += sv >> 16;
+      all_m += sv & 0xFFFF;
+    }
+    if (e < E) {
+      s_off[e] = base_c + inc_c - cnt;
+      s_pref[e] = base_m + inc_m - mt;
+    }
+    if (tid == 0) {
+      s_off[E] = all_c;
+      s_pref[E] = all_m;
+    }
+  }
+  __syncthreads();
+  // 4. rows of the kept slots (token order inside an expert)
+  for (int sl = tid; sl < nslots; sl += SK_NW * 64) {
+    const int t = sl / k;
+    int row = -1;
+    if (s_keep[sl]) {
+      const int e = s_idx[sl];
+      row = s_off[e] + __popc(s_mask[e] & ((1u << t) - 1u));
+      s_tok[row] = t;
+      if (writer) {
+        f.sorted_token[row] = t;
+        f.sorted_gate[row] = s_gate[sl];
+      }
+    }
+    if (writer) f.slot_pos[sl] = row;
+  }
+  if (writer && tid <= E) f.offsets[tid] = s_off[tid];
+  __syncthreads();
+
+  // 5. split-K tiles over the LDS tile list, as in expert_splitk_kernel
+  const int nb_count = N / COLS;
+  const int nk = K / KS;
+  const int nkw = w < nk ? (nk - 1 - w) / SK_NW + 1 : 0;
+  const int ntiles = s_pref[E] * nb_count;
+  const int per_xcd = (ntiles + NXCD - 1) / NXCD;
+  for (int wg = blockIdx.x; wg < NXCD * per_xcd; wg += gridDim.x) {
+    const int gi = (wg % NXCD) * per_xcd + wg / NXCD;
+    if (gi >= ntiles) continue;
+    int e, nb, row0, rows;
+    find_tile(gi, nb_count, BM, E, s_pref, s_off, e, nb, row0, rows);
+    const int col0 = nb * COLS;
+    const int64_t ebytes = int64_t(N) * K * int(sizeof(T));
+    const char* wm0 = reinterpret_cast<const char*>(a.W0) + int64_t(e) * ebytes;
+    const char* wm1 = reinterpret_cast<const char*>(a.W1) + int64_t(e) * ebytes;
+    const __amdgpu_buffer_rsrc_t wr0 = make_rsrc(wm0, uint32_t(ebytes));
+    const __amdgpu_buffer_rsrc_t wr1 = make_rsrc(wm1, uint32_t(ebytes));
+    int wv, ws, wstep;
+    if (a.packed) {
+      wv = l * 16;
+      ws = (col0 / 16) * nk * 1024;
+      wstep = 1024;
+    } else {
+      wv = (r16 * K + q * EPL) * int(sizeof(T));
+      ws = col0 * K * int(sizeof(T));
+      wstep = KS * int(sizeof(T));
+    }
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    if (nkw > 0) {
+      u32x4 wa[SK_NBK], wb[SK_NBK], xa[SK_NBK];
+      auto load_w = [&](int i0) {
+#pragma unroll
+        for (int b = 0; b < SK_NBK; ++b) {
+          const int j = w + SK_NW * min(i0 + b, nkw - 1);
+          wa[b] = buf_ld16(wr0, wv, ws + j * wstep);
+          wb[b] = buf_ld16(wr1, wv, ws + j * wstep);
+        }
+      };
+      load_w(0);
+      const int src_row = s_tok[row0 + min(r16, rows - 1)];
+      const uint32_t xbytes = uint32_t(int64_t(a.A_rows) * K * int(sizeof(T)));
+      const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.A, xbytes);
+      const int xv = r16 < rows ? (src_row * K + q * EPL) * int(sizeof(T)) : int(0x7FFFFFF0u);
+      for (int i0 = 0; i0 < nkw; i0 += SK_NBK) {
+        if (i0 > 0) load_w(i0);
+#pragma unroll
+        for (int b = 0; b < SK_NBK; ++b) {
+          const int j = w + SK_NW * min(i0 + b, nkw - 1);
+          xa[b] = buf_ld16(xrs, xv, j * KS * int(sizeof(T)));
+        }
+#pragma unroll
+        for (int b = 0; b < SK_NBK; ++b) {
+          if (i0 + b < nkw) {
+            acc0 = mma_step<T>(xa[b], wa[b], acc0);
+            acc1 = mma_step<T>(xa[b], wb[b], acc1);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s_red[w][0][4 * q + j][r16] = acc0[j];
+      s_red[w][1][4 * q + j][r16] = acc1[j];
+    }
+    __syncthreads();
+    if (tid < 256) {
+      const int row = tid >> 4, c = tid & 15;
+      if (row < rows) {
+        float v0 = s_red[0][0][row][c], v1 = s_red[0][1][row][c];
+#pragma unroll
+        for (int ww = 1; ww < SK_NW; ++ww) {
+          v0 += s_red[ww][0][row][c];
+          v1 += s_red[ww][1][row][c];
+        }
+        const int64_t pr = row0 + row;
+        reinterpret_cast<T*>(a.out)[pr * N + col0 + c] = St<T>::from_f32(silu(v0) * v1);
+      }
+    }
+    __syncthreads();
+  }
 }
 
 // Packed weight layout: [E][N/16][K/KS][64 lanes][16 bytes], where the
@@ -559,6 +772,24 @@ hipError_t launch_pack(int dtype, const void* src, void* dst, int E, int N, int 
   else
     hipLaunchKernelGGL(pack_weights_kernel<float>, grid, block, 0, s, static_cast<const float*>(src),
                        static_cast<float*>(dst), units, N, K);
+  return hipGetLastError();
+}
+
+#ifndef ACE_FUSED_WG_PER_CU
+#define ACE_FUSED_WG_PER_CU 2   // grid cap of the fused kernel (about the resident count): its workgroups
+                                // loop over the tiles, paying the routing prologue once (measured best)
+#endif
+
+hipError_t launch_fused_gateup(int dtype, const FusedArgs& a, int num_cu, hipStream_t s) {
+  const int64_t slots = int64_t(a.T) * a.k;
+  const int64_t mt_bound = (slots + 15) / 16 + std::min<int64_t>(a.g.E, slots);
+  const int64_t tiles_bound = mt_bound * (a.g.N / 16);
+  const int64_t cap = int64_t(std::max(num_cu, 1)) * ACE_FUSED_WG_PER_CU;
+  const int64_t grid = std::max<int64_t>(NXCD, (std::min(tiles_bound, cap) + NXCD - 1) / NXCD * NXCD);
+  if (dtype == 1)
+    hipLaunchKernelGGL(expert_splitk_fused_kernel<bf16_t>, dim3(unsigned(grid)), dim3(SK_NW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL(expert_splitk_fused_kernel<float>, dim3(unsigned(grid)), dim3(SK_NW * 64), 0, s, a);
   return hipGetLastError();
 }
 

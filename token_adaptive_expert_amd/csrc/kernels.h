@@ -51,6 +51,25 @@ struct ExpertArgs {
   int A_rows;                 // rows of A: T (gate/up) or T*k (down)
 };
 
+// Fused small-batch gate/up (T <= FUSED_TMAX tokens): routing and dispatch are
+// derived from the router logits inside every workgroup; workgroup 0 writes them.
+constexpr int FUSED_TMAX = 8;
+struct FusedArgs {
+  ExpertArgs g;               // gate/up GEMM (offsets / sorted_token unused: made in LDS)
+  const float* logits;        // [T, E] f32
+  const float* a_gsp;
+  const float* a_rcr;
+  float tau_gsp, tau_rcr;
+  int T, k, norm_topk, fusion;
+  int32_t* topk_idx;          // outputs, written by workgroup 0
+  float* topk_gate;
+  uint8_t* keep;
+  int32_t* offsets;
+  int32_t* sorted_token;
+  float* sorted_gate;
+  int32_t* slot_pos;
+};
+
 struct CombineArgs {
   const int32_t* slot_pos;
   const float* slot_out;
@@ -96,13 +115,16 @@ struct TablesArgs {
 };
 
 // Host launchers (return the launch status).
-hipError_t launch_route(int dtype, const RouteArgs& a, hipStream_t s);
+// with_topk false: RMSNorm and router logits only (the fused small-batch
+// path derives the top-k itself).
+hipError_t launch_route(int dtype, const RouteArgs& a, hipStream_t s, bool with_topk = true);
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
 size_t dispatch_workspace_bytes(int T, int E);
 // kind 0: gate/up, 1: down; stream_path selects the small-batch tiling.
 hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs& a, int T, int k, int num_cu,
                          hipStream_t s);
 hipError_t launch_combine(int dtype, const CombineArgs& a, hipStream_t s);
+hipError_t launch_fused_gateup(int dtype, const FusedArgs& a, int num_cu, hipStream_t s);
 size_t router_packed_bytes(int E, int H);
 hipError_t launch_pack_router(const float* w, void* dst, int E, int H, hipStream_t s);
 hipError_t launch_pack(int dtype, const void* src, void* dst, int E, int N, int K, hipStream_t s);

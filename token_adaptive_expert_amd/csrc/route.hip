@@ -6,6 +6,7 @@
 // sections 1 and 2); a slot is skipped only when both fall below their
 // thresholds, and the top-1 slot is always kept (Methodology section 3).
 #include "kernels.h"
+#include "topk.h"
 
 namespace ace {
 
@@ -17,6 +18,9 @@ constexpr int RNTHR = RW * 64;
 constexpr int NTHR = 256;     // 4 waves (top-k kernel)
 constexpr int EMAX = 256;
 constexpr int NARROW_HMAX = 8192;  // hidden size limit of the small-batch router variant
+#ifndef ACE_ROUTER_NARROW_GX
+#define ACE_ROUTER_NARROW_GX 8     // token blocks up to which the 16-expert router variant is used
+#endif
 
 // h for EPL consecutive hidden units of one token, rounded to the storage
 // type (gamma values passed in).  The same function feeds h_out and the
@@ -277,36 +281,7 @@ reduce:
   }
 }
 
-// Wave-wide max / min through DPP row shifts (within rows of 16 lanes) and
-// a combine of the four row results read from lanes 15, 31, 47 and 63; every
-// lane gets the result.  No LDS round trips on the dependency chain.
-template <int CTRL> __device__ __forceinline__ int dpp_shr(int v, int ident) {
-  return __builtin_amdgcn_update_dpp(ident, v, CTRL, 0xF, 0xF, false);
-}
-__device__ __forceinline__ float wave_max_f(float v) {
-  const int ni = __float_as_int(-INFINITY);
-  v = fmaxf(v, __int_as_float(dpp_shr<0x111>(__float_as_int(v), ni)));
-  v = fmaxf(v, __int_as_float(dpp_shr<0x112>(__float_as_int(v), ni)));
-  v = fmaxf(v, __int_as_float(dpp_shr<0x114>(__float_as_int(v), ni)));
-  v = fmaxf(v, __int_as_float(dpp_shr<0x118>(__float_as_int(v), ni)));
-  const int b = __float_as_int(v);
-  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 15)), __int_as_float(__builtin_amdgcn_readlane(b, 31))),
-               fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 47)), __int_as_float(__builtin_amdgcn_readlane(b, 63))));
-}
-__device__ __forceinline__ int wave_min_i(int v) {
-  constexpr int big = 0x7FFFFFFF;
-  v = min(v, dpp_shr<0x111>(v, big));
-  v = min(v, dpp_shr<0x112>(v, big));
-  v = min(v, dpp_shr<0x114>(v, big));
-  v = min(v, dpp_shr<0x118>(v, big));
-  return min(min(__builtin_amdgcn_readlane(v, 15), __builtin_amdgcn_readlane(v, 31)),
-             min(__builtin_amdgcn_readlane(v, 47), __builtin_amdgcn_readlane(v, 63)));
-}
-
-// Kernel 2: top-k, gates and skip mask, one wave per token.  k rounds of
-// arg-max: the wave-wide largest remaining logit, then the lowest expert
-// index among the lanes holding it (order: value descending, index
-// ascending).
+// Kernel 2: top-k, gates and skip mask, one wave per token (topk_slots).
 __global__ __launch_bounds__(NTHR) void topk_skip_kernel(RouteArgs a) {
   constexpr int NWV = NTHR / 64;
   __shared__ float s_tg[EMAX], s_tr[EMAX];
@@ -334,71 +309,13 @@ __global__ __launch_bounds__(NTHR) void topk_skip_kernel(RouteArgs a) {
     for (int rr = 0; rr < 4; ++rr)
       if (rr < R && l + 64 * rr < E) orow[l + 64 * rr] = v[rr];
   }
-  uint32_t avail = 0;  // bit rr: value rr of this lane is a real, not yet taken expert
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr)
-    if (rr < R && l + 64 * rr < E) avail |= 1u << rr;
-  int my_e = 0;
-  float my_logit = 0.f, top_logit = 0.f;
-  for (int i = 0; i < k; ++i) {
-    // this lane's candidate: largest available value, lowest index on ties
-    float cv = -INFINITY;
-    int ce = 0x7FFFFFFF;
-    int crr = -1;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      if (((avail >> rr) & 1u) && (crr < 0 || v[rr] > cv)) {
-        cv = v[rr];
-        ce = l + 64 * rr;
-        crr = rr;
-      }
-    }
-    const float m = wave_max_f(cv);
-    const int be = wave_min_i(crr >= 0 && cv == m ? ce : 0x7FFFFFFF);
-    if (ce == be) avail &= ~(1u << crr);
-    if (l == i) {
-      my_e = be;
-      my_logit = m;
-    }
-    if (i == 0) top_logit = m;
-  }
-  // softmax in float64, shifted by the top-1 logit; sums in ascending order
-  const double mx = double(top_logit);
-  const double z = (l < k) ? exp(double(my_logit) - mx) : 0.0;
-  if (a.norm_topk) {
-    if (l < k) s_z[w][l] = z;
-  } else {
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int e = l + 64 * rr;
-      if (rr < R && e < E) s_z[w][e] = exp(double(v[rr]) - mx);
-    }
-  }
   __syncthreads();
-  double s = 0.0;
-  const int nsum = a.norm_topk ? k : E;
-  for (int i = 0; i < nsum; ++i) s += s_z[w][i];
+  const TopkParams p{E, k, a.norm_topk, a.fusion, a.tau_gsp, a.tau_rcr};
+  int my_e;
+  float g;
+  bool keep;
+  topk_slots(v, p, s_tg, s_tr, s_z[w], my_e, g, keep);
   if (valid && l < k) {
-    const float g = float(z / s);
-    bool keep = true;
-    if (l > 0) {
-      const float sg = g * s_tg[my_e];
-      const float sr = g * s_tr[my_e];
-      const bool lg = sg < a.tau_gsp, lr = sr < a.tau_rcr;
-      bool skip;
-      switch (a.fusion) {
-        case 1: skip = lg || lr; break;
-        case 2:
-          skip = a.tau_gsp > 0.f && a.tau_rcr > 0.f &&
-                 0.5 * (double(sg) / double(a.tau_gsp) + double(sr) / double(a.tau_rcr)) < 1.0;
-          break;
-        case 3: skip = lg; break;
-        case 4: skip = lr; break;
-        case 5: skip = g < a.tau_gsp; break;
-        default: skip = lg && lr; break;
-      }
-      keep = !skip;
-    }
     const int64_t o = int64_t(t) * k + l;
     a.topk_idx[o] = my_e;
     a.topk_gate[o] = g;
@@ -440,13 +357,14 @@ hipError_t launch_pack_router(const float* w, void* dst, int E, int H, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_route(int dtype, const RouteArgs& a, hipStream_t s) {
+hipError_t launch_route(int dtype, const RouteArgs& a, hipStream_t s, bool with_topk) {
   static_assert(NTHR == EMAX, "the top-k kernel loads one table entry per thread");
   const dim3 block1(RNTHR), block(NTHR);
   const unsigned gx = unsigned((a.T + TB - 1) / TB);
   // small batches with the pre-split router: one 16-expert column block per
   // workgroup, so that more workgroups share the router weights
-  const bool narrow = dtype == 1 && a.router_packed && a.logits_in == nullptr && gx <= 8 && a.H <= NARROW_HMAX;
+  const bool narrow =
+      dtype == 1 && a.router_packed && a.logits_in == nullptr && gx <= ACE_ROUTER_NARROW_GX && a.H <= NARROW_HMAX;
   if (narrow) {
     hipLaunchKernelGGL((norm_router_kernel<bf16_t, 1>), dim3(gx, unsigned((a.E + 15) / 16)), block1, 0, s, a);
   } else {
@@ -457,7 +375,7 @@ hipError_t launch_route(int dtype, const RouteArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((norm_router_kernel<float, 2>), grid1, block1, 0, s, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !with_topk) return e;
   const dim3 grid2((a.T + NTHR / 64 - 1) / (NTHR / 64));
   hipLaunchKernelGGL(topk_skip_kernel, grid2, block, 0, s, a);
   return hipGetLastError();

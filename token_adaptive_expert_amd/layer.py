@@ -133,6 +133,21 @@ class AceMoeLayer:
 
     def forward(self, x, tau_gsp, tau_rcr, b: LayerBuffers | None = None, path=_lib.ACE_PATH_AUTO, logits_in=None,
                 residual=None, stream=None) -> torch.Tensor:
+        """The whole layer through moe_forward (one C call)."""
+        T = x.shape[0]
+        if b is None:
+            b = self.buffers(T)
+        if b.T < T:
+            raise ValueError(f"buffers sized for {b.T} tokens, got {T}")
+        _lib.moe_forward(self.desc(T), path, x, self.gamma, self.w_router, self.router_bias, logits_in, b.logits,
+                         self.a_gsp, self.a_rcr, tau_gsp, tau_rcr, self.w_gate, self.w_up, self.w_down, residual, b.h,
+                         b.topk_idx, b.topk_gate, b.keep, b.offsets, b.sorted_token, b.sorted_gate, b.slot_pos, b.act,
+                         b.slot_out, b.y, b.workspace, None, stream)
+        return b.y[:T]
+
+    def forward_steps(self, x, tau_gsp, tau_rcr, b: LayerBuffers | None = None, path=_lib.ACE_PATH_AUTO,
+                      logits_in=None, residual=None, stream=None) -> torch.Tensor:
+        """The same layer through the four step calls."""
         T = x.shape[0]
         if b is None:
             b = self.buffers(T)
