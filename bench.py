@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-tables", action="store_true", help="skip timing the offline table builder")
     p.add_argument("--no-stack", action="store_true", help="skip the 48-layer stack")
+    p.add_argument("--only", choices=["decode", "glm", "t32k", "stack", "tables"],
+                   help="run that leg alone and print its result (for profiling runs), not the contract line")
     p.add_argument("--no-extra", action="store_true",
                    help="skip the GLM-4.5-Air-shaped layer, the T=32768 run and the dense GEMM ceiling")
     p.add_argument("--cpu-tokens", type=int, default=1024, help="tokens in the oracle's timed sample")
@@ -428,6 +430,23 @@ def main():
         sys.exit(2)
     B = Bench(args)
     S = B.S
+    if args.only:
+        import workloads
+        if args.only in ("decode",):
+            tau = B.calibrate(B.P["x"], args.skip)
+            out = {"decode_us_per_layer": {str(m): round(v["us"], 2) for m, v in B.decode(tau).items()}}
+        elif args.only == "glm":
+            out = extra_prefill(B, "glm45_air_shape MoE layer prefill (Zipf router prior)",
+                                workloads.CONFIGS["glm45_air_shape"], 4096, 0.5, max(10, args.steps // 2), 3)
+        elif args.only == "t32k":
+            out = extra_prefill(B, "qwen3_30b_a3b layer at T=32768 (MFMA-bound supplement)", S, 32768, args.skip,
+                                max(5, args.steps // 4), 2, P=B.P, layer=B.layers[0])
+        elif args.only == "stack":
+            out = stack48(B)
+        else:
+            out = tables_build(B)
+        print(json.dumps({"only": args.only, "result": out}), flush=True)
+        return
     head = B.prefill(args.skip)
     T = S.T
     value = T / (head["ms"] * 1e-3)

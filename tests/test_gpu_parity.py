@@ -321,6 +321,46 @@ def test_fused_forward_matches_steps_f32(tiny, dev, fusion):
     _fused_vs_steps(gl.layer, x, float(tg), float(tr), None)
 
 
+# ---------------------------------------------------------------- multi-workgroup dispatch
+@pytest.mark.parametrize("T,k,E,keep_p,skew", [
+    (4097, 2, 7, 0.5, 0.0),      # 8194 slots: three blocks, the last holding two slots
+    (1100, 8, 200, 0.4, 1.1),    # 8800 slots, Zipf-like expert prior, many empty experts
+    (3000, 6, 256, 0.9, 0.0),    # 18000 slots, E at its maximum
+    (2049, 4, 64, 0.0, 0.0),     # only top-1 slots kept
+    (1025, 8, 128, 1.0, 3.0),    # everything kept, a few experts take most slots
+])
+def test_dispatch_large_batches(dev, T, k, E, keep_p, skew):
+    """Batches of more than 8192 slots go through the per-block count, scan and
+    row kernels: offsets, sorted tokens and gates and slot positions must equal
+    oracle.dispatch_order bit for bit.  Rows hold k distinct experts drawn by
+    Gumbel top-k from a power-law prior; the workspace starts as garbage."""
+    rng = np.random.default_rng(T * 1000 + E)
+    prior = -skew * np.log(np.arange(1, E + 1))
+    idx = np.argsort(-(rng.gumbel(size=(T, E)) + prior), axis=1)[:, :k].astype(np.int32)
+    gate = rng.random((T, k)).astype(np.float32)
+    keep = rng.random((T, k)) < keep_p
+    keep[:, 0] = True
+    d = ace.make_desc(T, 128, E, 128, k, "bf16")
+    nws = ace.moe_workspace_bytes(d)
+    assert nws >= 8 * E * ((T * k + 4095) // 4096)
+    ws = torch.full((nws,), 0x7F, dtype=torch.uint8, device=dev)
+    t_idx = torch.from_numpy(idx).to(dev)
+    t_gate = torch.from_numpy(gate).to(dev)
+    t_keep = torch.from_numpy(keep.astype(np.uint8)).to(dev)
+    off = torch.full((E + 1,), -7, dtype=torch.int32, device=dev)
+    tok = torch.full((T * k,), -7, dtype=torch.int32, device=dev)
+    sg = torch.full((T * k,), -7.0, dtype=torch.float32, device=dev)
+    pos = torch.full((T, k), -7, dtype=torch.int32, device=dev)
+    ace.moe_dispatch(d, t_idx, t_gate, t_keep, off, tok, sg, pos, ws)
+    torch.cuda.synchronize()
+    r_off, r_tok, r_slot, r_pos = oracle.dispatch_order(idx, keep, E)
+    n = int(r_off[-1])
+    assert np.array_equal(off.cpu().numpy(), r_off)
+    assert np.array_equal(tok.cpu().numpy()[:n], r_tok)
+    assert np.array_equal(pos.cpu().numpy(), r_pos)
+    assert np.array_equal(sg.cpu().numpy()[:n].view(np.uint32), gate[r_tok, r_slot].view(np.uint32))
+
+
 # ---------------------------------------------------------------- decode expert-pool cap
 @pytest.mark.parametrize("M,pool", [(1, 1), (4, 2), (8, 4), (8, 16), (32, 8), (32, 40), (64, 16), (64, 300)])
 def test_decode_expert_pool(qwen, dev, M, pool):

@@ -120,7 +120,7 @@ const char* moe_last_error(void) { return g_err.c_str(); }
 
 size_t moe_workspace_bytes(const ace_moe_desc* d) {
   if (check_desc(d) != ACE_OK) return 0;
-  return ace::dispatch_workspace_bytes(std::max(d->T, 1), d->E);
+  return ace::dispatch_workspace_bytes(std::max(d->T, 1), d->E, d->k);
 }
 
 ace_status moe_route_skip(const ace_moe_desc* d, const void* x, const float* gamma, const float* w_router,
@@ -191,7 +191,7 @@ ace_status moe_dispatch(const ace_moe_desc* d, const int32_t* topk_idx, const fl
     REQUIRE(sorted_gate);
     REQUIRE(slot_pos);
     REQUIRE(workspace);
-    const size_t need = ace::dispatch_workspace_bytes(std::max(d->T, 1), d->E);
+    const size_t need = ace::dispatch_workspace_bytes(std::max(d->T, 1), d->E, d->k);
     if (workspace_bytes < need)
       return fail(ACE_EWORKSPACE, "workspace_bytes=%zu < %zu needed", workspace_bytes, need);
     if (d->T == 0) return ok();
@@ -207,6 +207,7 @@ ace_status moe_dispatch(const ace_moe_desc* d, const int32_t* topk_idx, const fl
     a.E = d->E;
     a.k = d->k;
     a.pool = d->expert_pool;
+    a.ws = static_cast<int32_t*>(workspace);
     hipError_t e = ace::launch_dispatch(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail("dispatch launch", e);
     return ok();
@@ -237,9 +238,9 @@ ace_status moe_expert_forward(const ace_moe_desc* d, int32_t path, const void* h
     REQUIRE(act);
     REQUIRE(slot_out);
     REQUIRE(workspace);
-    if (workspace_bytes < ace::dispatch_workspace_bytes(d->T, d->E))
+    if (workspace_bytes < ace::dispatch_workspace_bytes(d->T, d->E, d->k))
       return fail(ACE_EWORKSPACE, "workspace_bytes=%zu < %zu needed", workspace_bytes,
-                  ace::dispatch_workspace_bytes(d->T, d->E));
+                  ace::dispatch_workspace_bytes(d->T, d->E, d->k));
     if (d->T == 0) return ok();
     int ncu = 0;
     st = num_cu(&ncu);
@@ -451,7 +452,7 @@ ace_status moe_forward(const ace_moe_desc* d, int32_t path, const void* x, const
     REQUIRE(workspace);
     if (!(tau_gsp >= 0.f) || !(tau_rcr >= 0.f))
       return fail(ACE_EINVAL, "thresholds must be >= 0 (got %g, %g)", double(tau_gsp), double(tau_rcr));
-    const size_t need = ace::dispatch_workspace_bytes(std::max(d->T, 1), d->E);
+    const size_t need = ace::dispatch_workspace_bytes(std::max(d->T, 1), d->E, d->k);
     if (workspace_bytes < need) return fail(ACE_EWORKSPACE, "workspace_bytes=%zu < %zu needed", workspace_bytes, need);
     if (d->T == 0) return ok();
     const bool fused = d->T <= ACE_FUSED_TOKENS && d->expert_pool == 0 && logits_in == nullptr &&

@@ -30,6 +30,13 @@
 // Reading of the decode expert pool of "ExFold: Unified Expert Folding for
 // Training-Free MoE Prefill-Decode Acceleration" (abstract; Tables 1, 5, 6),
 // without the folding of excluded experts.
+//
+// Batches of more than 8192 slots (no pool) spread over one workgroup per
+// 4096-slot block: dispatch_count_kernel counts each block's kept slots per
+// expert, dispatch_scan_kernel turns the counts into expert_offsets and each
+// block's first row per expert, and dispatch_kernel<false, true> runs step 3
+// on its own block from those rows.  The rows are the same as the one-
+// workgroup kernel's (slot order within an expert, whatever the split).
 #include "kernels.h"
 
 namespace ace {
@@ -39,6 +46,8 @@ constexpr int NW = 16;
 constexpr int NTHR = NW * 64;
 constexpr int EMAX = 256;
 constexpr int POOL_SLOTS = 8192;  // slots (T*k) the pool variant keeps in LDS
+constexpr int DBS = 4096;         // slots per block of the multi-workgroup path (64 chunks)
+constexpr int DBLOCK_MIN = 8192;  // slot count above which the multi-workgroup path is used
 
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -87,7 +96,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int32_t* s_wsum, int* tota
   return base + inc - v;
 }
 
-template <bool POOL>
+template <bool POOL, bool BLOCK>
 __global__ __launch_bounds__(NTHR) void dispatch_kernel(DispatchArgs a) {
   __shared__ uint32_t s_bits[NW][EMAX][2];
   __shared__ int32_t s_run[NW][EMAX];
@@ -104,8 +113,11 @@ __global__ __launch_bounds__(NTHR) void dispatch_kernel(DispatchArgs a) {
   const int E = a.E, k = a.k;
   const int64_t nslots = int64_t(a.T) * k;
   const int nchunks = int((nslots + 63) / 64);
-  const int cpw = (nchunks + NW - 1) / NW;
-  const int c0 = w * cpw, c1 = min(nchunks, c0 + cpw);
+  // BLOCK: workgroup b owns chunks [b*DBS/64, (b+1)*DBS/64)
+  const int cb0 = BLOCK ? int(blockIdx.x) * (DBS / 64) : 0;
+  const int cb1 = BLOCK ? min(nchunks, cb0 + DBS / 64) : nchunks;
+  const int cpw = (cb1 - cb0 + NW - 1) / NW;
+  const int c0 = cb0 + w * cpw, c1 = min(cb1, c0 + cpw);
 
   // 1. per-wave expert counts (and, with the pool, the top-1 experts)
   for (int e = l; e < E; e += 64) s_run[w][e] = 0;
@@ -134,15 +146,21 @@ __global__ __launch_bounds__(NTHR) void dispatch_kernel(DispatchArgs a) {
       tot += v;
     }
   }
-  int all = 0;
-  const int excl = block_excl_scan(tot, s_wsum, &all);
-  if (tid < E) {
-    s_off[tid] = excl;
-    if (!POOL) a.offsets[tid] = excl;
-  }
-  if (tid == 0) {
-    s_off[E] = all;
-    if (!POOL) a.offsets[E] = all;
+  if constexpr (BLOCK) {
+    // this block's first row in each expert's segment (dispatch_scan_kernel)
+    const int nblk = int((nslots + DBS - 1) / DBS);
+    if (tid < E) s_off[tid] = a.ws[int64_t(nblk) * E + int64_t(blockIdx.x) * E + tid];
+  } else {
+    int all = 0;
+    const int excl = block_excl_scan(tot, s_wsum, &all);
+    if (tid < E) {
+      s_off[tid] = excl;
+      if (!POOL) a.offsets[tid] = excl;
+    }
+    if (tid == 0) {
+      s_off[E] = all;
+      if (!POOL) a.offsets[E] = all;
+    }
   }
   __syncthreads();
   for (int e = l; e < E; e += 64) s_run[w][e] += s_off[e];
@@ -239,17 +257,99 @@ __global__ __launch_bounds__(NTHR) void dispatch_kernel(DispatchArgs a) {
   }
 }
 
-size_t dispatch_workspace_bytes(int T, int E) {
-  (void)T;
-  (void)E;
-  return 256;
+// Multi-workgroup path (large batches), kernel 1: kept slots per expert in
+// each block of DBS slots -> ws[b][e] (order-independent integer totals).
+__global__ __launch_bounds__(256) void dispatch_count_kernel(DispatchArgs a) {
+  __shared__ int32_t s_c[EMAX];
+  const int tid = threadIdx.x, E = a.E;
+  const int64_t nslots = int64_t(a.T) * a.k;
+  const int64_t s0 = int64_t(blockIdx.x) * DBS;
+  for (int e = tid; e < EMAX; e += 256) s_c[e] = 0;
+  __syncthreads();
+  int ev[DBS / 256];
+  bool kv[DBS / 256];
+#pragma unroll
+  for (int j = 0; j < DBS / 256; ++j) {
+    const int64_t s = min(s0 + j * 256 + tid, nslots - 1);
+    ev[j] = a.idx[s];
+    kv[j] = a.keep[s] != 0 && s0 + j * 256 + tid < nslots;
+  }
+#pragma unroll
+  for (int j = 0; j < DBS / 256; ++j)
+    if (kv[j] && unsigned(ev[j]) < unsigned(E)) atomicAdd(&s_c[ev[j]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) a.ws[int64_t(blockIdx.x) * E + e] = s_c[e];
+}
+
+// Kernel 2 (one workgroup): expert totals -> expert_offsets (exclusive scan
+// over experts); each block's first row per expert = offset + the counts of
+// the earlier blocks -> ws[nblk + b][e].  Thread (g, e) owns expert e over
+// the g-th contiguous run of blocks.
+__global__ __launch_bounds__(NTHR) void dispatch_scan_kernel(DispatchArgs a, int nblk) {
+  __shared__ int32_t s_wsum[NTHR / 64];
+  __shared__ int32_t s_part[NTHR];
+  const int tid = threadIdx.x, E = a.E;
+  const int G = NTHR / E;
+  const int g = tid / E, e = tid - g * E;
+  const int bpg = (nblk + G - 1) / G;
+  const int b0 = g * bpg, b1 = min(nblk, b0 + bpg);
+  const int32_t* __restrict__ cnt = a.ws;
+  int32_t* __restrict__ base = a.ws + int64_t(nblk) * E;
+  int part = 0;
+  if (g < G)
+    for (int b = b0; b < b1; ++b) part += cnt[int64_t(b) * E + e];
+  s_part[tid] = part;
+  __syncthreads();
+  int tot = 0;
+  if (tid < E)
+    for (int gg = 0; gg < G; ++gg) tot += s_part[gg * E + tid];
+  int all = 0;
+  const int excl = block_excl_scan(tot, s_wsum, &all);  // expert order (tid < E)
+  if (tid < E) {
+    a.offsets[tid] = excl;
+    // exclusive prefix over groups, in place: s_part[gg*E + e] -> row base of group gg
+    int run = excl;
+    for (int gg = 0; gg < G; ++gg) {
+      const int v = s_part[gg * E + tid];
+      s_part[gg * E + tid] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  if (g < G) {
+    int run = s_part[tid];
+    for (int b = b0; b < b1; ++b) {
+      base[int64_t(b) * E + e] = run;
+      run += cnt[int64_t(b) * E + e];
+    }
+  }
+  if (tid == 0) a.offsets[E] = all;
+}
+
+size_t dispatch_workspace_bytes(int T, int E, int k) {
+  const int64_t nslots = int64_t(T) * k;
+  if (nslots <= DBLOCK_MIN) return 256;
+  const int64_t nblk = (nslots + DBS - 1) / DBS;
+  return size_t((nblk * E * 2 * 4 + 255) / 256 * 256);
 }
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
-  if (a.pool > 0)
-    hipLaunchKernelGGL(dispatch_kernel<true>, dim3(1), dim3(NTHR), 0, s, a);
-  else
-    hipLaunchKernelGGL(dispatch_kernel<false>, dim3(1), dim3(NTHR), 0, s, a);
+  const int64_t nslots = int64_t(a.T) * a.k;
+  if (a.pool > 0) {
+    hipLaunchKernelGGL((dispatch_kernel<true, false>), dim3(1), dim3(NTHR), 0, s, a);
+  } else if (nslots <= DBLOCK_MIN) {
+    hipLaunchKernelGGL((dispatch_kernel<false, false>), dim3(1), dim3(NTHR), 0, s, a);
+  } else {
+    // large batches: per-block counts, one scan, per-block rows
+    const int nblk = int((nslots + DBS - 1) / DBS);
+    hipLaunchKernelGGL(dispatch_count_kernel, dim3(nblk), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(NTHR), 0, s, a, nblk);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dispatch_kernel<false, true>), dim3(nblk), dim3(NTHR), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -36,6 +36,9 @@ namespace {
 #ifndef ACE_WAVES_PER_EU
 #define ACE_WAVES_PER_EU 3    // occupancy target given to the register allocator
 #endif
+#ifndef ACE_BIG_RB
+#define ACE_BIG_RB 8          // 16-row blocks per tile for batches with >= 512 slots per expert
+#endif
 #ifndef ACE_GATEUP_NW
 #define ACE_GATEUP_NW 4       // waves per grouped gate/up tile (16 intermediate units each)
 #endif
@@ -178,7 +181,7 @@ __device__ __forceinline__ void find_xcd_tile(int j, int x, int nbc, int E, cons
 
 template <typename T, int RB, int NW, int KIND, int STAGES>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(RB <= 2 ? 4 : (RB >= 8 ? 2 : ACE_WAVES_PER_EU))))
+__attribute__((amdgpu_waves_per_eu(RB <= 2 ? 4 : (RB >= 16 ? 1 : (RB >= 8 ? 2 : ACE_WAVES_PER_EU)))))
 void expert_gemm_kernel(ExpertArgs a) {
   constexpr int EPL = St<T>::EPL;
   constexpr int KS = 4 * EPL;      // k values per k-step
@@ -808,7 +811,8 @@ hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs
       return kind == 0 ? launch_splitk<bf16_t, 0>(a, T, k, num_cu, s) : launch_splitk<bf16_t, 1>(a, T, k, num_cu, s);
     constexpr int NG = ACE_GATEUP_NW, ND = ACE_DOWN_NW;
     if (big_rb)
-      return kind == 0 ? launch_one<bf16_t, 8, 8, 0, 2>(a, T, k, s) : launch_one<bf16_t, 8, 8, 1, 2>(a, T, k, s);
+      return kind == 0 ? launch_one<bf16_t, ACE_BIG_RB, 8, 0, 2>(a, T, k, s)
+                       : launch_one<bf16_t, ACE_BIG_RB, 8, 1, 2>(a, T, k, s);
     if (small_rb)
       return kind == 0 ? launch_one<bf16_t, 2, NG, 0, S>(a, T, k, s) : launch_one<bf16_t, 2, ND, 1, S>(a, T, k, s);
     return kind == 0 ? launch_one<bf16_t, G, NG, 0, S>(a, T, k, s)

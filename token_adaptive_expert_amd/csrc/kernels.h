@@ -33,7 +33,8 @@ struct DispatchArgs {
   float* sorted_gate;
   int32_t* slot_pos;
   int T, E, k;
-  int pool;  // 0: off; m >= 1: batch-level expert-pool cap (T*k <= 8192)
+  int pool;      // 0: off; m >= 1: batch-level expert-pool cap (T*k <= 8192)
+  int32_t* ws;   // workspace: per-block expert counts and row bases (large batches)
 };
 
 struct ExpertArgs {
@@ -119,7 +120,7 @@ struct TablesArgs {
 // path derives the top-k itself).
 hipError_t launch_route(int dtype, const RouteArgs& a, hipStream_t s, bool with_topk = true);
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
-size_t dispatch_workspace_bytes(int T, int E);
+size_t dispatch_workspace_bytes(int T, int E, int k);
 // kind 0: gate/up, 1: down; stream_path selects the small-batch tiling.
 hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs& a, int T, int k, int num_cu,
                          hipStream_t s);
