@@ -162,7 +162,7 @@ ace_status moe_route_skip(const ace_moe_desc* d, const void* x, const float* gam
  * (abstract; Tables 1, 5, 6) without its folding.  The keep array is not
  * modified: slot_pos >= 0 marks the slots that run.
  * workspace: >= moe_workspace_bytes(d) bytes of device memory (batches of
- *      more than 8192 slots keep per-block expert counts there: 8 bytes per
+ *      more than 32768 slots keep per-block expert counts there: 8 bytes per
  *      expert per 4096 slots; smaller ones use none of it).
  */
 ace_status moe_dispatch(const ace_moe_desc* d, const int32_t* topk_idx, const float* topk_gate, const uint8_t* keep,

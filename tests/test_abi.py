@@ -102,10 +102,10 @@ def test_workspace_too_small():
     assert need > 0
     st = lib.moe_dispatch(ctypes.byref(d), *([0x1000] * 7), 0x1000, need - 1, None)
     assert st == 3 and str(need) in lib.moe_last_error().decode()
-    # more than 8192 slots: per-block counts and row bases, 8 bytes per expert per 4096 slots
-    d = m.make_desc(4096, 4096, 128, 1408, 8, "bf16")
+    # more than 32768 slots: per-block counts and row bases, 8 bytes per expert per 4096 slots
+    d = m.make_desc(8192, 4096, 128, 1408, 8, "bf16")
     need = lib.moe_workspace_bytes(ctypes.byref(d))
-    assert need >= 8 * 128 * 8
+    assert need >= 8 * 128 * 16
     st = lib.moe_dispatch(ctypes.byref(d), *([0x1000] * 7), 0x1000, need - 1, None)
     assert st == 3 and str(need) in lib.moe_last_error().decode()
 

@@ -323,15 +323,21 @@ def test_fused_forward_matches_steps_f32(tiny, dev, fusion):
 
 # ---------------------------------------------------------------- multi-workgroup dispatch
 @pytest.mark.parametrize("T,k,E,keep_p,skew", [
-    (4097, 2, 7, 0.5, 0.0),      # 8194 slots: three blocks, the last holding two slots
+    # recount mode (1024 < T*k <= 32768: one workgroup per 1024 slots)
+    (513, 2, 7, 0.5, 0.0),       # 1026 slots: the second block holds two slots
     (1100, 8, 200, 0.4, 1.1),    # 8800 slots, Zipf-like expert prior, many empty experts
     (3000, 6, 256, 0.9, 0.0),    # 18000 slots, E at its maximum
     (2049, 4, 64, 0.0, 0.0),     # only top-1 slots kept
-    (1025, 8, 128, 1.0, 3.0),    # everything kept, a few experts take most slots
+    (4096, 8, 128, 1.0, 3.0),    # 32768 slots, all kept, a few experts take most slots
+    # block mode (T*k > 32768: count, scan and row kernels)
+    (16385, 2, 7, 0.5, 0.0),     # 32770 slots: the last 4096-slot block holds two
+    (5000, 8, 128, 0.4, 1.1),    # 40000 slots, Zipf-like prior
+    (40000, 1, 16, 1.0, 0.0),    # top-1 routing only
 ])
 def test_dispatch_large_batches(dev, T, k, E, keep_p, skew):
-    """Batches of more than 8192 slots go through the per-block count, scan and
-    row kernels: offsets, sorted tokens and gates and slot positions must equal
+    """Batches of more than 1024 slots spread over several workgroups (recount
+    mode up to 32768 slots, then the per-block count, scan and row kernels):
+    offsets, sorted tokens and gates and slot positions must equal
     oracle.dispatch_order bit for bit.  Rows hold k distinct experts drawn by
     Gumbel top-k from a power-law prior; the workspace starts as garbage."""
     rng = np.random.default_rng(T * 1000 + E)
@@ -342,7 +348,8 @@ def test_dispatch_large_batches(dev, T, k, E, keep_p, skew):
     keep[:, 0] = True
     d = ace.make_desc(T, 128, E, 128, k, "bf16")
     nws = ace.moe_workspace_bytes(d)
-    assert nws >= 8 * E * ((T * k + 4095) // 4096)
+    if T * k > 32768:
+        assert nws >= 8 * E * ((T * k + 4095) // 4096)
     ws = torch.full((nws,), 0x7F, dtype=torch.uint8, device=dev)
     t_idx = torch.from_numpy(idx).to(dev)
     t_gate = torch.from_numpy(gate).to(dev)

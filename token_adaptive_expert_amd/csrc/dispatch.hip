@@ -31,12 +31,17 @@
 // Training-Free MoE Prefill-Decode Acceleration" (abstract; Tables 1, 5, 6),
 // without the folding of excluded experts.
 //
-// Batches of more than 8192 slots (no pool) spread over one workgroup per
-// 4096-slot block: dispatch_count_kernel counts each block's kept slots per
-// expert, dispatch_scan_kernel turns the counts into expert_offsets and each
-// block's first row per expert, and dispatch_kernel<false, true> runs step 3
-// on its own block from those rows.  The rows are the same as the one-
-// workgroup kernel's (slot order within an expert, whatever the split).
+// Without the pool, batches of more than 1024 slots spread step 3 over
+// several workgroups, each owning a block of consecutive slots:
+//   * up to 32768 slots (recount mode): one workgroup per 1024 slots; each
+//     counts the whole batch itself (per expert: all kept slots, and those
+//     before its block), so one launch does the job;
+//   * above that (block mode): one workgroup per 4096 slots, after
+//     dispatch_count_kernel (each block's counts per expert) and
+//     dispatch_scan_kernel (expert_offsets and each block's first row per
+//     expert, kept in the workspace).
+// The rows are the same as the one-workgroup kernel's (slot order within an
+// expert, whatever the split).
 #include "kernels.h"
 
 namespace ace {
@@ -46,8 +51,14 @@ constexpr int NW = 16;
 constexpr int NTHR = NW * 64;
 constexpr int EMAX = 256;
 constexpr int POOL_SLOTS = 8192;  // slots (T*k) the pool variant keeps in LDS
-constexpr int DBS = 4096;         // slots per block of the multi-workgroup path (64 chunks)
-constexpr int DBLOCK_MIN = 8192;  // slot count above which the multi-workgroup path is used
+// Launch modes of dispatch_kernel
+constexpr int DSP_ONE = 0;       // one workgroup for the whole batch
+constexpr int DSP_RECOUNT = 1;   // one workgroup per RBS slots; each counts the whole batch itself
+constexpr int DSP_BLOCK = 2;     // one workgroup per DBS slots; counts and row bases from the workspace
+constexpr int RBS = 64 * NW;     // slots per workgroup, recount mode (one 64-slot chunk per wave)
+constexpr int RECOUNT_MAX = 32768;  // largest batch (slots) of the recount mode
+constexpr int RC_BATCH = 8;      // chunk loads in flight per wave while recounting
+constexpr int DBS = 4096;        // slots per workgroup, block mode (64 chunks)
 
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -96,7 +107,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int32_t* s_wsum, int* tota
   return base + inc - v;
 }
 
-template <bool POOL, bool BLOCK>
+template <bool POOL, int MODE>
 __global__ __launch_bounds__(NTHR) void dispatch_kernel(DispatchArgs a) {
   __shared__ uint32_t s_bits[NW][EMAX][2];
   __shared__ int32_t s_run[NW][EMAX];
@@ -109,24 +120,62 @@ __global__ __launch_bounds__(NTHR) void dispatch_kernel(DispatchArgs a) {
   __shared__ int32_t s_flag[POOL ? EMAX : 1];       // bit 0: top-1 expert; bit 1: retained
   __shared__ int32_t s_list[POOL ? EMAX : 1];
   __shared__ int32_t s_noff[POOL ? EMAX : 1];
+  // recount mode only: kept slots per expert outside this block, and before it
+  __shared__ int32_t s_tot[MODE == DSP_RECOUNT ? EMAX : 1];
+  __shared__ int32_t s_pre[MODE == DSP_RECOUNT ? EMAX : 1];
   const int w = wave_id(), l = lane_id(), tid = threadIdx.x;
   const int E = a.E, k = a.k;
   const int64_t nslots = int64_t(a.T) * k;
   const int nchunks = int((nslots + 63) / 64);
-  // BLOCK: workgroup b owns chunks [b*DBS/64, (b+1)*DBS/64)
-  const int cb0 = BLOCK ? int(blockIdx.x) * (DBS / 64) : 0;
-  const int cb1 = BLOCK ? min(nchunks, cb0 + DBS / 64) : nchunks;
+  // workgroup b owns chunks [b*BCH, (b+1)*BCH) (all of them in DSP_ONE)
+  constexpr int BCH = MODE == DSP_RECOUNT ? RBS / 64 : DBS / 64;
+  const int cb0 = MODE != DSP_ONE ? int(blockIdx.x) * BCH : 0;
+  const int cb1 = MODE != DSP_ONE ? min(nchunks, cb0 + BCH) : nchunks;
   const int cpw = (cb1 - cb0 + NW - 1) / NW;
   const int c0 = cb0 + w * cpw, c1 = min(cb1, c0 + cpw);
 
   // 1. per-wave expert counts (and, with the pool, the top-1 experts)
   for (int e = l; e < E; e += 64) s_run[w][e] = 0;
   if (POOL && tid < EMAX) s_flag[tid] = 0;
+  if (MODE == DSP_RECOUNT && tid < EMAX) {
+    s_tot[tid] = 0;
+    s_pre[tid] = 0;
+  }
   __syncthreads();
+  // recount mode: each wave owns one chunk of the block; its slots are loaded
+  // once, before the recount, and serve steps 1 and 3
+  SlotVals own{};
+  if constexpr (MODE == DSP_RECOUNT) own = load_slot(a, int64_t(min(c0, nchunks - 1)) * 64 + l, nslots, true);
+  if constexpr (MODE == DSP_RECOUNT) {
+    // the chunks outside this block, dealt round-robin over the waves, RC_BATCH
+    // loads in flight: kept slots per expert, and those before the block
+    const int nown = cb1 - cb0, nout = nchunks - nown;
+    for (int i0 = w; i0 < nout; i0 += NW * RC_BATCH) {
+      int ev[RC_BATCH], kv[RC_BATCH];
+#pragma unroll
+      for (int b = 0; b < RC_BATCH; ++b) {
+        const int i = min(i0 + NW * b, nout - 1);
+        const int c = i < cb0 ? i : i + nown;
+        const int64_t sl = min(int64_t(c) * 64 + l, nslots - 1);
+        ev[b] = a.idx[sl];
+        kv[b] = a.keep[sl];
+      }
+#pragma unroll
+      for (int b = 0; b < RC_BATCH; ++b) {
+        const int i = i0 + NW * b;
+        const int c = i < cb0 ? i : i + nown;
+        if (i < nout && int64_t(c) * 64 + l < nslots && kv[b] && unsigned(ev[b]) < unsigned(E)) {
+          atomicAdd(&s_tot[ev[b]], 1);
+          if (c < cb0) atomicAdd(&s_pre[ev[b]], 1);
+        }
+      }
+    }
+  }
   if (c0 < c1) {
-    SlotVals cur = load_slot(a, int64_t(c0) * 64 + l, nslots, false);
+    SlotVals cur = MODE == DSP_RECOUNT ? own : load_slot(a, int64_t(c0) * 64 + l, nslots, false);
     for (int c = c0; c < c1; ++c) {
-      const SlotVals nxt = load_slot(a, int64_t(min(c + 1, c1 - 1)) * 64 + l, nslots, false);
+      const SlotVals nxt =
+          MODE == DSP_RECOUNT ? cur : load_slot(a, int64_t(min(c + 1, c1 - 1)) * 64 + l, nslots, false);
       const int64_t s = int64_t(c) * 64 + l;
       if (s < nslots && unsigned(cur.e) < unsigned(E)) {
         if (cur.kept) atomicAdd(&s_run[w][cur.e], 1);
@@ -146,10 +195,19 @@ __global__ __launch_bounds__(NTHR) void dispatch_kernel(DispatchArgs a) {
       tot += v;
     }
   }
-  if constexpr (BLOCK) {
+  if constexpr (MODE == DSP_BLOCK) {
     // this block's first row in each expert's segment (dispatch_scan_kernel)
     const int nblk = int((nslots + DBS - 1) / DBS);
     if (tid < E) s_off[tid] = a.ws[int64_t(nblk) * E + int64_t(blockIdx.x) * E + tid];
+  } else if constexpr (MODE == DSP_RECOUNT) {
+    // whole-batch totals -> offsets; this block starts after the slots before it
+    int all = 0;
+    const int excl = block_excl_scan(tot + (tid < E ? s_tot[tid] : 0), s_wsum, &all);
+    if (tid < E) {
+      s_off[tid] = excl + s_pre[tid];
+      if (blockIdx.x == 0) a.offsets[tid] = excl;
+    }
+    if (tid == 0 && blockIdx.x == 0) a.offsets[E] = all;
   } else {
     int all = 0;
     const int excl = block_excl_scan(tot, s_wsum, &all);
@@ -169,9 +227,10 @@ __global__ __launch_bounds__(NTHR) void dispatch_kernel(DispatchArgs a) {
   // 3. rows, chunk by chunk in slot order
   if (c0 < c1) {
     const uint64_t below = (uint64_t(1) << l) - 1u;
-    SlotVals cur = load_slot(a, int64_t(c0) * 64 + l, nslots, true);
+    SlotVals cur = MODE == DSP_RECOUNT ? own : load_slot(a, int64_t(c0) * 64 + l, nslots, true);
     for (int c = c0; c < c1; ++c) {
-      const SlotVals nxt = load_slot(a, int64_t(min(c + 1, c1 - 1)) * 64 + l, nslots, true);
+      const SlotVals nxt =
+          MODE == DSP_RECOUNT ? cur : load_slot(a, int64_t(min(c + 1, c1 - 1)) * 64 + l, nslots, true);
       const int64_t s = int64_t(c) * 64 + l;
       const bool live = s < nslots && cur.kept && unsigned(cur.e) < unsigned(E);
       for (int e = l; e < E; e += 64) {
@@ -328,7 +387,7 @@ __global__ __launch_bounds__(NTHR) void dispatch_scan_kernel(DispatchArgs a, int
 
 size_t dispatch_workspace_bytes(int T, int E, int k) {
   const int64_t nslots = int64_t(T) * k;
-  if (nslots <= DBLOCK_MIN) return 256;
+  if (nslots <= RECOUNT_MAX) return 256;
   const int64_t nblk = (nslots + DBS - 1) / DBS;
   return size_t((nblk * E * 2 * 4 + 255) / 256 * 256);
 }
@@ -336,9 +395,12 @@ size_t dispatch_workspace_bytes(int T, int E, int k) {
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   const int64_t nslots = int64_t(a.T) * a.k;
   if (a.pool > 0) {
-    hipLaunchKernelGGL((dispatch_kernel<true, false>), dim3(1), dim3(NTHR), 0, s, a);
-  } else if (nslots <= DBLOCK_MIN) {
-    hipLaunchKernelGGL((dispatch_kernel<false, false>), dim3(1), dim3(NTHR), 0, s, a);
+    hipLaunchKernelGGL((dispatch_kernel<true, DSP_ONE>), dim3(1), dim3(NTHR), 0, s, a);
+  } else if (nslots <= RBS) {
+    hipLaunchKernelGGL((dispatch_kernel<false, DSP_ONE>), dim3(1), dim3(NTHR), 0, s, a);
+  } else if (nslots <= RECOUNT_MAX) {
+    hipLaunchKernelGGL((dispatch_kernel<false, DSP_RECOUNT>), dim3(int((nslots + RBS - 1) / RBS)), dim3(NTHR), 0,
+                       s, a);
   } else {
     // large batches: per-block counts, one scan, per-block rows
     const int nblk = int((nslots + DBS - 1) / DBS);
@@ -348,7 +410,7 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(NTHR), 0, s, a, nblk);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dispatch_kernel<false, true>), dim3(nblk), dim3(NTHR), 0, s, a);
+    hipLaunchKernelGGL((dispatch_kernel<false, DSP_BLOCK>), dim3(nblk), dim3(NTHR), 0, s, a);
   }
   return hipGetLastError();
 }
