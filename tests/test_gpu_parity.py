@@ -231,6 +231,34 @@ def test_qwen3_prefill_full_size(qwen, dev):
         assert np.array_equal(gp[name], g[name]), name
 
 
+def test_router_variants_batch_invariant(qwen, dev):
+    """A token's h and logits do not depend on the batch around it: the router
+    variants picked by batch size (16 experts per workgroup for small batches,
+    32, then 32 or 64 tokens per workgroup from T = 2048 and 4096) and the
+    linear layout (weights split on the fly) must agree bit for bit on shared
+    rows, and match the oracle on sampled rows."""
+    from workloads.device import make_tokens_device
+    L, tg, tr = qwen
+    S = L["shape"]
+    x = make_tokens_device(S, dev, seed=0, step=5, T=4100)
+    gl = GpuLayer(L, dev, packed=True)
+    full = gl.run(tg, tr, x=x)
+    lin = GpuLayer(L, dev, P=gl.P).run(tg, tr, x=x)
+    assert np.array_equal(full["h"], lin["h"])
+    assert np.array_equal(full["logits"].view(np.uint32), lin["logits"].view(np.uint32))
+    for T in (2050, 1024, 100, 3):
+        part = gl.run(tg, tr, x=x[:T].contiguous())
+        assert np.array_equal(part["h"], full["h"][:T]), T
+        assert np.array_equal(part["logits"].view(np.uint32), full["logits"][:T].view(np.uint32)), T
+    rows = [0, 15, 16, 63, 64, 2047, 2048, 4095, 4096, 4099]
+    xh = x[rows].float().cpu().numpy()
+    h_ref = oracle.rmsnorm(oracle.round_to_bf16(xh), L["gamma"], S.rms_eps, S.dtype)
+    diff = np.abs(values(full["h"][rows]) - h_ref)
+    assert np.all(diff <= np.abs(h_ref) * 2.0 ** -7 + 1e-30)
+    lg_ref = oracle.router_logits(h_ref, L["w_router"], L["router_bias"]).astype(np.float64)
+    assert np.max(np.abs(full["logits"][rows].astype(np.float64) - lg_ref)) <= 4e-3
+
+
 def test_glm45_air_shape_full_size(dev):
     """GLM-4.5-Air-shaped layer (H=4096, E=128, I=1408, top-8, bf16, T=4096,
     Zipf(1.1) router prior, lognormal(0,0.7) tables, 50% skip), drawn on the

@@ -18,6 +18,15 @@ constexpr int RNTHR = RW * 64;
 constexpr int NTHR = 256;     // 4 waves (top-k kernel)
 constexpr int EMAX = 256;
 constexpr int NARROW_HMAX = 8192;  // hidden size limit of the small-batch router variant
+#ifndef ACE_ROUTER_WIDE_T
+#define ACE_ROUTER_WIDE_T 2048     // batch from which the 32/64-token router variant is used
+#endif
+#ifndef ACE_ROUTER_WIDE_MT4_T
+#define ACE_ROUTER_WIDE_MT4_T (2 * ACE_ROUTER_WIDE_T)  // batch from which the 64-token variant is used
+#endif
+#ifndef ACE_ROUTER_WIDE_NBK4
+#define ACE_ROUTER_WIDE_NBK4 1     // k-steps per load batch of the 64-token variant
+#endif
 #ifndef ACE_ROUTER_NARROW_GX
 #define ACE_ROUTER_NARROW_GX 8     // token blocks up to which the 16-expert router variant is used
 #endif
@@ -281,6 +290,144 @@ reduce:
   }
 }
 
+// Kernel 1, large batches (bf16 with the pre-split router): 16*MT tokens x
+// 32 experts per workgroup, so that each plane fragment read feeds MT token
+// blocks instead of one.  Every step that fixes a value is the one of
+// norm_router_kernel: the inverse RMS of a row (same lane split, same wave
+// sum), h = make_h, the wave classes of k-steps (wave w takes k-steps w,
+// w+16, ...), the MFMA chain of each class in k order with planes 0, 1, 2,
+// and the sum of the 16 class partials in wave order, then the bias.  So a
+// logit is bit-identical to the one the other variants compute, whatever the
+// batch.  Workgroup L serves token block 8*(L/(8*ncb)) + L%8 and column
+// block (L/8) % ncb: a token block's column blocks run on one XCD, eight
+// launch slots apart, and share its x rows through that XCD's L2.
+template <int MT, int NBK>
+__global__ __launch_bounds__(RNTHR) void norm_router_wide_kernel(RouteArgs a, int gxw) {
+  static_assert(MT % 2 == 0, "rows of the RMS prologue go in pairs");
+  constexpr int TBW = TB * MT;
+  constexpr int ECBW = 32;
+  constexpr int EPL = 8, KS = 32;
+  __shared__ float s_inv[TBW];
+  __shared__ float s_part[RW][TB][ECBW + 1];
+  const int E = a.E, H = a.H;
+  const int ncb = (E + ECBW - 1) / ECBW;
+  const int L = blockIdx.x;
+  const int cbk = (L / 8) % ncb;
+  const int tbk = 8 * (L / (8 * ncb)) + L % 8;
+  if (tbk >= gxw) return;  // padding of the grid to whole groups of 8
+  const int w = wave_id(), l = lane_id();
+  const int tok0 = tbk * TBW;
+  const int q = l >> 4, r16 = l & 15;
+  const bf16_t* x = reinterpret_cast<const bf16_t*>(a.x);
+  bf16_t* hout = reinterpret_cast<bf16_t*>(a.h_out);
+  const int nks = H / KS;
+  const int CB = (E + 15) / 16;
+  const int cb0 = min(2 * cbk, CB - 1), cb1 = min(2 * cbk + 1, CB - 1);
+  const uint8_t* wp = reinterpret_cast<const uint8_t*>(a.w_router);
+  const int64_t plane_bytes = int64_t(CB) * nks * 1024;
+  const int nki = w < nks ? (nks - 1 - w) / RW + 1 : 0;
+  float bias_v = 0.f;
+  if (a.bias != nullptr && threadIdx.x < TB * ECBW) bias_v = a.bias[min(cbk * ECBW + int(threadIdx.x) % ECBW, E - 1)];
+
+  // inverse RMS: wave w owns tokens tok0 + w + 16*m, two rows in flight
+  {
+    constexpr int SEG = 64 * EPL;
+#pragma unroll
+    for (int m0 = 0; m0 < MT; m0 += 2) {
+      float ss[2] = {0.f, 0.f};
+      for (int j0 = 0; j0 < H; j0 += 8 * SEG) {
+        u32x4 v[2][8];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const bf16_t* row = x + int64_t(min(tok0 + w + 16 * (m0 + m), a.T - 1)) * H;
+#pragma unroll
+          for (int b = 0; b < 8; ++b) v[m][b] = ld16(row + min(j0 + b * SEG + l * EPL, H - EPL));
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int b = 0; b < 8; ++b)
+            if (j0 + b * SEG + l * EPL < H) ss[m] += sumsq16<bf16_t>(v[m][b]);
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const float t = wave_sum_dpp(ss[m]);
+        if (l == 0) s_inv[w + 16 * (m0 + m)] = 1.0f / sqrtf(t / float(H) + a.eps);
+      }
+    }
+  }
+  __syncthreads();
+  float inv[MT];
+  const bf16_t* xrow[MT];
+  bf16_t* hrow[MT];
+  bool wr[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    inv[m] = s_inv[16 * m + r16];
+    const int tt = tok0 + 16 * m + r16;
+    const int t = min(tt, a.T - 1);
+    xrow[m] = x + int64_t(t) * H;
+    hrow[m] = hout + int64_t(t) * H;
+    wr[m] = cbk == 0 && tt < a.T;
+  }
+
+  f32x4 acc[MT][2];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 px[NBK][MT], pl[NBK][2][3];
+  for (int i0 = 0; i0 < nki; i0 += NBK) {
+#pragma unroll
+    for (int b = 0; b < NBK; ++b) {
+      const int j = w + RW * min(i0 + b, nki - 1);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) px[b][m] = ld16(xrow[m] + j * KS + q * EPL);
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        pl[b][0][p] = ld16(wp + p * plane_bytes + (int64_t(cb0) * nks + j) * 1024 + l * 16);
+        pl[b][1][p] = ld16(wp + p * plane_bytes + (int64_t(cb1) * nks + j) * 1024 + l * 16);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NBK; ++b) {
+      if (i0 + b < nki) {
+        const int k0 = (w + RW * (i0 + b)) * KS + q * EPL;
+        f32x4 g[2];
+        g[0] = *reinterpret_cast<const f32x4*>(a.gamma + k0);
+        g[1] = *reinterpret_cast<const f32x4*>(a.gamma + k0 + 4);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const u32x4 h = make_h<bf16_t>(px[b][m], inv[m], g);
+          if (wr[m]) st16(hrow[m] + k0, h);
+          acc[m][0] = mma3(h, pl[b][0], acc[m][0]);
+          acc[m][1] = mma3(h, pl[b][1], acc[m][1]);
+        }
+      }
+    }
+  }
+
+  // class partials summed in wave order, one 16-token block at a time
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if (m > 0) __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) s_part[w][4 * q + j][16 * c + r16] = acc[m][c][j];
+    __syncthreads();
+    if (threadIdx.x < TB * ECBW) {
+      const int u = threadIdx.x;
+      const int tl = u / ECBW, c = u % ECBW, e = cbk * ECBW + c, to = tok0 + 16 * m + tl;
+      if (to < a.T && e < E) {
+        float v = s_part[0][tl][c];
+#pragma unroll
+        for (int ww = 1; ww < RW; ++ww) v += s_part[ww][tl][c];
+        if (a.bias) v += bias_v;
+        a.logits_out[int64_t(to) * E + e] = v;
+      }
+    }
+  }
+}
+
 // Kernel 2: top-k, gates and skip mask, one wave per token (topk_slots).
 __global__ __launch_bounds__(NTHR) void topk_skip_kernel(RouteArgs a) {
   constexpr int NWV = NTHR / 64;
@@ -365,7 +512,17 @@ hipError_t launch_route(int dtype, const RouteArgs& a, hipStream_t s, bool with_
   // workgroup, so that more workgroups share the router weights
   const bool narrow =
       dtype == 1 && a.router_packed && a.logits_in == nullptr && gx <= ACE_ROUTER_NARROW_GX && a.H <= NARROW_HMAX;
-  if (narrow) {
+  // large batches with the pre-split router: 32 or 64 tokens per workgroup
+  const bool wide = dtype == 1 && a.router_packed && a.logits_in == nullptr && a.T >= ACE_ROUTER_WIDE_T;
+  if (wide) {
+    const int mt = a.T >= ACE_ROUTER_WIDE_MT4_T ? 4 : 2;
+    const int gxw = (a.T + TB * mt - 1) / (TB * mt);
+    const unsigned nwg = unsigned((gxw + 7) / 8 * 8 * ((a.E + 31) / 32));
+    if (mt == 4)
+      hipLaunchKernelGGL((norm_router_wide_kernel<4, ACE_ROUTER_WIDE_NBK4>), dim3(nwg), block1, 0, s, a, gxw);
+    else
+      hipLaunchKernelGGL((norm_router_wide_kernel<2, 2>), dim3(nwg), block1, 0, s, a, gxw);
+  } else if (narrow) {
     hipLaunchKernelGGL((norm_router_kernel<bf16_t, 1>), dim3(gx, unsigned((a.E + 15) / 16)), block1, 0, s, a);
   } else {
     const dim3 grid1(gx, a.logits_in ? 1 : unsigned((a.E + 31) / 32));
