@@ -27,6 +27,9 @@ constexpr int NARROW_HMAX = 8192;  // hidden size limit of the small-batch route
 #ifndef ACE_ROUTER_WIDE_NBK4
 #define ACE_ROUTER_WIDE_NBK4 1     // k-steps per load batch of the 64-token variant
 #endif
+#ifndef ACE_ROUTER_NARROW_WG
+#define ACE_ROUTER_NARROW_WG 64    // workgroups aimed at by the small-batch variant's expert sub-blocks
+#endif
 #ifndef ACE_ROUTER_NARROW_GX
 #define ACE_ROUTER_NARROW_GX 8     // token blocks up to which the 16-expert router variant is used
 #endif
@@ -134,9 +137,15 @@ template <> __device__ __forceinline__ float sumsq16<float>(u32x4 v) {
 // rows past T and expert rows past E read a clamped valid row whose results
 // are never stored.  For small batches (NCB = 1: more workgroups share the
 // pre-split router planes) the first batch of a wave's weight and x loads is
-// issued before the RMS prologue, so that the two latencies overlap.
-template <typename T, int NCB>
+// issued before the RMS prologue, so that the two latencies overlap; with
+// SUB > 1 the column block is further cut into SUB sub-blocks of 16/SUB
+// experts, one per workgroup (lanes of other experts load nothing and their
+// MFMA columns are discarded: an output column depends only on its own
+// weights), so that the plane bytes of a decode batch spread over SUB times
+// more compute units.
+template <typename T, int NCB, int SUB = 1>
 __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
+  static_assert(SUB == 1 || NCB == 1, "sub-blocks of one column block only");
   constexpr int ECBW = 16 * NCB;          // experts per workgroup
   constexpr int NBK = NCB == 1 ? 4 : 2;   // k-steps per wave per load batch (pre-split planes)
   __shared__ float s_inv[TB];
@@ -162,9 +171,12 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
   // pre-split planes: [3][CB][nks][64][16 B]; this workgroup's column blocks
   const bool packed = sizeof(T) == 2 && do_router && a.router_packed;
   const int CB = (E + 15) / 16;
+  const int ycb = int(blockIdx.y) / SUB;                 // column block (pair) index
+  const int sub = int(blockIdx.y) % SUB;                 // sub-block of 16/SUB experts
+  const bool lane_e = SUB == 1 || r16 / (16 / SUB) == sub;  // this lane's expert is computed here
   int cb[NCB];
 #pragma unroll
-  for (int c = 0; c < NCB; ++c) cb[c] = min(int(blockIdx.y) * NCB + c, CB - 1);
+  for (int c = 0; c < NCB; ++c) cb[c] = min(ycb * NCB + c, CB - 1);
   const uint8_t* wp = reinterpret_cast<const uint8_t*>(a.w_router);
   const int64_t plane_bytes = int64_t(CB) * nks * 1024;
   const int nki = w < nks ? (nks - 1 - w) / RW + 1 : 0;  // this wave's k-steps
@@ -178,8 +190,10 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
 #pragma unroll
       for (int c = 0; c < NCB; ++c)
 #pragma unroll
-        for (int p = 0; p < 3; ++p)
-          pl[b][c][p] = ld16(wp + p * plane_bytes + (int64_t(cb[c]) * nks + j) * 1024 + l * 16);
+        for (int p = 0; p < 3; ++p) {
+          pl[b][c][p] = u32x4{0u, 0u, 0u, 0u};
+          if (lane_e) pl[b][c][p] = ld16(wp + p * plane_bytes + (int64_t(cb[c]) * nks + j) * 1024 + l * 16);
+        }
     }
   };
   constexpr bool EARLY = NCB == 1;  // registers allow the early batch only with one column block
@@ -187,7 +201,7 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
   // router bias of this thread's output (read after the last barrier)
   float bias_v = 0.f;
   if (do_router && a.bias != nullptr && threadIdx.x < TB * ECBW)
-    bias_v = a.bias[min(int(blockIdx.y) * ECBW + int(threadIdx.x) % ECBW, E - 1)];
+    bias_v = a.bias[min(ycb * ECBW + int(threadIdx.x) % ECBW, E - 1)];
   if constexpr (EARLY) {
     // gamma into LDS (H <= NARROW_HMAX on this path), read back after the barrier
     for (int h = threadIdx.x * 4; h < H; h += RNTHR * 4)
@@ -279,8 +293,8 @@ reduce:
   static_assert(TB * ECBW <= RNTHR, "one output per thread");
   if (threadIdx.x < TB * ECBW) {
     const int u = threadIdx.x;
-    const int tl = u / ECBW, c = u % ECBW, e = blockIdx.y * ECBW + c, to = tok0 + tl;
-    if (to < a.T && e < E) {
+    const int tl = u / ECBW, c = u % ECBW, e = ycb * ECBW + c, to = tok0 + tl;
+    if (to < a.T && e < E && (SUB == 1 || c / (16 / SUB) == sub)) {
       float v = s_part[0][tl][c];
 #pragma unroll
       for (int ww = 1; ww < RW; ++ww) v += s_part[ww][tl][c];
@@ -523,7 +537,15 @@ hipError_t launch_route(int dtype, const RouteArgs& a, hipStream_t s, bool with_
     else
       hipLaunchKernelGGL((norm_router_wide_kernel<2, 2>), dim3(nwg), block1, 0, s, a, gxw);
   } else if (narrow) {
-    hipLaunchKernelGGL((norm_router_kernel<bf16_t, 1>), dim3(gx, unsigned((a.E + 15) / 16)), block1, 0, s, a);
+    // sub-blocks: about ACE_ROUTER_NARROW_WG workgroups in all
+    const unsigned cb = unsigned((a.E + 15) / 16);
+    const unsigned sub = std::max(1u, std::min(4u, unsigned(ACE_ROUTER_NARROW_WG) / (gx * cb)));
+    if (sub >= 4)
+      hipLaunchKernelGGL((norm_router_kernel<bf16_t, 1, 4>), dim3(gx, cb * 4), block1, 0, s, a);
+    else if (sub >= 2)
+      hipLaunchKernelGGL((norm_router_kernel<bf16_t, 1, 2>), dim3(gx, cb * 2), block1, 0, s, a);
+    else
+      hipLaunchKernelGGL((norm_router_kernel<bf16_t, 1, 1>), dim3(gx, cb), block1, 0, s, a);
   } else {
     const dim3 grid1(gx, a.logits_in ? 1 : unsigned((a.E + 31) / 32));
     if (dtype == 1)
