@@ -329,7 +329,7 @@ def _fused_vs_steps(layer, x, tg, tr, residual):
         assert torch.equal(a1.view(torch.uint8), a2.view(torch.uint8)), name
 
 
-@pytest.mark.parametrize("M", [1, 3, 8])
+@pytest.mark.parametrize("M", [1, 3, 8, 9, 17, 32])
 @pytest.mark.parametrize("packed", [False, True])
 def test_fused_forward_matches_steps(qwen, dev, M, packed):
     """moe_forward at decode sizes (top-k, gates, skip rule and dispatch inside
@@ -342,10 +342,11 @@ def test_fused_forward_matches_steps(qwen, dev, M, packed):
 
 
 @pytest.mark.parametrize("fusion", ["max", "min", "mean", "score"])
-def test_fused_forward_matches_steps_f32(tiny, dev, fusion):
+@pytest.mark.parametrize("T", [6, 30])
+def test_fused_forward_matches_steps_f32(tiny, dev, fusion, T):
     L, tg, tr = tiny
     gl = GpuLayer(L, dev, fusion=fusion)
-    x = gl.P["x"][:6].contiguous()
+    x = gl.P["x"][:T].contiguous()
     _fused_vs_steps(gl.layer, x, float(tg), float(tr), None)
 
 

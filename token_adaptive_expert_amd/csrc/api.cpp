@@ -97,7 +97,7 @@ ace_status check_desc(const ace_moe_desc* d) {
 #ifndef ACE_FUSED_TOKENS
 #define ACE_FUSED_TOKENS 8
 #endif
-static_assert(ACE_FUSED_TOKENS <= ace::FUSED_TMAX, "fused kernel: one wave per token");
+static_assert(ACE_FUSED_TOKENS <= ace::FUSED_TMAX, "fused kernel: at most FUSED_TMAX tokens");
 
 #define REQUIRE(p)                                                                                     \
   do {                                                                                                 \
@@ -455,8 +455,9 @@ ace_status moe_forward(const ace_moe_desc* d, int32_t path, const void* x, const
     const size_t need = ace::dispatch_workspace_bytes(std::max(d->T, 1), d->E, d->k);
     if (workspace_bytes < need) return fail(ACE_EWORKSPACE, "workspace_bytes=%zu < %zu needed", workspace_bytes, need);
     if (d->T == 0) return ok();
+    // the fused kernel is the split-K tiling: only where moe_expert_forward would take it too
     const bool fused = d->T <= ACE_FUSED_TOKENS && d->expert_pool == 0 && logits_in == nullptr &&
-                       path != ACE_PATH_GROUPED;
+                       (path == ACE_PATH_STREAM || (path == ACE_PATH_AUTO && int64_t(d->T) * d->k <= 256));
     if (!fused) {
       st = moe_route_skip(d, x, gamma, w_router, router_bias, logits_in, logits_out, a_gsp, a_rcr, tau_gsp, tau_rcr,
                           h_out, topk_idx, topk_gate, keep, stream);

@@ -537,9 +537,9 @@ __global__ __launch_bounds__(SK_NW * 64) void expert_splitk_fused_kernel(FusedAr
   constexpr int COLS = 16;
   constexpr int SK_NBK = 8;
   constexpr int MAXS = FUSED_TMAX * 16;
-  static_assert(SK_NW >= FUSED_TMAX, "one wave per token");
+  static_assert(FUSED_TMAX <= 32, "an expert's tokens are a 32-bit mask");
   __shared__ float s_tg[EMAX_EXP], s_tr[EMAX_EXP];
-  __shared__ double s_z[FUSED_TMAX][EMAX_EXP];
+  __shared__ double s_z[SK_NW][EMAX_EXP];
   __shared__ int32_t s_idx[MAXS];
   __shared__ float s_gate[MAXS];
   __shared__ uint8_t s_keep[MAXS];
@@ -556,7 +556,7 @@ __global__ __launch_bounds__(SK_NW * 64) void expert_splitk_fused_kernel(FusedAr
   const int nslots = Tn * k;
   const bool writer = blockIdx.x == 0;
 
-  // 1. tables, masks, logits of token w
+  // 1. tables, masks, the first token's logits of each wave
   for (int e = tid; e < EMAX_EXP; e += SK_NW * 64) {
     const int ec = min(e, E - 1);
     s_tg[e] = f.a_gsp[ec];
@@ -564,27 +564,32 @@ __global__ __launch_bounds__(SK_NW * 64) void expert_splitk_fused_kernel(FusedAr
     s_mask[e] = 0u;
   }
   float v[4];
-  const int tw = min(w, Tn - 1);
+  auto load_logits = [&](int t) {
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) v[rr] = f.logits[int64_t(tw) * E + min(l + 64 * rr, E - 1)];
+    for (int rr = 0; rr < 4; ++rr) v[rr] = f.logits[int64_t(min(t, Tn - 1)) * E + min(l + 64 * rr, E - 1)];
+  };
+  load_logits(w);
   __syncthreads();
-  // 2. top-k, gates, skip decision: wave t for token t
-  if (w < Tn) {
+  // 2. top-k, gates, skip decision: wave w for tokens w, w + SK_NW, ...
+  {
     const TopkParams p{E, k, f.norm_topk, f.fusion, f.tau_gsp, f.tau_rcr};
-    int my_e;
-    float g;
-    bool kp;
-    topk_slots(v, p, s_tg, s_tr, s_z[w], my_e, g, kp);
-    if (l < k) {
-      const int sidx = w * k + l;
-      s_idx[sidx] = my_e;
-      s_gate[sidx] = g;
-      s_keep[sidx] = kp ? 1 : 0;
-      if (kp) atomicOr(&s_mask[my_e], 1u << w);
-      if (writer) {
-        f.topk_idx[sidx] = my_e;
-        f.topk_gate[sidx] = g;
-        f.keep[sidx] = kp ? 1 : 0;
+    for (int t = w; t < Tn; t += SK_NW) {
+      if (t > w) load_logits(t);
+      int my_e;
+      float g;
+      bool kp;
+      topk_slots(v, p, s_tg, s_tr, s_z[w], my_e, g, kp);
+      if (l < k) {
+        const int sidx = t * k + l;
+        s_idx[sidx] = my_e;
+        s_gate[sidx] = g;
+        s_keep[sidx] = kp ? 1 : 0;
+        if (kp) atomicOr(&s_mask[my_e], 1u << t);
+        if (writer) {
+          f.topk_idx[sidx] = my_e;
+          f.topk_gate[sidx] = g;
+          f.keep[sidx] = kp ? 1 : 0;
+        }
       }
     }
   }

@@ -54,7 +54,7 @@ struct ExpertArgs {
 
 // Fused small-batch gate/up (T <= FUSED_TMAX tokens): routing and dispatch are
 // derived from the router logits inside every workgroup; workgroup 0 writes them.
-constexpr int FUSED_TMAX = 8;
+constexpr int FUSED_TMAX = 32;
 struct FusedArgs {
   ExpertArgs g;               // gate/up GEMM (offsets / sorted_token unused: made in LDS)
   const float* logits;        // [T, E] f32
