@@ -42,6 +42,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-tables", action="store_true", help="skip timing the offline table builder")
     p.add_argument("--no-stack", action="store_true", help="skip the 48-layer stack")
+    p.add_argument("--decode-m", type=int, nargs="+", help="decode batch sizes to run (default: all)")
     p.add_argument("--only", choices=["decode", "glm", "t32k", "stack", "tables"],
                    help="run that leg alone and print its result (for profiling runs), not the contract line")
     p.add_argument("--no-extra", action="store_true",
@@ -202,17 +203,37 @@ class Bench:
         from workloads.torch_io import to_torch
         out = {}
         S = self.S
-        for M in workloads.DECODE_M:
+        for M in (self.args.decode_m or workloads.DECODE_M):
             Sd = workloads.CONFIGS["qwen3_30b_a3b_decode"].with_tokens(M)
             x = to_torch(workloads.make_tokens(Sd, seed=0, step=1), self.dev)
             ms, bufs = self.run_steps(x, tau, max(self.args.steps, 50), self.args.warmup, 0)
             gms, _ = self.graph_ms(x, tau, self.layers)
             gms /= len(self.layers)
+            iso = self.isolated_ms(x, tau)
             n_kept, U = self.counts(bufs)
             wbytes = U * 3 * S.H * S.I * 2
-            out[M] = dict(us=gms * 1e3, eager_us=ms * 1e3, U=U, n_kept=n_kept, retained_weight_MB=wbytes / 1e6,
-                          hbm_frac=(wbytes / (gms * 1e-3)) / (HBM_PEAK_GBS * 1e9))
+            out[M] = dict(us=gms * 1e3, eager_us=ms * 1e3, isolated_us=iso * 1e3, U=U, n_kept=n_kept,
+                          retained_weight_MB=wbytes / 1e6, hbm_frac=(wbytes / (gms * 1e-3)) / (HBM_PEAK_GBS * 1e9))
         return out
+
+    def isolated_ms(self, x, tau, reps=30):
+        """Median ms of one layer forward launched alone: the device idle
+        before it (synchronised), HIP events around the single call, weights
+        rotating over the copies."""
+        torch = self.torch
+        bufs = self.layers[0].buffers(x.shape[0])
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t = []
+        for i in range(reps + 3):
+            lay = self.layers[i % len(self.layers)]
+            torch.cuda.synchronize()
+            start.record()
+            lay.forward(x, tau[0], tau[1], bufs)
+            stop.record()
+            torch.cuda.synchronize()
+            if i >= 3:
+                t.append(start.elapsed_time(stop))
+        return float(np.median(t))
 
     def decode_pool(self, tau, pools=(16, 32), Ms=(8, 32, 64)):
         """Decode with the batch-level expert-pool cap m (graph replays)."""
@@ -434,7 +455,10 @@ def main():
         import workloads
         if args.only in ("decode",):
             tau = B.calibrate(B.P["x"], args.skip)
-            out = {"decode_us_per_layer": {str(m): round(v["us"], 2) for m, v in B.decode(tau).items()}}
+            dec = B.decode(tau)
+            out = {"decode_us_per_layer": {str(m): round(v["us"], 2) for m, v in dec.items()},
+                   "decode_isolated_us_per_layer": {str(m): round(v["isolated_us"], 2) for m, v in dec.items()},
+                   "U": {str(m): v["U"] for m, v in dec.items()}}
         elif args.only == "glm":
             out = extra_prefill(B, "glm45_air_shape MoE layer prefill (Zipf router prior)",
                                 workloads.CONFIGS["glm45_air_shape"], 4096, 0.5, max(10, args.steps // 2), 3)
@@ -501,6 +525,7 @@ def main():
         dec = B.decode(head["tau"])
         res["decode_us_per_layer"] = {str(m): round(v["us"], 2) for m, v in dec.items()}
         res["decode_eager_us_per_layer"] = {str(m): round(v["eager_us"], 2) for m, v in dec.items()}
+        res["decode_isolated_us_per_layer"] = {str(m): round(v["isolated_us"], 2) for m, v in dec.items()}
         res["decode_pool"] = B.decode_pool(head["tau"])
         res["decode_detail"] = {str(m): {k2: (round(v2, 4) if isinstance(v2, float) else v2) for k2, v2 in v.items()}
                                 for m, v in dec.items()}
