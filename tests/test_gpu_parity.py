@@ -197,6 +197,43 @@ def test_one_expert_takes_every_token(dev, path):
     assert rel_l2(values(g["y"]), ref["y"]) <= TOL["bf16"]
 
 
+# ---------------------------------------------------------------- seeded random shapes
+def _random_case(i):
+    rng = np.random.default_rng(9000 + i)
+    dtype = "f32" if i % 4 == 0 else "bf16"
+    E = int(rng.integers(2, 65))
+    k = int(rng.integers(1, min(E, 16) + 1))
+    T = int(rng.integers(1, max(2, 2048 // k)))
+    H = 128 * int(rng.integers(1, 5))
+    I = 128 * int(rng.integers(1, 5))
+    S = workloads.small_shape(T=T, H=H, E=E, I=I, k=k, dtype=dtype, cfg_id=200 + i,
+                              zipf_s=float(rng.choice([0.0, 1.1])), norm_topk=int(rng.integers(0, 2)))
+    path = int(rng.choice(PATHS + [ace.ACE_PATH_AUTO]))
+    fusion = str(rng.choice(["max", "max", "min", "mean", "gsp", "rcr", "score"]))
+    rate = float(rng.choice([0.0, 0.3, 0.6]))
+    packed = dtype == "bf16" and bool(rng.integers(0, 2))
+    return S, path, fusion, rate, packed
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_shapes(dev, i):
+    """Seeded random layers (E 2..64, k 1..16, T up to 2047 slots, H and I from
+    128 to 512, f32 and bf16, Zipf or flat routers, every fusion rule and
+    tiling, both weight layouts) against the oracle: routing, gates, skip mask
+    and dispatch bit for bit on shared logits, y and slot rows within the
+    dtype's tolerance."""
+    S, path, fusion, rate, packed = _random_case(i)
+    print(f"[random case {i}] {S} path={path} fusion={fusion} rate={rate} packed={packed}", flush=True)
+    L = workloads.make_layer(S)
+    tg, tr = oracle_thresholds(L, min(rate, (S.k - 1) / S.k))
+    g = GpuLayer(L, dev, fusion=fusion, packed=packed).run(tg, tr, path)
+    check_routing_shared_logits(L, g, tg, tr, fusion=fusion)
+    check_dispatch(S, g)
+    ref = oracle_y(L, g, tg, tr, fusion=fusion)
+    assert rel_l2(values(g["y"]), ref["y"]) <= TOL[S.dtype]
+    check_slot_outputs(L, g, ref, TOL[S.dtype])
+
+
 # ---------------------------------------------------------------- full Qwen3-30B-A3B-shaped layer
 @pytest.fixture(scope="module")
 def qwen():
