@@ -39,6 +39,12 @@ namespace {
 #ifndef ACE_BIG_RB
 #define ACE_BIG_RB 8          // 16-row blocks per tile for batches with >= 512 slots per expert
 #endif
+#ifndef ACE_SMALL_RB_GATEUP
+#define ACE_SMALL_RB_GATEUP 3 // 16-row blocks per gate/up tile for moderate batches (<= 64 slots per expert)
+#endif
+#ifndef ACE_SMALL_RB_DOWN
+#define ACE_SMALL_RB_DOWN 2   // the same for the down projection
+#endif
 #ifndef ACE_GATEUP_NW
 #define ACE_GATEUP_NW 4       // waves per grouped gate/up tile (16 intermediate units each)
 #endif
@@ -819,7 +825,8 @@ hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs
       return kind == 0 ? launch_one<bf16_t, ACE_BIG_RB, 8, 0, 2>(a, T, k, s)
                        : launch_one<bf16_t, ACE_BIG_RB, 8, 1, 2>(a, T, k, s);
     if (small_rb)
-      return kind == 0 ? launch_one<bf16_t, 2, NG, 0, S>(a, T, k, s) : launch_one<bf16_t, 2, ND, 1, S>(a, T, k, s);
+      return kind == 0 ? launch_one<bf16_t, ACE_SMALL_RB_GATEUP, NG, 0, S>(a, T, k, s)
+                       : launch_one<bf16_t, ACE_SMALL_RB_DOWN, ND, 1, S>(a, T, k, s);
     return kind == 0 ? launch_one<bf16_t, G, NG, 0, S>(a, T, k, s)
                      : launch_one<bf16_t, G, ND, 1, S>(a, T, k, s);
   }
