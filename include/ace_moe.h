@@ -57,9 +57,11 @@ typedef enum {
 
 typedef enum { ACE_F32 = 0, ACE_BF16 = 1 } ace_dtype;
 
-/* Expert-GEMM schedule.  GROUPED tiles 64 slot rows per weight tile (prefill);
- * STREAM tiles 16 rows and splits weights finer, for small batches whose cost
- * is reading the retained experts' weights (decode).  AUTO picks by T*k. */
+/* Expert-GEMM schedule.  GROUPED tiles 32 to 128 slot rows per weight tile
+ * (prefill and most decode batches); STREAM tiles 16 rows and splits the
+ * contraction over the waves of a tile, for the smallest batches, whose cost
+ * is reading the retained experts' weights with little work per byte.  AUTO
+ * takes STREAM for T*k <= 64 routed slots, GROUPED above. */
 typedef enum { ACE_PATH_AUTO = 0, ACE_PATH_GROUPED = 1, ACE_PATH_STREAM = 2 } ace_path;
 /* Optional bits or-ed into the path argument of moe_expert_forward to run
  * only one of its two kernels (for timing a stage alone); no bit = both. */
@@ -200,8 +202,9 @@ ace_status moe_combine(const ace_moe_desc* d, const int32_t* slot_pos, const flo
  * moe_forward -- the whole layer in one call: moe_route_skip, moe_dispatch,
  * moe_expert_forward (path) and moe_combine with the arguments of those four
  * calls (same meanings, layouts and outputs; residual may be NULL).  For
- * decode-sized batches (1 <= T <= 8, desc->expert_pool = 0, logits_in NULL,
- * path AUTO or STREAM) the top-k, gates, skip rule and dispatch run inside
+ * decode-sized batches (1 <= T <= 8 with T*k <= 64 for path AUTO, or path
+ * STREAM; desc->expert_pool = 0; logits_in NULL) the top-k, gates, skip
+ * rule and dispatch run inside
  * the gate/up kernel's workgroups (two fewer dependent launches); every
  * output is bit-identical to the four separate calls.  All arguments are
  * validated before anything is launched.

@@ -94,6 +94,11 @@ ace_status check_desc(const ace_moe_desc* d) {
 // aligned (the kernels use 16-byte vector loads and stores).
 // Largest batch that moe_forward runs through the fused small-batch kernel
 // (at most ace::FUSED_TMAX).
+// AUTO path: batches of at most this many routed slots take the split-K
+// ("stream") expert tiling, larger ones the grouped tiling.
+#ifndef ACE_STREAM_MAX_SLOTS
+#define ACE_STREAM_MAX_SLOTS 64
+#endif
 #ifndef ACE_FUSED_TOKENS
 #define ACE_FUSED_TOKENS 8
 #endif
@@ -246,7 +251,7 @@ ace_status moe_expert_forward(const ace_moe_desc* d, int32_t path, const void* h
     st = num_cu(&ncu);
     if (st != ACE_OK) return st;
     const bool stream_path =
-        path == ACE_PATH_STREAM || (path == ACE_PATH_AUTO && int64_t(d->T) * d->k <= 256);
+        path == ACE_PATH_STREAM || (path == ACE_PATH_AUTO && int64_t(d->T) * d->k <= ACE_STREAM_MAX_SLOTS);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
     g_ev_start = g_ev_stop = nullptr;
@@ -457,7 +462,7 @@ ace_status moe_forward(const ace_moe_desc* d, int32_t path, const void* x, const
     if (d->T == 0) return ok();
     // the fused kernel is the split-K tiling: only where moe_expert_forward would take it too
     const bool fused = d->T <= ACE_FUSED_TOKENS && d->expert_pool == 0 && logits_in == nullptr &&
-                       (path == ACE_PATH_STREAM || (path == ACE_PATH_AUTO && int64_t(d->T) * d->k <= 256));
+                       (path == ACE_PATH_STREAM || (path == ACE_PATH_AUTO && int64_t(d->T) * d->k <= ACE_STREAM_MAX_SLOTS));
     if (!fused) {
       st = moe_route_skip(d, x, gamma, w_router, router_bias, logits_in, logits_out, a_gsp, a_rcr, tau_gsp, tau_rcr,
                           h_out, topk_idx, topk_gate, keep, stream);
