@@ -811,9 +811,12 @@ hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs
                          hipStream_t s) {
   constexpr int G = ACE_GROUPED_RB, S = ACE_GROUPED_STAGES;
   // moderate batches (up to 64 routed slots per expert on average before
-  // skipping): 32-row tiles, more of them, less padding.  Very large batches
-  // (at least 512 slots per expert): 128-row tiles of 8 waves, which halve
-  // the L2 traffic per MFMA when the GEMMs become compute-bound.
+  // skipping): 48-row gate/up tiles (3 per CU) and 32-row down tiles (4 per
+  // CU); with one m-tile per expert the tile count then fills whole rounds
+  // of the resident slots at the sizes measured (1536 gate/up tiles at
+  // T = 1024, E = 128).  Very large batches (at least 512 slots per expert):
+  // 128-row tiles of 8 waves, which halve the L2 traffic per MFMA when the
+  // GEMMs become compute-bound.  Between the two: 64-row tiles.
   const bool small_rb = int64_t(T) * k <= int64_t(64) * a.E && G > 2;
   // (the 8-wave down tile covers 256 output columns: H must be a multiple of 256)
   const bool big_rb = int64_t(T) * k >= int64_t(512) * a.E && a.N % (kind == 0 ? 128 : 256) == 0;
