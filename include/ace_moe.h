@@ -122,7 +122,9 @@ size_t moe_workspace_bytes(const ace_moe_desc* d);
  *   h[t]      = x[t] / sqrt(mean_j x[t,j]^2 + rms_eps) * gamma   (x = x̄Γ, Theoretical
  *               Foundation), stored in dtype.
  *   logits[t] = h[t] . w_router^T (+ router_bias), float32 accumulation in a
- *               fixed order (deterministic).
+ *               fixed order (deterministic), the same for every batch size
+ *               and layout: a token's h and logits do not depend on the
+ *               other rows of x.
  *   topk_idx  = the k largest logits, descending, equal logits to the lower
  *               expert index; slot 0 is the top-1 expert.
  *   topk_gate = softmax of the logits in float64 (over all E, or over the k
