@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--no-tables", action="store_true", help="skip timing the offline table builder")
     p.add_argument("--no-stack", action="store_true", help="skip the 48-layer stack")
     p.add_argument("--decode-m", type=int, nargs="+", help="decode batch sizes to run (default: all)")
-    p.add_argument("--only", choices=["decode", "glm", "t32k", "stack", "tables"],
+    p.add_argument("--only", choices=["decode", "glm", "t32k", "stack", "tables", "calib"],
                    help="run that leg alone and print its result (for profiling runs), not the contract line")
     p.add_argument("--no-extra", action="store_true",
                    help="skip the GLM-4.5-Air-shaped layer, the T=32768 run and the dense GEMM ceiling")
@@ -371,6 +371,32 @@ def stack48(B, decode_steps=128, M=8):
     return out
 
 
+def calibration_leg(B, reps=5):
+    """Time moe_calibrate_thresholds (per-layer thresholds by quantile mapping
+    on the layer's own routed slots, 60% skip) at T = 1024 and 4096 on the
+    generated layer; the skip count it yields is checked against the target."""
+    torch, ace, S = B.torch, B.ace, B.S
+    from workloads.device import make_tokens_device
+    lay = B.layers[0]
+    out = {}
+    for T in (1024, 4096):
+        x = B.P["x"] if T == S.T else make_tokens_device(S, B.dev, seed=0, step=11, T=T)
+        b = lay.buffers(T)
+        lay.route(x, 0.0, 0.0, b)
+        d = lay.desc(T)
+        ws = torch.empty(ace.moe_calibrate_workspace_bytes(d), dtype=torch.uint8, device=B.dev)
+        tau = torch.zeros(2, dtype=torch.float32, device=B.dev)
+        run = lambda i: ace.moe_calibrate_thresholds(d, b.topk_idx, b.topk_gate, lay.a_gsp, lay.a_rcr, 0.6, tau,
+                                                     None, ws)
+        ms = timed(torch, run, reps, 1)
+        tg, tr = [float(v) for v in tau.cpu()]
+        lay.route(x, tg, tr, b)
+        skipped = int((b.keep == 0).sum().item())
+        out[str(T)] = {"ms": round(ms, 4), "eligible_slots": T * (S.k - 1),
+                       "skipped": skipped, "target": int(math.floor(0.6 * T * S.k + 0.5))}
+    return out
+
+
 def tables_build(B, reps=5):
     """Time moe_build_tables (A^GSP and A^RCR of the layer from its weights,
     done once per checkpoint) on the generated layer's linear weights.
@@ -467,6 +493,8 @@ def main():
                                 max(5, args.steps // 4), 2, P=B.P, layer=B.layers[0])
         elif args.only == "stack":
             out = stack48(B)
+        elif args.only == "calib":
+            out = calibration_leg(B)
         else:
             out = tables_build(B)
         print(json.dumps({"only": args.only, "result": out}), flush=True)
@@ -541,6 +569,7 @@ def main():
         res["stack48"] = stack48(B)
     if not args.no_tables:
         res["tables_build"] = tables_build(B)
+        res["calibration"] = calibration_leg(B)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(B.L, S, head["tau"], args.cpu_tokens)
     print(json.dumps(res), flush=True)

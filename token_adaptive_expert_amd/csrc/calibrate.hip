@@ -16,10 +16,14 @@
 // "both scores below their thresholds" selects exactly the slots of fused
 // rank < m.
 //
-// Kernel 1 ranks every eligible slot in both views by counting, against LDS
-// tiles of all scores (O(N^2) compares, which is cheap at calibration sizes
-// and needs no sort).  Kernel 2 (one workgroup) binary-searches m and places
-// the two thresholds.
+// A slot's rank in a view is the number of eligible slots with a smaller
+// (score, slot) key: unique 64-bit keys (the score's order-preserving bits,
+// then the slot index) make "ties by slot order" a plain comparison.
+// Kernel 1 sorts the keys of each tile of CALIB_TILE slots in LDS (bitonic
+// network); kernel 2 gives every slot its rank as the sum, over the tiles,
+// of the number of keys below its own (a binary search in the tile, staged
+// in LDS): O(N log N) work per tile pass instead of N^2 compares.  Kernel 3
+// (one workgroup) binary-searches m and places the two thresholds.
 #include "kernels.h"
 
 namespace ace {
@@ -39,24 +43,82 @@ __device__ __forceinline__ void slot_scores(const CalibArgs& a, int j, float* sg
 }
 }  // namespace
 
+// Order-preserving 32-bit image of a float (finite values and +-0).
+__device__ __forceinline__ uint32_t ordered_bits(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ void slot_keys(const CalibArgs& a, int j, uint64_t* kg, uint64_t* kr, float* sg,
+                                          float* sr) {
+  slot_scores(a, j, sg, sr);
+  *kg = (uint64_t(ordered_bits(*sg)) << 32) | uint32_t(j);
+  *kr = (uint64_t(ordered_bits(*sr)) << 32) | uint32_t(j);
+}
+
+// Kernel 1: keys of one tile sorted ascending in LDS (bitonic network, one
+// compare-exchange pair per thread per stage); slots past N get the largest key.
+__global__ __launch_bounds__(CALIB_TILE / 2) void calib_tile_sort_kernel(CalibArgs a) {
+  constexpr int TL = CALIB_TILE;
+  __shared__ uint64_t s_k[2][TL];
+  const int tid = threadIdx.x;
+  const int base = blockIdx.x * TL;
+  for (int u = tid; u < TL; u += TL / 2) {
+    uint64_t kg = ~uint64_t(0), kr = ~uint64_t(0);
+    float sg, sr;
+    if (base + u < a.N) slot_keys(a, base + u, &kg, &kr, &sg, &sr);
+    s_k[0][u] = kg;
+    s_k[1][u] = kr;
+  }
+  __syncthreads();
+  for (int kk = 2; kk <= TL; kk <<= 1) {
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      const int i = (tid / jj) * 2 * jj + (tid % jj), ixj = i + jj;  // pair (i, i ^ jj), i < ixj
+      const bool asc = (i & kk) == 0;
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const uint64_t x = s_k[v][i], y = s_k[v][ixj];
+        if ((x > y) == asc) {
+          s_k[v][i] = y;
+          s_k[v][ixj] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int u = tid; u < TL; u += TL / 2) {
+    a.ws_key_g[base + u] = s_k[0][u];
+    a.ws_key_r[base + u] = s_k[1][u];
+  }
+}
+
+// Number of keys below x in a sorted LDS tile of CALIB_TILE keys.
+__device__ __forceinline__ int count_below(const uint64_t* s, uint64_t x) {
+  int pos = 0;
+#pragma unroll
+  for (int step = CALIB_TILE; step > 0; step >>= 1)
+    if (pos + step <= CALIB_TILE && s[pos + step - 1] < x) pos += step;
+  return pos;
+}
+
+// Kernel 2: ranks in both views, and the scores in rank order.
 __global__ __launch_bounds__(RT) void calib_rank_kernel(CalibArgs a) {
-  __shared__ float s_g[RT], s_r[RT];
+  __shared__ uint64_t s_k[2][CALIB_TILE];
   const int N = a.N;
   const int j = blockIdx.x * RT + threadIdx.x;
+  uint64_t kg = 0, kr = 0;
   float mg = 0.f, mr = 0.f;
-  if (j < N) slot_scores(a, j, &mg, &mr);
+  if (j < N) slot_keys(a, j, &kg, &kr, &mg, &mr);
   int rg = 0, rr = 0;
-  for (int base = 0; base < N; base += RT) {
-    const int jj = base + threadIdx.x;
-    if (jj < N) slot_scores(a, jj, &s_g[threadIdx.x], &s_r[threadIdx.x]);
-    __syncthreads();
-    const int lim = min(RT, N - base);
-    for (int u = 0; u < lim; ++u) {
-      const int o = base + u;
-      const float vg = s_g[u], vr = s_r[u];
-      rg += (vg < mg || (vg == mg && o < j)) ? 1 : 0;
-      rr += (vr < mr || (vr == mr && o < j)) ? 1 : 0;
+  const int ntiles = (N + CALIB_TILE - 1) / CALIB_TILE;
+  for (int t = 0; t < ntiles; ++t) {
+    for (int u = threadIdx.x; u < CALIB_TILE; u += RT) {
+      s_k[0][u] = a.ws_key_g[int64_t(t) * CALIB_TILE + u];
+      s_k[1][u] = a.ws_key_r[int64_t(t) * CALIB_TILE + u];
     }
+    __syncthreads();
+    rg += count_below(s_k[0], kg);
+    rr += count_below(s_k[1], kr);
     __syncthreads();
   }
   if (j < N) {
@@ -140,19 +202,26 @@ __global__ __launch_bounds__(FT) void calib_finish_kernel(CalibArgs a) {
 
 size_t calib_workspace_bytes(int T, int k) {
   const size_t N = size_t(T) * size_t(k > 1 ? k - 1 : 0);
-  return 4 * ((N * sizeof(int32_t) + 255) & ~size_t(255));
+  const size_t npad = (N + CALIB_TILE - 1) / CALIB_TILE * CALIB_TILE;
+  return 4 * ((N * sizeof(int32_t) + 255) & ~size_t(255)) + 2 * npad * sizeof(uint64_t);
 }
 
 hipError_t launch_calibrate(CalibArgs a, void* workspace, hipStream_t s) {
   const size_t stride = (size_t(a.N) * sizeof(int32_t) + 255) & ~size_t(255);
+  const size_t npad = (size_t(a.N) + CALIB_TILE - 1) / CALIB_TILE * CALIB_TILE;
   uint8_t* w = static_cast<uint8_t*>(workspace);
   a.ws_rank_g = reinterpret_cast<int32_t*>(w);
   a.ws_rank_r = reinterpret_cast<int32_t*>(w + stride);
   a.ws_score_g = reinterpret_cast<float*>(w + 2 * stride);
   a.ws_score_r = reinterpret_cast<float*>(w + 3 * stride);
+  a.ws_key_g = reinterpret_cast<uint64_t*>(w + 4 * stride);
+  a.ws_key_r = reinterpret_cast<uint64_t*>(w + 4 * stride + npad * sizeof(uint64_t));
   if (a.N > 0 && a.n_target > 0) {
-    hipLaunchKernelGGL(calib_rank_kernel, dim3((a.N + RT - 1) / RT), dim3(RT), 0, s, a);
+    hipLaunchKernelGGL(calib_tile_sort_kernel, dim3(unsigned(npad / CALIB_TILE)), dim3(CALIB_TILE / 2), 0, s, a);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(calib_rank_kernel, dim3((a.N + RT - 1) / RT), dim3(RT), 0, s, a);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(calib_finish_kernel, dim3(1), dim3(FT), 0, s, a);

@@ -90,8 +90,11 @@ struct CalibArgs {
   int32_t* ws_rank_r;
   float* ws_score_g;    // scores in ascending rank order
   float* ws_score_r;
+  uint64_t* ws_key_g;   // (score, slot) keys, sorted within tiles of CALIB_TILE
+  uint64_t* ws_key_r;
   int T, k, N, n_target;
 };
+constexpr int CALIB_TILE = 1024;
 
 struct TablesArgs {
   const float* gamma;     // [H]
