@@ -197,29 +197,47 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
     }
   };
   constexpr bool EARLY = NCB == 1;  // registers allow the early batch only with one column block
-  if (EARLY && packed && nki > 0) issue(0);
+  constexpr int GQ = NARROW_HMAX / (RNTHR * 4);  // gamma quads per thread for the LDS copy
   // router bias of this thread's output (read after the last barrier)
   float bias_v = 0.f;
   if (do_router && a.bias != nullptr && threadIdx.x < TB * ECBW)
     bias_v = a.bias[min(ycb * ECBW + int(threadIdx.x) % ECBW, E - 1)];
-  if constexpr (EARLY) {
-    // gamma into LDS (H <= NARROW_HMAX on this path), read back after the barrier
-    for (int h = threadIdx.x * 4; h < H; h += RNTHR * 4)
-      *reinterpret_cast<f32x4*>(&s_gam[h]) = *reinterpret_cast<const f32x4*>(a.gamma + h);
-  }
 
   // inverse RMS: wave w owns token tok0 + w; a row is read 8 segments of
-  // 64 lanes x 16 bytes at a time, all in flight together
+  // 64 lanes x 16 bytes at a time, all in flight together.  With EARLY, the
+  // gamma quads for the LDS copy (H <= NARROW_HMAX on this path) and the
+  // first batch of router loads go out behind the row's first segments:
+  // loads complete in order, so the sum waits for the row only and the
+  // router planes stay in flight across the barrier.
   {
     const T* row = x + int64_t(min(tok0 + w, a.T - 1)) * H;
     constexpr int SEG = 64 * EPL;
+    // segments per batch (4 with EARLY, for registers); the per-lane sum runs
+    // over the segments in order either way, so the result is the same
+    constexpr int RSEG = EARLY ? 4 : 8;
     float ss = 0.f;
-    for (int j0 = 0; j0 < H; j0 += 8 * SEG) {
-      u32x4 v[8];
+    for (int j0 = 0; j0 < H; j0 += RSEG * SEG) {
+      u32x4 v[RSEG];
 #pragma unroll
-      for (int b = 0; b < 8; ++b) v[b] = ld16(row + min(j0 + b * SEG + l * EPL, H - EPL));
+      for (int b = 0; b < RSEG; ++b) v[b] = ld16(row + min(j0 + b * SEG + l * EPL, H - EPL));
+      if constexpr (EARLY) {
+        if (j0 == 0) {
+          f32x4 gq[GQ];
 #pragma unroll
-      for (int b = 0; b < 8; ++b)
+          for (int i = 0; i < GQ; ++i) {
+            const int h = (int(threadIdx.x) + i * RNTHR) * 4;
+            if (h < H) gq[i] = *reinterpret_cast<const f32x4*>(a.gamma + h);
+          }
+          if (packed && nki > 0) issue(0);
+#pragma unroll
+          for (int i = 0; i < GQ; ++i) {
+            const int h = (int(threadIdx.x) + i * RNTHR) * 4;
+            if (h < H) *reinterpret_cast<f32x4*>(&s_gam[h]) = gq[i];  // read back after the barrier
+          }
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < RSEG; ++b)
         if (j0 + b * SEG + l * EPL < H) ss += sumsq16<T>(v[b]);
     }
     ss = wave_sum_dpp(ss);
