@@ -234,6 +234,34 @@ def test_random_shapes(dev, i):
     check_slot_outputs(L, g, ref, TOL[S.dtype])
 
 
+@pytest.mark.parametrize("i", range(6))
+def test_random_large_batches(dev, i):
+    """Seeded random layers of 1000-4200 tokens (multi-workgroup dispatch, the
+    32/64-token router, 64- and 128-row tiles): routing, gates, skip mask and
+    dispatch bit for bit on shared logits; y on sampled tokens."""
+    rng = np.random.default_rng(77000 + i)
+    E = int(rng.choice([8, 16, 64, 128, 256]))
+    k = int(rng.integers(1, min(E, 16) + 1))
+    T = int(rng.integers(1000, 4200))
+    H, I = 128 * int(rng.integers(1, 5)), 128 * int(rng.integers(1, 5))
+    dtype = "bf16" if i % 5 else "f32"
+    S = workloads.small_shape(T=T, H=H, E=E, I=I, k=k, dtype=dtype, cfg_id=600 + i,
+                              zipf_s=float(rng.choice([0.0, 1.1])), norm_topk=int(rng.integers(0, 2)))
+    path = int(rng.choice([0, 0, 1, 2]))
+    fusion = str(rng.choice(["max", "max", "min", "mean"]))
+    rate = float(rng.choice([0.0, 0.5, 0.6]))
+    packed = dtype == "bf16" and bool(rng.integers(0, 2))
+    print(f"[large random case {i}] {S} path={path} fusion={fusion} rate={rate} packed={packed}", flush=True)
+    L = workloads.make_layer(S)
+    tg, tr = oracle_thresholds(L, min(rate, (k - 1) / k))
+    g = GpuLayer(L, dev, fusion=fusion, packed=packed).run(tg, tr, path)
+    check_routing_shared_logits(L, g, tg, tr, fusion=fusion)
+    check_dispatch(S, g)
+    toks = sorted(set([0, 1, T // 2, T - 2, T - 1] + rng.integers(0, T, 12).tolist()))
+    ref = oracle_y(L, g, tg, tr, tokens=toks, fusion=fusion)
+    assert rel_l2(values(g["y"][toks]), ref["y"][toks]) <= TOL[dtype]
+
+
 # ---------------------------------------------------------------- full Qwen3-30B-A3B-shaped layer
 @pytest.fixture(scope="module")
 def qwen():
