@@ -89,12 +89,7 @@ __device__ __forceinline__ SlotVals load_slot(const DispatchArgs& a, int64_t s, 
 // thread of the workgroup must call it.
 __device__ __forceinline__ int block_excl_scan(int v, int32_t* s_wsum, int* total) {
   const int w = wave_id(), l = lane_id();
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(inc, o, 64);
-    if (l >= o) inc += u;
-  }
+  const int inc = wave_incl_scan(v);
   if (l == 63) s_wsum[w] = inc;
   __syncthreads();
   int base = 0, all = 0;

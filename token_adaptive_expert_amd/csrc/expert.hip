@@ -84,12 +84,7 @@ __device__ __forceinline__ void build_tile_list(const ExpertArgs& a, int32_t* s_
     cnt[j] = c;
     loc += c;
   }
-  int inc = loc;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(inc, o, 64);
-    if (l >= o) inc += v;
-  }
+  const int inc = wave_incl_scan(loc);
   int run = inc - loc;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -150,12 +145,7 @@ __device__ __forceinline__ void build_xcd_tile_list(const ExpertArgs& a, int x, 
     cnt[j] = c;
     loc += c;
   }
-  int inc = loc;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(inc, o, 64);
-    if (l >= o) inc += v;
-  }
+  const int inc = wave_incl_scan(loc);
   int run = inc - loc;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -377,26 +367,28 @@ void expert_gemm_kernel(ExpertArgs a) {
 }
 
 // Small-batch ("stream") path: split-K inside the workgroup.  A tile is one
-// expert, up to 16 of its slot rows and 32 weight rows (gate/up: 16 gate and
-// the 16 up rows of the same intermediate units; down: 32 output columns).
-// Its SK_NW waves take interleaved k-steps (wave w: w, w+SK_NW, ...) and
-// issue all weight and slot-row loads of up to SK_NBK k-steps at once, so
-// that with few rows per expert the weight stream is limited by bandwidth,
-// not by one wave's loads in flight.  The waves' partial sums meet in LDS
-// and are added in wave order (deterministic), then SiLU(gate)*up or the
-// gate scale is applied.  Slot rows are read straight from global memory
-// (they are few and stay in L2).
+// expert, up to 16 of its slot rows and NGRP groups of 16 weight rows
+// (gate/up: the 16 gate and the 16 up rows of the same intermediate units;
+// down: 16*NGRP output columns).  Its SK_NW waves take interleaved k-steps
+// (wave w: w, w+SK_NW, ...) and issue all weight and slot-row loads of up to
+// SK_NBK k-steps at once, so that with few rows per expert the weight stream
+// is limited by bandwidth, not by one wave's loads in flight.  The waves'
+// partial sums meet in LDS and are added in wave order (deterministic, and
+// the same bits for any NGRP), then SiLU(gate)*up or the gate scale is
+// applied.  Slot rows are read straight from global memory (they are few and
+// stay in L2).
 constexpr int SK_NW = 8;
 
-template <typename T, int KIND, int SK_NBK>
+template <typename T, int KIND, int SK_NBK, int NGRP>
 __global__ __launch_bounds__(SK_NW * 64) void expert_splitk_kernel(ExpertArgs a) {
+  static_assert(KIND == 1 || NGRP == 2, "gate/up tiles hold one gate and one up group");
   constexpr int EPL = St<T>::EPL;
   constexpr int KS = 4 * EPL;
   constexpr int BM = 16;
-  constexpr int COLS = (KIND == 0) ? 16 : 32;  // output columns per tile
+  constexpr int COLS = (KIND == 0) ? 16 : 16 * NGRP;  // output columns per tile
   __shared__ int32_t s_pref[257];
   __shared__ int32_t s_off[257];
-  __shared__ float s_red[SK_NW][2][16][17];
+  __shared__ float s_red[SK_NW][NGRP][16][17];
 
   const int w = wave_id(), l = lane_id(), tid = threadIdx.x;
   const int q = l >> 4, r16 = l & 15;
@@ -415,34 +407,36 @@ __global__ __launch_bounds__(SK_NW * 64) void expert_splitk_kernel(ExpertArgs a)
     int e, nb, row0, rows;
     find_tile(g, nb_count, BM, E, s_pref, s_off, e, nb, row0, rows);
     const int col0 = nb * COLS;
-    const int n0[2] = {col0, (KIND == 0) ? col0 : col0 + 16};
     const int64_t ebytes = int64_t(N) * K * int(sizeof(T));
     const char* wm0 = reinterpret_cast<const char*>(a.W0) + int64_t(e) * ebytes;
     const char* wm1 = reinterpret_cast<const char*>((KIND == 0) ? a.W1 : a.W0) + int64_t(e) * ebytes;
     const __amdgpu_buffer_rsrc_t wr0 = make_rsrc(wm0, uint32_t(ebytes));
     const __amdgpu_buffer_rsrc_t wr1 = make_rsrc(wm1, uint32_t(ebytes));
-    int wv, ws[2], wstep;
+    // group gg: weight rows n0 = col0 (gate/up: both groups) or col0 + 16*gg (down)
+    int wv, ws[NGRP], wstep;
     if (a.packed) {
       wv = l * 16;
 #pragma unroll
-      for (int gg = 0; gg < 2; ++gg) ws[gg] = (n0[gg] / 16) * nk * 1024;
+      for (int gg = 0; gg < NGRP; ++gg) ws[gg] = ((KIND == 0 ? col0 : col0 + 16 * gg) / 16) * nk * 1024;
       wstep = 1024;
     } else {
       wv = (r16 * K + q * EPL) * int(sizeof(T));
 #pragma unroll
-      for (int gg = 0; gg < 2; ++gg) ws[gg] = n0[gg] * K * int(sizeof(T));
+      for (int gg = 0; gg < NGRP; ++gg) ws[gg] = (KIND == 0 ? col0 : col0 + 16 * gg) * K * int(sizeof(T));
       wstep = KS * int(sizeof(T));
     }
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[NGRP];
+#pragma unroll
+    for (int gg = 0; gg < NGRP; ++gg) acc[gg] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (nkw > 0) {
       // weight loads of the first batch go out before the slot row is known
-      u32x4 wa[SK_NBK], wb[SK_NBK], xa[SK_NBK];
+      u32x4 wq[SK_NBK][NGRP], xa[SK_NBK];
       auto load_w = [&](int i0) {
 #pragma unroll
         for (int b = 0; b < SK_NBK; ++b) {
           const int j = w + SK_NW * min(i0 + b, nkw - 1);
-          wa[b] = buf_ld16(wr0, wv, ws[0] + j * wstep);
-          wb[b] = buf_ld16(wr1, wv, ws[1] + j * wstep);
+#pragma unroll
+          for (int gg = 0; gg < NGRP; ++gg) wq[b][gg] = buf_ld16((KIND == 0 && gg == 1) ? wr1 : wr0, wv, ws[gg] + j * wstep);
         }
       };
       load_w(0);
@@ -463,36 +457,36 @@ __global__ __launch_bounds__(SK_NW * 64) void expert_splitk_kernel(ExpertArgs a)
 #pragma unroll
         for (int b = 0; b < SK_NBK; ++b) {
           if (i0 + b < nkw) {
-            acc0 = mma_step<T>(xa[b], wa[b], acc0);
-            acc1 = mma_step<T>(xa[b], wb[b], acc1);
+#pragma unroll
+            for (int gg = 0; gg < NGRP; ++gg) acc[gg] = mma_step<T>(xa[b], wq[b][gg], acc[gg]);
           }
         }
       }
     }
     // lane (q, r16) holds rows 4q..4q+3 of weight column r16 in each group
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      s_red[w][0][4 * q + j][r16] = acc0[j];
-      s_red[w][1][4 * q + j][r16] = acc1[j];
-    }
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int gg = 0; gg < NGRP; ++gg) s_red[w][gg][4 * q + j][r16] = acc[gg][j];
     __syncthreads();
     if (tid < 256) {
       const int row = tid >> 4, c = tid & 15;
       if (row < rows) {
-        float v0 = s_red[0][0][row][c], v1 = s_red[0][1][row][c];
+        float v[NGRP];
 #pragma unroll
-        for (int ww = 1; ww < SK_NW; ++ww) {
-          v0 += s_red[ww][0][row][c];
-          v1 += s_red[ww][1][row][c];
+        for (int gg = 0; gg < NGRP; ++gg) {
+          v[gg] = s_red[0][gg][row][c];
+#pragma unroll
+          for (int ww = 1; ww < SK_NW; ++ww) v[gg] += s_red[ww][gg][row][c];
         }
         const int64_t p = row0 + row;
         if (KIND == 0) {
-          reinterpret_cast<T*>(a.out)[p * N + col0 + c] = St<T>::from_f32(silu(v0) * v1);
+          reinterpret_cast<T*>(a.out)[p * N + col0 + c] = St<T>::from_f32(silu(v[0]) * v[1]);
         } else {
           const float gt = a.sorted_gate[p];
           float* o = reinterpret_cast<float*>(a.out) + p * N + col0 + c;
-          o[0] = gt * v0;
-          o[16] = gt * v1;
+#pragma unroll
+          for (int gg = 0; gg < NGRP; ++gg) o[16 * gg] = gt * v[gg];
         }
       }
     }
@@ -505,22 +499,32 @@ __global__ __launch_bounds__(SK_NW * 64) void expert_splitk_kernel(ExpertArgs a)
 // the tiles (workgroups past the last tile exit after the tile-list prologue,
 // so an uncapped worst-case grid would mostly pay that prologue).  k-steps
 // per load batch: 8 for gate/up (K = H), 4 for down (K = I; fewer registers,
-// more resident workgroups).
+// more resident workgroups).  Down tiles are 32 output columns, or 64 from
+// ACE_SK_DOWN_WIDE_SLOTS routed slots on, where the tiles outnumber the
+// resident workgroups and twice the bytes in flight per workgroup pay.
 #ifndef ACE_SK_WG_PER_CU
 #define ACE_SK_WG_PER_CU 2      // grid cap per CU of the split-K kernel (measured best for decode)
+#endif
+#ifndef ACE_SK_DOWN_WIDE_SLOTS
+#define ACE_SK_DOWN_WIDE_SLOTS 32
 #endif
 constexpr int SK_WG_PER_CU = ACE_SK_WG_PER_CU;
 
 template <typename T, int KIND>
 hipError_t launch_splitk(const ExpertArgs& a, int ntok, int k, int num_cu, hipStream_t s) {
-  constexpr int COLS = (KIND == 0) ? 16 : 32;
   const int64_t slots = int64_t(ntok) * k;
+  const bool wide = KIND == 1 && slots >= ACE_SK_DOWN_WIDE_SLOTS && a.N % 64 == 0;
+  const int COLS = (KIND == 0) ? 16 : (wide ? 64 : 32);
   const int64_t mt_bound = (slots + 15) / 16 + std::min<int64_t>(a.E, slots);
   const int64_t tiles_bound = mt_bound * (a.N / COLS);
   const int64_t cap = int64_t(std::max(num_cu, 1)) * SK_WG_PER_CU;
   const int64_t grid = std::max<int64_t>(NXCD, (std::min(tiles_bound, cap) + NXCD - 1) / NXCD * NXCD);
-  hipLaunchKernelGGL((expert_splitk_kernel<T, KIND, KIND == 0 ? 8 : 4>), dim3(unsigned(grid)), dim3(SK_NW * 64), 0,
-                     s, a);
+  if (KIND == 0)
+    hipLaunchKernelGGL((expert_splitk_kernel<T, 0, 8, 2>), dim3(unsigned(grid)), dim3(SK_NW * 64), 0, s, a);
+  else if (wide)
+    hipLaunchKernelGGL((expert_splitk_kernel<T, 1, 4, 4>), dim3(unsigned(grid)), dim3(SK_NW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((expert_splitk_kernel<T, 1, 4, 2>), dim3(unsigned(grid)), dim3(SK_NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -553,7 +557,6 @@ __global__ __launch_bounds__(SK_NW * 64) void expert_splitk_fused_kernel(FusedAr
   __shared__ int32_t s_pref[EMAX_EXP + 1];
   __shared__ int32_t s_off[EMAX_EXP + 1];
   __shared__ int32_t s_tok[MAXS];
-  __shared__ int32_t s_wsum[SK_NW];
   __shared__ float s_red[SK_NW][2][16][17];
   const ExpertArgs& a = f.g;
   const int w = wave_id(), l = lane_id(), tid = threadIdx.x;
@@ -569,10 +572,12 @@ __global__ __launch_bounds__(SK_NW * 64) void expert_splitk_fused_kernel(FusedAr
     s_tr[e] = f.a_rcr[ec];
     s_mask[e] = 0u;
   }
+  // lane l holds the logits of experts l*R .. l*R + R-1 (topk_slots' layout)
+  const int R = topk_per_lane(E);
   float v[4];
   auto load_logits = [&](int t) {
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) v[rr] = f.logits[int64_t(min(t, Tn - 1)) * E + min(l + 64 * rr, E - 1)];
+    for (int rr = 0; rr < 4; ++rr) v[rr] = rr < R ? f.logits[int64_t(min(t, Tn - 1)) * E + min(l * R + rr, E - 1)] : 0.f;
   };
   load_logits(w);
   __syncthreads();
@@ -600,40 +605,32 @@ __global__ __launch_bounds__(SK_NW * 64) void expert_splitk_fused_kernel(FusedAr
     }
   }
   __syncthreads();
-  // 3. expert offsets and m-tile prefix (thread e owns expert e; waves 0..3)
-  {
-    const int e = tid;
-    const int cnt = e < E ? __popc(s_mask[e]) : 0;
-    const int mt = (cnt + BM - 1) / BM;
-    // two exclusive scans in one pass (rows, m-tiles) over the first 4 waves
-    int inc_c = cnt, inc_m = mt;
+  // 3. expert offsets and m-tile prefix: wave 0, lane l owns experts
+  //    4l..4l+3; rows and m-tiles travel packed (rows << 16 | m-tiles, both
+  //    at most FUSED_TMAX * 16 here) through one wave scan
+  if (w == 0) {
+    uint32_t pk[4], tot = 0;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int vc = __shfl_up(inc_c, o, 64), vm = __shfl_up(inc_m, o, 64);
-      if (l >= o) {
-        inc_c += vc;
-        inc_m += vm;
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * l + j;
+      const int cnt = e < E ? __popc(s_mask[e]) : 0;
+      pk[j] = (uint32_t(cnt) << 16) | uint32_t((cnt + BM - 1) / BM);
+      tot += pk[j];
+    }
+    const uint32_t inc = uint32_t(wave_incl_scan(int(tot)));
+    uint32_t run = inc - tot;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * l + j;
+      if (e < E) {
+        s_off[e] = int(run >> 16);
+        s_pref[e] = int(run & 0xFFFFu);
       }
+      run += pk[j];
     }
-    if (l == 63) s_wsum[w] = (inc_c << 16) | inc_m;  // both < 2^15 here
-    __syncthreads();
-    int base_c = 0, base_m = 0, all_c = 0, all_m = 0;
-    for (int ww = 0; ww < SK_NW; ++ww) {
-      const int sv = s_wsum[ww];
-      if (ww < w) {
-        base_c += sv >> 16;
-        base_m += sv & 0xFFFF;
-      }
-      all_c += sv >> 16;
-      all_m += sv & 0xFFFF;
-    }
-    if (e < E) {
-      s_off[e] = base_c + inc_c - cnt;
-      s_pref[e] = base_m + inc_m - mt;
-    }
-    if (tid == 0) {
-      s_off[E] = all_c;
-      s_pref[E] = all_m;
+    if (l == 63) {
+      s_off[E] = int(inc >> 16);
+      s_pref[E] = int(inc & 0xFFFFu);
     }
   }
   __syncthreads();

@@ -470,12 +470,12 @@ __global__ __launch_bounds__(NTHR) void topk_skip_kernel(RouteArgs a) {
   const bool valid = t_raw < a.T;
   const int t = min(t_raw, a.T - 1);
   const int E = a.E, k = a.k;
-  const int R = (E + 63) / 64;
+  const int R = topk_per_lane(E);
   const float* lrow = (a.logits_in ? a.logits_in : a.logits_out) + int64_t(t) * E;
-  // lane l holds experts l, l+64, ... (indices clamped: every load in bounds)
+  // lane l holds experts l*R .. l*R + R-1 (indices clamped: every load in bounds)
   float v[4];
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) v[rr] = lrow[min(l + 64 * rr, E - 1)];
+  for (int rr = 0; rr < 4; ++rr) v[rr] = rr < R ? lrow[min(l * R + rr, E - 1)] : 0.f;
   {
     // tables, shared by the workgroup's tokens (entries >= E are never read)
     const int e = min(int(threadIdx.x), E - 1);
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(NTHR) void topk_skip_kernel(RouteArgs a) {
     float* orow = a.logits_out + int64_t(t) * E;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
-      if (rr < R && l + 64 * rr < E) orow[l + 64 * rr] = v[rr];
+      if (rr < R && l * R + rr < E) orow[l * R + rr] = v[rr];
   }
   __syncthreads();
   const TopkParams p{E, k, a.norm_topk, a.fusion, a.tau_gsp, a.tau_rcr};

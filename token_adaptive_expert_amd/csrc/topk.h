@@ -14,30 +14,41 @@
 
 namespace ace {
 
-// Wave-wide max / min through DPP row shifts (within rows of 16 lanes) and a
-// combine of the four row results read from lanes 15, 31, 47 and 63; every
-// lane gets the result.  No LDS round trips on the dependency chain.
-template <int CTRL> __device__ __forceinline__ int dpp_shr(int v, int ident) {
-  return __builtin_amdgcn_update_dpp(ident, v, CTRL, 0xF, 0xF, false);
+// Order-preserving map of a float32 logit to a uint32 key: a larger logit
+// gives a larger key, -0 is folded onto +0 (they compare equal), NaN maps
+// to 1 (below every number) and 0 is left free to mark a taken entry.
+__device__ __forceinline__ uint32_t logit_key(float v) {
+  if (v != v) return 1u;
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ float wave_max_f(float v) {
-  const int ni = __float_as_int(-INFINITY);
-  v = fmaxf(v, __int_as_float(dpp_shr<0x111>(__float_as_int(v), ni)));
-  v = fmaxf(v, __int_as_float(dpp_shr<0x112>(__float_as_int(v), ni)));
-  v = fmaxf(v, __int_as_float(dpp_shr<0x114>(__float_as_int(v), ni)));
-  v = fmaxf(v, __int_as_float(dpp_shr<0x118>(__float_as_int(v), ni)));
-  const int b = __float_as_int(v);
-  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 15)), __int_as_float(__builtin_amdgcn_readlane(b, 31))),
-               fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 47)), __int_as_float(__builtin_amdgcn_readlane(b, 63))));
+__device__ __forceinline__ float key_logit(uint32_t kk) {
+  return __uint_as_float((kk & 0x80000000u) ? (kk & 0x7FFFFFFFu) : ~kk);
 }
-__device__ __forceinline__ int wave_min_i(int v) {
-  constexpr int big = 0x7FFFFFFF;
-  v = min(v, dpp_shr<0x111>(v, big));
-  v = min(v, dpp_shr<0x112>(v, big));
-  v = min(v, dpp_shr<0x114>(v, big));
-  v = min(v, dpp_shr<0x118>(v, big));
-  return min(min(__builtin_amdgcn_readlane(v, 15), __builtin_amdgcn_readlane(v, 31)),
-             min(__builtin_amdgcn_readlane(v, 47), __builtin_amdgcn_readlane(v, 63)));
+
+// Wave-wide maximum: DPP row shifts within rows of 16 lanes (lane 15 of a
+// row then holds the row maximum), two row broadcasts that carry it into
+// lane 63, and one read of lane 63 (a uniform value).
+template <int CTRL, int ROWS> __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+  v = max(v, dpp_u<0x111, 0xF>(v));  // row_shr:1
+  v = max(v, dpp_u<0x112, 0xF>(v));  // row_shr:2
+  v = max(v, dpp_u<0x114, 0xF>(v));  // row_shr:4
+  v = max(v, dpp_u<0x118, 0xF>(v));  // row_shr:8
+  v = max(v, dpp_u<0x142, 0xA>(v));  // row_bcast:15 into rows 1 and 3
+  v = max(v, dpp_u<0x143, 0xC>(v));  // row_bcast:31 into rows 2 and 3
+  return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
+}
+
+// Lane `lane`'s double (a uniform value).
+__device__ __forceinline__ double readlane_d(double x, int lane) {
+  const uint64_t u = uint64_t(__double_as_longlong(x));
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u)), lane));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u >> 32)), lane));
+  return __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
 }
 
 // Make this wave's LDS writes visible to its own later LDS reads.
@@ -52,63 +63,83 @@ struct TopkParams {
   float tau_gsp, tau_rcr;
 };
 
-// One token, one wave.  v[rr]: this lane's logit of expert l + 64*rr (entries
-// for experts >= E are ignored).  k rounds of arg-max: the wave-wide largest
-// remaining logit, then the lowest expert index among the lanes holding it
-// (order: value descending, index ascending).  Gates: softmax in float64
-// shifted by the top-1 logit, over the k selected (norm_topk) or all E,
-// sums in ascending order, rounded once to float32.  Lane i < k gets slot i:
-// its expert, gate and keep flag.  tg / tr: the two tables (any address
-// space); zrow: EMAX doubles of LDS owned by this wave.
+// Experts per lane for E experts (at most 4): lane l holds the logits of
+// experts l*R .. l*R + R-1, so that a lower lane always means a lower index.
+__device__ __forceinline__ int topk_per_lane(int E) { return (E + 63) / 64; }
+
+// k rounds of selection over order-preserving keys, NR registers per lane
+// (R <= NR of them used): each lane's candidate is its largest remaining key
+// (the lower slot on ties), the wave-wide largest candidate wins, and the
+// lowest lane holding it has the lowest expert index (order: value
+// descending, index ascending).  Lane i < k receives round i's expert and
+// key; top_key is round 0's.
+template <int NR>
+__device__ __forceinline__ void topk_rounds(const float (&v)[4], int E, int R, int k, int& my_e, uint32_t& my_key,
+                                            uint32_t& top_key) {
+  const int l = lane_id();
+  uint32_t key[NR];
+#pragma unroll
+  for (int rr = 0; rr < NR; ++rr) key[rr] = (rr < R && l * R + rr < E) ? logit_key(v[rr]) : 0u;
+  my_e = 0;
+  my_key = 0u;
+  top_key = 0u;
+  for (int i = 0; i < k; ++i) {
+    uint32_t cv = key[0];
+    int cr = 0;
+#pragma unroll
+    for (int rr = 1; rr < NR; ++rr)
+      if (key[rr] > cv) {
+        cv = key[rr];
+        cr = rr;
+      }
+    const uint32_t m = wave_max_u(cv);
+    const int lsel = __builtin_ctzll(__builtin_amdgcn_ballot_w64(cv == m));  // k <= E: m is a real key
+    const int esel = lsel * R + __builtin_amdgcn_readlane(cr, lsel);
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr)
+      if (l == lsel && cr == rr) key[rr] = 0u;
+    if (l == i) {
+      my_e = esel;
+      my_key = m;
+    }
+    if (i == 0) top_key = m;
+  }
+}
+
+// One token, one wave.  v[rr]: this lane's logit of expert l*R + rr with
+// R = topk_per_lane(E) (entries for experts >= E are ignored).  Selection as
+// in topk_rounds.  Gates: softmax in float64 shifted by the top-1 logit, over
+// the k selected (norm_topk) or all E, sums in ascending order, rounded once
+// to float32.  Lane i < k gets slot i: its expert, gate and keep flag.
+// tg / tr: the two tables (any address space); zrow: EMAX doubles of LDS
+// owned by this wave (used when the softmax runs over all E).
 __device__ __forceinline__ void topk_slots(const float (&v)[4], const TopkParams& p, const float* tg,
                                            const float* tr, double* zrow, int& my_e, float& gate, bool& keep) {
   const int l = lane_id();
   const int E = p.E, k = p.k;
-  const int R = (E + 63) / 64;
-  uint32_t avail = 0;  // bit rr: value rr of this lane is a real, not yet taken expert
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr)
-    if (rr < R && l + 64 * rr < E) avail |= 1u << rr;
-  my_e = 0;
-  float my_logit = 0.f, top_logit = 0.f;
-  for (int i = 0; i < k; ++i) {
-    // this lane's candidate: largest available value, lowest index on ties
-    float cv = -INFINITY;
-    int ce = 0x7FFFFFFF;
-    int crr = -1;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      if (((avail >> rr) & 1u) && (crr < 0 || v[rr] > cv)) {
-        cv = v[rr];
-        ce = l + 64 * rr;
-        crr = rr;
-      }
-    }
-    const float m = wave_max_f(cv);
-    const int be = wave_min_i(crr >= 0 && cv == m ? ce : 0x7FFFFFFF);
-    if (ce == be) avail &= ~(1u << crr);
-    if (l == i) {
-      my_e = be;
-      my_logit = m;
-    }
-    if (i == 0) top_logit = m;
-  }
-  const double mx = double(top_logit);
-  const double z = (l < k) ? exp(double(my_logit) - mx) : 0.0;
+  const int R = topk_per_lane(E);
+  uint32_t my_key, top_key;
+  if (R == 1)
+    topk_rounds<1>(v, E, R, k, my_e, my_key, top_key);
+  else if (R == 2)
+    topk_rounds<2>(v, E, R, k, my_e, my_key, top_key);
+  else
+    topk_rounds<4>(v, E, R, k, my_e, my_key, top_key);
+  const double mx = double(key_logit(top_key));
+  const double z = (l < k) ? exp(double(key_logit(my_key)) - mx) : 0.0;
+  double s = 0.0;
   if (p.norm_topk) {
-    if (l < k) zrow[l] = z;
+    for (int i = 0; i < k; ++i) s += readlane_d(z, i);
   } else {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const int e = l + 64 * rr;
+      const int e = l * R + rr;
       if (rr < R && e < E) zrow[e] = exp(double(v[rr]) - mx);
     }
+    wave_lds_sync();
+    for (int i = 0; i < E; ++i) s += zrow[i];
+    wave_lds_sync();  // zrow may be rewritten by this wave's next token
   }
-  wave_lds_sync();
-  double s = 0.0;
-  const int nsum = p.norm_topk ? k : E;
-  for (int i = 0; i < nsum; ++i) s += zrow[i];
-  wave_lds_sync();  // zrow may be rewritten by this wave's next token
   gate = float(z / s);
   keep = true;
   if (l > 0 && l < k) {
