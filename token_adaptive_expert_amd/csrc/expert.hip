@@ -380,7 +380,7 @@ void expert_gemm_kernel(ExpertArgs a) {
 constexpr int SK_NW = 8;
 
 template <typename T, int KIND, int SK_NBK, int NGRP>
-__global__ __launch_bounds__(SK_NW * 64) void expert_splitk_kernel(ExpertArgs a) {
+__global__ __launch_bounds__(SK_NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void expert_splitk_kernel(ExpertArgs a) {
   static_assert(KIND == 1 || NGRP == 2, "gate/up tiles hold one gate and one up group");
   constexpr int EPL = St<T>::EPL;
   constexpr int KS = 4 * EPL;
@@ -399,6 +399,7 @@ __global__ __launch_bounds__(SK_NW * 64) void expert_splitk_kernel(ExpertArgs a)
 
   build_tile_list<BM>(a, s_pref, s_off);
   __syncthreads();
+  // XCD x takes the x-th contiguous part of the expert-major tile list
   const int ntiles = s_pref[E] * nb_count;
   const int per_xcd = (ntiles + NXCD - 1) / NXCD;
   for (int wg = blockIdx.x; wg < NXCD * per_xcd; wg += gridDim.x) {
@@ -540,7 +541,8 @@ hipError_t launch_splitk(const ExpertArgs& a, int ntok, int k, int num_cu, hipSt
 // sorted_token, sorted_gate and slot_pos for the later kernels (down
 // projection, combine) and the caller.  Saves two dependent launches.
 template <typename T>
-__global__ __launch_bounds__(SK_NW * 64) void expert_splitk_fused_kernel(FusedArgs f) {
+// Two workgroups per CU (4 waves per SIMD) need at most 128 VGPRs.
+__global__ __launch_bounds__(SK_NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void expert_splitk_fused_kernel(FusedArgs f) {
   constexpr int EPL = St<T>::EPL;
   constexpr int KS = 4 * EPL;
   constexpr int BM = 16;
@@ -657,10 +659,9 @@ __global__ __launch_bounds__(SK_NW * 64) void expert_splitk_fused_kernel(FusedAr
   const int nk = K / KS;
   const int nkw = w < nk ? (nk - 1 - w) / SK_NW + 1 : 0;
   const int ntiles = s_pref[E] * nb_count;
-  const int per_xcd = (ntiles + NXCD - 1) / NXCD;
-  for (int wg = blockIdx.x; wg < NXCD * per_xcd; wg += gridDim.x) {
-    const int gi = (wg % NXCD) * per_xcd + wg / NXCD;
-    if (gi >= ntiles) continue;
+  // tile gi runs on XCD gi % 8 (the grid is a multiple of 8): dealt over the
+  // XCDs, measured faster here than contiguous parts
+  for (int gi = blockIdx.x; gi < ntiles; gi += gridDim.x) {
     int e, nb, row0, rows;
     find_tile(gi, nb_count, BM, E, s_pref, s_off, e, nb, row0, rows);
     const int col0 = nb * COLS;
