@@ -18,6 +18,8 @@ constexpr int RNTHR = RW * 64;
 constexpr int NTHR = 256;     // 4 waves (top-k kernel)
 constexpr int EMAX = 256;
 constexpr int NARROW_HMAX = 8192;  // hidden size limit of the small-batch router variant
+constexpr int XL_HMAX = 2048;      // hidden size limit of the router's x rows in LDS
+constexpr int XL_PITCH = XL_HMAX + 8;  // bf16 elements per LDS row
 #ifndef ACE_ROUTER_WIDE_T
 #define ACE_ROUTER_WIDE_T 2048     // batch from which the 32/64-token router variant is used
 #endif
@@ -143,14 +145,20 @@ template <> __device__ __forceinline__ float sumsq16<float>(u32x4 v) {
 // MFMA columns are discarded: an output column depends only on its own
 // weights), so that the plane bytes of a decode batch spread over SUB times
 // more compute units.
-template <typename T, int NCB, int SUB = 1>
+template <typename T, int NCB, int SUB = 1, bool XL = false>
 __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
   static_assert(SUB == 1 || NCB == 1, "sub-blocks of one column block only");
+  static_assert(!XL || sizeof(T) == 2, "x rows in LDS: bf16 only");
   constexpr int ECBW = 16 * NCB;          // experts per workgroup
   constexpr int NBK = NCB == 1 ? 4 : 2;   // k-steps per wave per load batch (pre-split planes)
   __shared__ float s_inv[TB];
   __shared__ float s_part[RW][TB][ECBW + 1];
   __shared__ __attribute__((aligned(16))) float s_gam[NCB == 1 ? NARROW_HMAX : 4];
+  // XL (H <= XL_HMAX): the RMS prologue keeps the 16 x rows in LDS and the
+  // MFMA operands are read from there instead of a second pass over global
+  // memory (each vector-memory instruction costs the CU the same time however
+  // few of its lanes are active); rows padded by 16 bytes (no bank conflicts)
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[XL ? TB * XL_PITCH : 8];
 
   constexpr int EPL = St<T>::EPL;
   constexpr int KS = 4 * EPL;
@@ -163,8 +171,14 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
   const int t = min(tt, a.T - 1);
   const T* xrow = x + int64_t(t) * H;
   T* hrow = reinterpret_cast<T*>(a.h_out) + int64_t(t) * H;
-  const bool write_h = blockIdx.y == 0 && tt < a.T;
+  // h_out: every column-block workgroup of a token block computes the same h
+  // fragments; k-step j is written by workgroup j % gridDim.y, so the stores
+  // (whose completion later load waits include) are spread evenly
   const bool do_router = a.logits_in == nullptr;
+  const bool row_ok = tt < a.T;
+  auto write_h = [&](int j) -> bool {
+    return row_ok && (do_router ? j % int(gridDim.y) == int(blockIdx.y) : blockIdx.y == 0);
+  };
   const int nks = H / KS;
   f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 
@@ -186,7 +200,8 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
 #pragma unroll
     for (int b = 0; b < NBK; ++b) {
       const int j = w + RW * min(i0 + b, nki - 1);
-      px[b] = ld16(xrow + j * KS + q * EPL);
+      px[b] = u32x4{0u, 0u, 0u, 0u};
+      if (!XL && tt < a.T) px[b] = ld16(xrow + j * KS + q * EPL);  // rows past the batch: no loads
 #pragma unroll
       for (int c = 0; c < NCB; ++c)
 #pragma unroll
@@ -211,6 +226,7 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
   // router planes stay in flight across the barrier.
   {
     const T* row = x + int64_t(min(tok0 + w, a.T - 1)) * H;
+    const bool row_valid = tok0 + w < a.T;  // waves past the batch load no row
     constexpr int SEG = 64 * EPL;
     // segments per batch (4 with EARLY, for registers); the per-lane sum runs
     // over the segments in order either way, so the result is the same
@@ -219,7 +235,10 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
     for (int j0 = 0; j0 < H; j0 += RSEG * SEG) {
       u32x4 v[RSEG];
 #pragma unroll
-      for (int b = 0; b < RSEG; ++b) v[b] = ld16(row + min(j0 + b * SEG + l * EPL, H - EPL));
+      for (int b = 0; b < RSEG; ++b) {
+        v[b] = u32x4{0u, 0u, 0u, 0u};
+        if (row_valid) v[b] = ld16(row + min(j0 + b * SEG + l * EPL, H - EPL));
+      }
       if constexpr (EARLY) {
         if (j0 == 0) {
           f32x4 gq[GQ];
@@ -238,7 +257,10 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
       }
 #pragma unroll
       for (int b = 0; b < RSEG; ++b)
-        if (j0 + b * SEG + l * EPL < H) ss += sumsq16<T>(v[b]);
+        if (j0 + b * SEG + l * EPL < H) {
+          ss += sumsq16<T>(v[b]);
+          if constexpr (XL) *reinterpret_cast<u32x4*>(&s_x[w * XL_PITCH + j0 + b * SEG + l * EPL]) = v[b];
+        }
     }
     ss = wave_sum_dpp(ss);
     if (l == 0) s_inv[w] = 1.0f / sqrtf(ss / float(H) + a.eps);
@@ -253,13 +275,16 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
 #pragma unroll
         for (int b = 0; b < NBK; ++b) {
           if (i0 + b < nki) {
-            const int k0 = (w + RW * (i0 + b)) * KS + q * EPL;
+            const int jb = w + RW * (i0 + b);
+            const int k0 = jb * KS + q * EPL;
             const float* gp = EARLY ? s_gam + k0 : a.gamma + k0;
             f32x4 g[2];
             g[0] = *reinterpret_cast<const f32x4*>(gp);
             g[1] = *reinterpret_cast<const f32x4*>(gp + 4);
-            const u32x4 h = make_h<T>(px[b], inv, g);
-            if (write_h) st16(hrow + k0, h);
+            u32x4 xv = px[b];
+            if constexpr (XL) xv = *reinterpret_cast<const u32x4*>(&s_x[r16 * XL_PITCH + k0]);
+            const u32x4 h = make_h<T>(xv, inv, g);
+            if (write_h(jb)) st16(hrow + k0, h);
 #pragma unroll
             for (int c = 0; c < NCB; ++c) acc[c] = mma3(h, pl[b][c], acc[c]);
           }
@@ -285,14 +310,14 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
           f1.load_x(xrow, a.gamma, k1);
         }
         const u32x4 h0 = make_h<T>(f0.x, inv, f0.g);
-        if (write_h) st16(hrow + k0, h0);
+        if (write_h(j0)) st16(hrow + k0, h0);
         if (do_router) {
           acc[0] = router_mma<T>(h0, f0.w0, acc[0]);
           acc[1] = router_mma<T>(h0, f0.w1, acc[1]);
         }
         if (j1 < nks) {
           const u32x4 h1 = make_h<T>(f1.x, inv, f1.g);
-          if (write_h) st16(hrow + k1, h1);
+          if (write_h(j1)) st16(hrow + k1, h1);
           if (do_router) {
             acc[0] = router_mma<T>(h1, f1.w0, acc[0]);
             acc[1] = router_mma<T>(h1, f1.w1, acc[1]);
@@ -400,7 +425,7 @@ __global__ __launch_bounds__(RNTHR) void norm_router_wide_kernel(RouteArgs a, in
     const int t = min(tt, a.T - 1);
     xrow[m] = x + int64_t(t) * H;
     hrow[m] = hout + int64_t(t) * H;
-    wr[m] = cbk == 0 && tt < a.T;
+    wr[m] = tt < a.T;  // k-step j of h is written by column block j % ncb (stores spread evenly)
   }
 
   f32x4 acc[MT][2];
@@ -422,14 +447,16 @@ __global__ __launch_bounds__(RNTHR) void norm_router_wide_kernel(RouteArgs a, in
 #pragma unroll
     for (int b = 0; b < NBK; ++b) {
       if (i0 + b < nki) {
-        const int k0 = (w + RW * (i0 + b)) * KS + q * EPL;
+        const int jb = w + RW * (i0 + b);
+        const int k0 = jb * KS + q * EPL;
+        const bool wj = jb % ncb == cbk;
         f32x4 g[2];
         g[0] = *reinterpret_cast<const f32x4*>(a.gamma + k0);
         g[1] = *reinterpret_cast<const f32x4*>(a.gamma + k0 + 4);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           const u32x4 h = make_h<bf16_t>(px[b][m], inv[m], g);
-          if (wr[m]) st16(hrow[m] + k0, h);
+          if (wr[m] && wj) st16(hrow[m] + k0, h);
           acc[m][0] = mma3(h, pl[b][0], acc[m][0]);
           acc[m][1] = mma3(h, pl[b][1], acc[m][1]);
         }
@@ -558,15 +585,24 @@ hipError_t launch_route(int dtype, const RouteArgs& a, hipStream_t s, bool with_
     // sub-blocks: about ACE_ROUTER_NARROW_WG workgroups in all
     const unsigned cb = unsigned((a.E + 15) / 16);
     const unsigned sub = std::max(1u, std::min(4u, unsigned(ACE_ROUTER_NARROW_WG) / (gx * cb)));
-    if (sub >= 4)
+    const bool xl = a.H <= XL_HMAX;
+    if (sub >= 4 && xl)
+      hipLaunchKernelGGL((norm_router_kernel<bf16_t, 1, 4, true>), dim3(gx, cb * 4), block1, 0, s, a);
+    else if (sub >= 4)
       hipLaunchKernelGGL((norm_router_kernel<bf16_t, 1, 4>), dim3(gx, cb * 4), block1, 0, s, a);
+    else if (sub >= 2 && xl)
+      hipLaunchKernelGGL((norm_router_kernel<bf16_t, 1, 2, true>), dim3(gx, cb * 2), block1, 0, s, a);
     else if (sub >= 2)
       hipLaunchKernelGGL((norm_router_kernel<bf16_t, 1, 2>), dim3(gx, cb * 2), block1, 0, s, a);
+    else if (xl)
+      hipLaunchKernelGGL((norm_router_kernel<bf16_t, 1, 1, true>), dim3(gx, cb), block1, 0, s, a);
     else
       hipLaunchKernelGGL((norm_router_kernel<bf16_t, 1, 1>), dim3(gx, cb), block1, 0, s, a);
   } else {
     const dim3 grid1(gx, a.logits_in ? 1 : unsigned((a.E + 31) / 32));
-    if (dtype == 1)
+    if (dtype == 1 && a.router_packed && a.logits_in == nullptr && a.H <= XL_HMAX)
+      hipLaunchKernelGGL((norm_router_kernel<bf16_t, 2, 1, true>), grid1, block1, 0, s, a);
+    else if (dtype == 1)
       hipLaunchKernelGGL((norm_router_kernel<bf16_t, 2>), grid1, block1, 0, s, a);
     else
       hipLaunchKernelGGL((norm_router_kernel<float, 2>), grid1, block1, 0, s, a);
