@@ -213,17 +213,20 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
   };
   constexpr bool EARLY = NCB == 1;  // registers allow the early batch only with one column block
   constexpr int GQ = NARROW_HMAX / (RNTHR * 4);  // gamma quads per thread for the LDS copy
+  // EARLY: gamma is copied to LDS once (read there by every k-step of the MFMA loop)
+  const bool gam_lds = EARLY && packed;
   // router bias of this thread's output (read after the last barrier)
   float bias_v = 0.f;
   if (do_router && a.bias != nullptr && threadIdx.x < TB * ECBW)
     bias_v = a.bias[min(ycb * ECBW + int(threadIdx.x) % ECBW, E - 1)];
 
   // inverse RMS: wave w owns token tok0 + w; a row is read 8 segments of
-  // 64 lanes x 16 bytes at a time, all in flight together.  With EARLY, the
-  // gamma quads for the LDS copy (H <= NARROW_HMAX on this path) and the
-  // first batch of router loads go out behind the row's first segments:
-  // loads complete in order, so the sum waits for the row only and the
-  // router planes stay in flight across the barrier.
+  // 64 lanes x 16 bytes at a time, all in flight together (segments past H
+  // are not loaded).  With EARLY, the gamma quads for the LDS copy (H <=
+  // NARROW_HMAX on this path) and the first batch of router loads go out
+  // behind the row's first segments: loads complete in order, so the sum
+  // waits for the row only and the router planes stay in flight across the
+  // barrier.
   {
     const T* row = x + int64_t(min(tok0 + w, a.T - 1)) * H;
     const bool row_valid = tok0 + w < a.T;  // waves past the batch load no row
@@ -237,22 +240,22 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
 #pragma unroll
       for (int b = 0; b < RSEG; ++b) {
         v[b] = u32x4{0u, 0u, 0u, 0u};
-        if (row_valid) v[b] = ld16(row + min(j0 + b * SEG + l * EPL, H - EPL));
+        if (row_valid && j0 + b * SEG < H) v[b] = ld16(row + min(j0 + b * SEG + l * EPL, H - EPL));
       }
-      if constexpr (EARLY) {
-        if (j0 == 0) {
-          f32x4 gq[GQ];
+      if (j0 == 0 && gam_lds) {
+        f32x4 gq[GQ];
 #pragma unroll
-          for (int i = 0; i < GQ; ++i) {
-            const int h = (int(threadIdx.x) + i * RNTHR) * 4;
-            if (h < H) gq[i] = *reinterpret_cast<const f32x4*>(a.gamma + h);
-          }
-          if (packed && nki > 0) issue(0);
+        for (int i = 0; i < GQ; ++i) {
+          const int h = (int(threadIdx.x) + i * RNTHR) * 4;
+          if (h < H) gq[i] = *reinterpret_cast<const f32x4*>(a.gamma + h);
+        }
+        if constexpr (EARLY) {
+          if (nki > 0) issue(0);
+        }
 #pragma unroll
-          for (int i = 0; i < GQ; ++i) {
-            const int h = (int(threadIdx.x) + i * RNTHR) * 4;
-            if (h < H) *reinterpret_cast<f32x4*>(&s_gam[h]) = gq[i];  // read back after the barrier
-          }
+        for (int i = 0; i < GQ; ++i) {
+          const int h = (int(threadIdx.x) + i * RNTHR) * 4;
+          if (h < H) *reinterpret_cast<f32x4*>(&s_gam[h]) = gq[i];  // read back after the barrier
         }
       }
 #pragma unroll
@@ -277,7 +280,7 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
           if (i0 + b < nki) {
             const int jb = w + RW * (i0 + b);
             const int k0 = jb * KS + q * EPL;
-            const float* gp = EARLY ? s_gam + k0 : a.gamma + k0;
+            const float* gp = gam_lds ? s_gam + k0 : a.gamma + k0;
             f32x4 g[2];
             g[0] = *reinterpret_cast<const f32x4*>(gp);
             g[1] = *reinterpret_cast<const f32x4*>(gp + 4);
