@@ -419,6 +419,8 @@ def test_fused_forward_matches_steps_f32(tiny, dev, fusion, T):
 @pytest.mark.parametrize("T,k,E,keep_p,skew", [
     # recount mode (1024 < T*k <= 32768: one workgroup per 1024 slots)
     (513, 2, 7, 0.5, 0.0),       # 1026 slots: the second block holds two slots
+    (1001, 3, 50, 0.6, 0.0),     # 3003 slots: the batch ends inside a four-slot quad
+    (1367, 5, 96, 0.5, 1.1),     # 6835 slots, ragged last quad, Zipf-like prior
     (1100, 8, 200, 0.4, 1.1),    # 8800 slots, Zipf-like expert prior, many empty experts
     (3000, 6, 256, 0.9, 0.0),    # 18000 slots, E at its maximum
     (2049, 4, 64, 0.0, 0.0),     # only top-1 slots kept

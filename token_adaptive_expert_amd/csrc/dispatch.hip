@@ -57,7 +57,7 @@ constexpr int DSP_RECOUNT = 1;   // one workgroup per RBS slots; each counts the
 constexpr int DSP_BLOCK = 2;     // one workgroup per DBS slots; counts and row bases from the workspace
 constexpr int RBS = 64 * NW;     // slots per workgroup, recount mode (one 64-slot chunk per wave)
 constexpr int RECOUNT_MAX = 32768;  // largest batch (slots) of the recount mode
-constexpr int RC_BATCH = 8;      // chunk loads in flight per wave while recounting
+constexpr int RC_BATCH = 2;      // slot quads in flight per thread while recounting
 constexpr int DBS = 4096;        // slots per workgroup, block mode (64 chunks)
 
 __device__ __forceinline__ void wave_sync_lds() {
@@ -142,29 +142,49 @@ __global__ __launch_bounds__(NTHR) void dispatch_kernel(DispatchArgs a) {
   SlotVals own{};
   if constexpr (MODE == DSP_RECOUNT) own = load_slot(a, int64_t(min(c0, nchunks - 1)) * 64 + l, nslots, true);
   if constexpr (MODE == DSP_RECOUNT) {
-    // the chunks outside this block, dealt round-robin over the waves, RC_BATCH
-    // loads in flight: kept slots per expert, and those before the block
-    const int nown = cb1 - cb0, nout = nchunks - nown;
-    for (int i0 = w; i0 < nout; i0 += NW * RC_BATCH) {
-      int ev[RC_BATCH], kv[RC_BATCH];
+    // the slots outside this block: kept slots per expert, and those before
+    // the block.  Counting ignores slot order, so each thread takes four
+    // consecutive slots per load (16-byte and 4-byte loads: the ABI's
+    // buffers are 16-byte aligned and block boundaries are multiples of 64
+    // slots), RC_BATCH quads in flight; a quad that reaches past the end of
+    // the batch is read slot by slot.
+    auto count = [&](int64_t sb, int64_t se, bool before) {
+      for (int64_t q0 = sb + 4 * int64_t(tid); q0 < se; q0 += int64_t(4) * NTHR * RC_BATCH) {
+        int4 ev[RC_BATCH];
+        uint32_t kv[RC_BATCH];
 #pragma unroll
-      for (int b = 0; b < RC_BATCH; ++b) {
-        const int i = min(i0 + NW * b, nout - 1);
-        const int c = i < cb0 ? i : i + nown;
-        const int64_t sl = min(int64_t(c) * 64 + l, nslots - 1);
-        ev[b] = a.idx[sl];
-        kv[b] = a.keep[sl];
-      }
+        for (int b = 0; b < RC_BATCH; ++b) {
+          const int64_t q = q0 + int64_t(4) * NTHR * b;
+          ev[b] = int4{0, 0, 0, 0};
+          kv[b] = 0u;
+          if (q + 4 <= nslots) {
+            if (q < se) {
+              ev[b] = *reinterpret_cast<const int4*>(a.idx + q);
+              kv[b] = *reinterpret_cast<const uint32_t*>(a.keep + q);
+            }
+          } else if (q < se) {
+            ev[b].x = a.idx[q];
+            kv[b] = a.keep[q];
+            if (q + 1 < nslots) { ev[b].y = a.idx[q + 1]; kv[b] |= uint32_t(a.keep[q + 1]) << 8; }
+            if (q + 2 < nslots) { ev[b].z = a.idx[q + 2]; kv[b] |= uint32_t(a.keep[q + 2]) << 16; }
+          }
+        }
 #pragma unroll
-      for (int b = 0; b < RC_BATCH; ++b) {
-        const int i = i0 + NW * b;
-        const int c = i < cb0 ? i : i + nown;
-        if (i < nout && int64_t(c) * 64 + l < nslots && kv[b] && unsigned(ev[b]) < unsigned(E)) {
-          atomicAdd(&s_tot[ev[b]], 1);
-          if (c < cb0) atomicAdd(&s_pre[ev[b]], 1);
+        for (int b = 0; b < RC_BATCH; ++b) {
+          const int64_t q = q0 + int64_t(4) * NTHR * b;
+          const int e4[4] = {ev[b].x, ev[b].y, ev[b].z, ev[b].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (q + j < se && ((kv[b] >> (8 * j)) & 0xFFu) && unsigned(e4[j]) < unsigned(E)) {
+              atomicAdd(&s_tot[e4[j]], 1);
+              if (before) atomicAdd(&s_pre[e4[j]], 1);
+            }
+          }
         }
       }
-    }
+    };
+    count(0, int64_t(cb0) * 64, true);
+    count(int64_t(cb1) * 64, nslots, false);
   }
   if (c0 < c1) {
     SlotVals cur = MODE == DSP_RECOUNT ? own : load_slot(a, int64_t(c0) * 64 + l, nslots, false);
