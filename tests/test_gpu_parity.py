@@ -415,6 +415,68 @@ def test_fused_forward_matches_steps_f32(tiny, dev, fusion, T):
     _fused_vs_steps(gl.layer, x, float(tg), float(tr), None)
 
 
+def _adversarial_logits(T, E, rng):
+    """Rows that stress the selection order: exact ties (a few distinct
+    values, or all equal), signed zeros among negatives, -inf entries, huge
+    magnitudes and neighbours one float32 ulp apart."""
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    for t in range(T):
+        kind = t % 8
+        if kind == 0:
+            lg[t] = rng.choice(np.array([-1.0, 0.0, 1.0, 2.0], np.float32), E)
+        elif kind == 1:
+            lg[t] = np.float32(0.75)
+        elif kind == 2:
+            lg[t] = -np.abs(lg[t]) - 1.0
+            z = rng.choice(E, size=min(E, 6), replace=False)
+            lg[t, z] = np.where(np.arange(z.size) % 2 == 0, np.float32(0.0), np.float32(-0.0))
+        elif kind == 3:
+            lg[t, rng.choice(E, size=E // 2, replace=False)] = -np.inf
+        elif kind == 4:
+            lg[t] = (lg[t] * np.float32(1e30)).astype(np.float32)
+        elif kind == 5:
+            base = np.float32(1.5)
+            steps = rng.integers(0, 3, E)
+            lg[t] = np.array([np.nextafter(base, np.float32(2), dtype=np.float32) if s_ == 1 else
+                              (np.nextafter(base, np.float32(1), dtype=np.float32) if s_ == 2 else base)
+                              for s_ in steps], np.float32)
+        elif kind == 6:
+            n = E // 2
+            lg[t, 0:2 * n:2] = lg[t, 1:2 * n:2]  # pairwise ties, the lower index first
+    return lg
+
+
+@pytest.mark.parametrize("E,k", [(16, 4), (64, 8), (65, 8), (128, 8), (128, 16), (150, 6), (192, 16), (256, 8), (256, 1)])
+@pytest.mark.parametrize("norm_topk", [True, False])
+def test_topk_adversarial_logits(dev, E, k, norm_topk):
+    """Top-k indices, gates and the skip mask from crafted float32 logits
+    (through logits_in) equal the oracle's bit for bit, for every per-lane
+    layout of the selection (1 to 4 experts per lane)."""
+    T = 48
+    S = workloads.small_shape(T=T, H=128, E=E, I=128, k=k, dtype="f32", cfg_id=700 + E + k)
+    L = workloads.make_layer(S)
+    rng = np.random.default_rng(1000 * E + k)
+    lg = _adversarial_logits(T, E, rng)
+    tg = tr = 0.05
+    g = GpuLayer(L, dev, norm_topk=int(norm_topk)).run(tg, tr, logits_in=lg)
+    idx = np.stack([oracle.topk_experts(lg[t], k) for t in range(T)])
+    gate = np.stack([oracle.topk_gates(lg[t], idx[t], norm_topk) for t in range(T)])
+    keep = oracle.skip_mask(idx, gate, L["a_gsp"], L["a_rcr"], tg, tr)
+    assert np.array_equal(g["topk_idx"], idx)
+    assert np.array_equal(g["topk_gate"].view(np.uint32), gate.view(np.uint32))
+    assert np.array_equal(g["keep"], keep)
+
+
+@pytest.mark.parametrize("E,k,T", [(150, 6, 7), (256, 8, 8), (65, 3, 5)])
+def test_fused_forward_matches_steps_wide_expert_sets(dev, E, k, T):
+    """The fused decode path with 2 to 4 experts per lane in its top-k."""
+    S = workloads.small_shape(T=T, H=256, E=E, I=128, k=k, dtype="bf16", cfg_id=760 + E)
+    L = workloads.make_layer(S)
+    tg, tr = oracle_thresholds(L, 0.5)
+    gl = GpuLayer(L, dev, packed=True)
+    _fused_vs_steps(gl.layer, gl.P["x"], float(tg), float(tr), None)
+
+
 # ---------------------------------------------------------------- multi-workgroup dispatch
 @pytest.mark.parametrize("T,k,E,keep_p,skew", [
     # recount mode (1024 < T*k <= 32768: one workgroup per 1024 slots)
