@@ -407,7 +407,7 @@ def test_fused_forward_matches_steps(qwen, dev, M, packed):
 
 
 @pytest.mark.parametrize("fusion", ["max", "min", "mean", "score"])
-@pytest.mark.parametrize("T", [6, 30])
+@pytest.mark.parametrize("T", [1, 2, 6, 30])
 def test_fused_forward_matches_steps_f32(tiny, dev, fusion, T):
     L, tg, tr = tiny
     gl = GpuLayer(L, dev, fusion=fusion)
@@ -467,7 +467,7 @@ def test_topk_adversarial_logits(dev, E, k, norm_topk):
     assert np.array_equal(g["keep"], keep)
 
 
-@pytest.mark.parametrize("E,k,T", [(150, 6, 7), (256, 8, 8), (65, 3, 5)])
+@pytest.mark.parametrize("E,k,T", [(150, 6, 7), (256, 8, 8), (65, 3, 5), (65, 3, 2), (256, 8, 1)])
 def test_fused_forward_matches_steps_wide_expert_sets(dev, E, k, T):
     """The fused decode path with 2 to 4 experts per lane in its top-k."""
     S = workloads.small_shape(T=T, H=256, E=E, I=128, k=k, dtype="bf16", cfg_id=760 + E)

@@ -532,16 +532,16 @@ hipError_t launch_splitk(const ExpertArgs& a, int ntok, int k, int num_cu, hipSt
 // Fused small-batch gate/up (decode, T <= FUSED_TMAX): instead of reading
 // the outputs of a separate top-k kernel and a dispatch kernel, every
 // workgroup derives them from the router logits in LDS (a few hundred slots
-// at most): wave t runs topk_slots for token t (the same code and bits as
-// the routing kernel); kept (expert, token) pairs set bit t of a per-expert
+// at most): wave w runs topk_slots for tokens w, w + 8, ... (the same code
+// and bits as the routing kernel); kept (expert, token) pairs set bit t of a per-expert
 // token mask, so expert e's count is the mask's popcount and slot (t, i)'s
 // row is offset[e] + popcount(mask[e] below bit t) (token order, as in
 // moe_dispatch); then the split-K tiles run as in expert_splitk_kernel.
 // Workgroup 0 writes topk_idx, topk_gate, keep, expert_offsets,
 // sorted_token, sorted_gate and slot_pos for the later kernels (down
 // projection, combine) and the caller.  Saves two dependent launches.
-template <typename T>
 // Two workgroups per CU (4 waves per SIMD) need at most 128 VGPRs.
+template <typename T>
 __global__ __launch_bounds__(SK_NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void expert_splitk_fused_kernel(FusedArgs f) {
   constexpr int EPL = St<T>::EPL;
   constexpr int KS = 4 * EPL;
