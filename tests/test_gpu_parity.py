@@ -296,6 +296,26 @@ def test_qwen3_prefill_full_size(qwen, dev):
         assert np.array_equal(gp[name], g[name]), name
 
 
+def test_qwen3_layer_T32768_sampled(qwen, dev):
+    """The MFMA-bound size (T = 32768, 262144 routed slots) in the
+    configuration bench.py times (packed weights, pre-split router): the
+    64-token router, block-mode dispatch and 128-row tiles.  Top-k, gates,
+    skip mask and dispatch bit-exact on every token (shared logits); logits
+    and y on sampled tokens."""
+    L, tg, tr = qwen
+    S = L["shape"].with_tokens(32768)
+    Lt = dict(L, x=workloads.make_tokens(S, seed=0, step=7), shape=S)
+    g = GpuLayer(Lt, dev, packed=True).run(tg, tr)
+    check_routing_shared_logits(Lt, g, tg, tr)
+    check_dispatch(S, g)
+    rows = [0, 1, 63, 64, 4095, 4096, 16383, 20000, 32766, 32767]
+    h_ref = oracle.rmsnorm(Lt["x"][rows], L["gamma"], S.rms_eps, S.dtype)
+    lg_ref = oracle.router_logits(h_ref, L["w_router"], L["router_bias"]).astype(np.float64)
+    assert np.max(np.abs(g["logits"][rows].astype(np.float64) - lg_ref)) <= 2e-3
+    ref = oracle_y(Lt, g, tg, tr, tokens=rows)
+    assert rel_l2(values(g["y"][rows]), ref["y"][rows]) <= TOL["bf16"]
+
+
 def test_router_variants_batch_invariant(qwen, dev):
     """A token's h and logits do not depend on the batch around it: the router
     variants picked by batch size (16 experts per workgroup for small batches,
