@@ -136,10 +136,11 @@ template <> __device__ __forceinline__ float sumsq16<float>(u32x4 v) {
 // experts.  Sixteen waves split the hidden dimension: wave w takes k-steps
 // w, w+16, w+32, ...  Their partial logits are summed in a fixed wave order,
 // so a logit does not depend on timing, on NCB or on the batch size.  Token
-// rows past T and expert rows past E read a clamped valid row whose results
-// are never stored.  For small batches (NCB = 1: more workgroups share the
-// pre-split router planes) the first batch of a wave's weight and x loads is
-// issued before the RMS prologue, so that the two latencies overlap; with
+// rows past T load nothing (zeros) and expert rows past E read a clamped
+// valid row; their results are never stored.  For small batches (NCB = 1:
+// more workgroups share the pre-split router planes) the first batch of a
+// wave's weight loads (and x loads, without XL) is issued before the RMS
+// prologue, so that the two latencies overlap; with
 // SUB > 1 the column block is further cut into SUB sub-blocks of 16/SUB
 // experts, one per workgroup (lanes of other experts load nothing and their
 // MFMA columns are discarded: an output column depends only on its own
