@@ -558,6 +558,7 @@ __global__ __launch_bounds__(SK_NW * 64) __attribute__((amdgpu_waves_per_eu(4)))
   __shared__ uint32_t s_mask[EMAX_EXP];
   __shared__ int32_t s_pref[EMAX_EXP + 1];
   __shared__ int32_t s_off[EMAX_EXP + 1];
+  __shared__ int32_t s_mte[MAXS / 16 + EMAX_EXP];  // expert of each m-tile (expert order)
   __shared__ int32_t s_tok[MAXS];
   __shared__ float s_red[SK_NW][2][16][17];
   const ExpertArgs& a = f.g;
@@ -627,6 +628,7 @@ __global__ __launch_bounds__(SK_NW * 64) __attribute__((amdgpu_waves_per_eu(4)))
       if (e < E) {
         s_off[e] = int(run >> 16);
         s_pref[e] = int(run & 0xFFFFu);
+        for (int m = 0; m < int(pk[j] & 0xFFFFu); ++m) s_mte[int(run & 0xFFFFu) + m] = e;
       }
       run += pk[j];
     }
@@ -661,9 +663,13 @@ __global__ __launch_bounds__(SK_NW * 64) __attribute__((amdgpu_waves_per_eu(4)))
   const int ntiles = s_pref[E] * nb_count;
   // tile gi runs on XCD gi % 8 (the grid is a multiple of 8): dealt over the
   // XCDs, measured faster here than contiguous parts
+  // tiles in m-tile-major order (m-tile, then n-block): the tile's expert
+  // and rows come from the m-tile table in three LDS reads
   for (int gi = blockIdx.x; gi < ntiles; gi += gridDim.x) {
-    int e, nb, row0, rows;
-    find_tile(gi, nb_count, BM, E, s_pref, s_off, e, nb, row0, rows);
+    const int mt = gi / nb_count, nb = gi - mt * nb_count;
+    const int e = s_mte[mt];
+    const int row0 = s_off[e] + BM * (mt - s_pref[e]);
+    const int rows = min(BM, s_off[e + 1] - row0);
     const int col0 = nb * COLS;
     const int64_t ebytes = int64_t(N) * K * int(sizeof(T));
     const char* wm0 = reinterpret_cast<const char*>(a.W0) + int64_t(e) * ebytes;
