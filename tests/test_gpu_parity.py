@@ -466,6 +466,20 @@ def _adversarial_logits(T, E, rng):
     return lg
 
 
+def test_stream_tiling_beyond_its_mtile_table(dev):
+    """The split-K tiling forced on a batch with more m-tiles than its LDS
+    m-tile table holds (256 experts x ~8 m-tiles): it falls back to the
+    expert-major list; dispatch bit-exact, outputs within the bf16 bar."""
+    S = workloads.small_shape(T=4000, H=128, E=256, I=128, k=8, dtype="bf16", cfg_id=880)
+    L = workloads.make_layer(S)
+    g = GpuLayer(L, dev).run(0.0, 0.0, path=ace.ACE_PATH_STREAM)
+    off = check_dispatch(S, g)[0]
+    assert int(np.sum((np.diff(off) + 15) // 16)) > 1024
+    rows = [0, 1, 999, 2000, 3998, 3999]
+    ref = oracle_y(L, g, 0.0, 0.0, tokens=rows)
+    assert rel_l2(values(g["y"][rows]), ref["y"][rows]) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("E,k", [(16, 4), (64, 8), (65, 8), (128, 8), (128, 16), (150, 6), (192, 16), (256, 8), (256, 1)])
 @pytest.mark.parametrize("norm_topk", [True, False])
 def test_topk_adversarial_logits(dev, E, k, norm_topk):

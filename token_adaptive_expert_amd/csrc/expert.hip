@@ -68,7 +68,8 @@ constexpr int LDS_PITCH = ACE_LDS_PITCH;
 // ceil(n_e / BM) m-tiles; s_pref = exclusive prefix of those counts over the
 // experts (s_pref[E] = total), s_off = expert_offsets.
 template <int BM>
-__device__ __forceinline__ void build_tile_list(const ExpertArgs& a, int32_t* s_pref, int32_t* s_off) {
+__device__ __forceinline__ void build_tile_list(const ExpertArgs& a, int32_t* s_pref, int32_t* s_off,
+                                                int32_t* s_mte = nullptr, int mte_cap = 0) {
   if (wave_id() != 0) return;
   const int l = lane_id(), E = a.E;
   int cnt[4], loc = 0;
@@ -90,6 +91,9 @@ __device__ __forceinline__ void build_tile_list(const ExpertArgs& a, int32_t* s_
   for (int j = 0; j < 4; ++j) {
     const int e = l * 4 + j;
     if (e < E) s_pref[e] = run;
+    // optional m-tile table: the expert of each m-tile (entries past mte_cap dropped)
+    if (s_mte != nullptr)
+      for (int m = run; m < min(run + cnt[j], mte_cap); ++m) s_mte[m] = e;
     run += cnt[j];
   }
   if (l == 63) s_pref[E] = inc;
@@ -378,6 +382,7 @@ void expert_gemm_kernel(ExpertArgs a) {
 // applied.  Slot rows are read straight from global memory (they are few and
 // stay in L2).
 constexpr int SK_NW = 8;
+constexpr int SK_MT_CAP = 1024;  // m-tile table entries of the split-K kernel
 
 template <typename T, int KIND, int SK_NBK, int NGRP>
 __global__ __launch_bounds__(SK_NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void expert_splitk_kernel(ExpertArgs a) {
@@ -388,6 +393,7 @@ __global__ __launch_bounds__(SK_NW * 64) __attribute__((amdgpu_waves_per_eu(4)))
   constexpr int COLS = (KIND == 0) ? 16 : 16 * NGRP;  // output columns per tile
   __shared__ int32_t s_pref[257];
   __shared__ int32_t s_off[257];
+  __shared__ int32_t s_mte[SK_MT_CAP];
   __shared__ float s_red[SK_NW][NGRP][16][17];
 
   const int w = wave_id(), l = lane_id(), tid = threadIdx.x;
@@ -397,16 +403,27 @@ __global__ __launch_bounds__(SK_NW * 64) __attribute__((amdgpu_waves_per_eu(4)))
   const int nk = K / KS;
   const int nkw = w < nk ? (nk - 1 - w) / SK_NW + 1 : 0;  // this wave's k-steps
 
-  build_tile_list<BM>(a, s_pref, s_off);
+  build_tile_list<BM>(a, s_pref, s_off, s_mte, SK_MT_CAP);
   __syncthreads();
-  // XCD x takes the x-th contiguous part of the expert-major tile list
+  // XCD x takes the x-th contiguous part of the tile list: m-tile-major
+  // (m-tile, then n-block; expert and rows from the m-tile table) when the
+  // table holds every m-tile, else expert-major with a binary search
   const int ntiles = s_pref[E] * nb_count;
+  const bool table = s_pref[E] <= SK_MT_CAP;
   const int per_xcd = (ntiles + NXCD - 1) / NXCD;
   for (int wg = blockIdx.x; wg < NXCD * per_xcd; wg += gridDim.x) {
     const int g = (wg % NXCD) * per_xcd + wg / NXCD;
     if (g >= ntiles) continue;
     int e, nb, row0, rows;
-    find_tile(g, nb_count, BM, E, s_pref, s_off, e, nb, row0, rows);
+    if (table) {
+      const int mt = g / nb_count;
+      nb = g - mt * nb_count;
+      e = s_mte[mt];
+      row0 = s_off[e] + BM * (mt - s_pref[e]);
+      rows = min(BM, s_off[e + 1] - row0);
+    } else {
+      find_tile(g, nb_count, BM, E, s_pref, s_off, e, nb, row0, rows);
+    }
     const int col0 = nb * COLS;
     const int64_t ebytes = int64_t(N) * K * int(sizeof(T));
     const char* wm0 = reinterpret_cast<const char*>(a.W0) + int64_t(e) * ebytes;
