@@ -138,9 +138,8 @@ template <> __device__ __forceinline__ float sumsq16<float>(u32x4 v) {
 // so a logit does not depend on timing, on NCB or on the batch size.  Token
 // rows past T load nothing (zeros) and expert rows past E read a clamped
 // valid row; their results are never stored.  For small batches (NCB = 1:
-// more workgroups share the pre-split router planes) the first batch of a
-// wave's weight loads (and x loads, without XL) is issued before the RMS
-// prologue, so that the two latencies overlap; with
+// more workgroups share the pre-split router planes) gamma is staged in LDS;
+// with
 // SUB > 1 the column block is further cut into SUB sub-blocks of 16/SUB
 // experts, one per workgroup (lanes of other experts load nothing and their
 // MFMA columns are discarded: an output column depends only on its own
@@ -212,10 +211,9 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
         }
     }
   };
-  constexpr bool EARLY = NCB == 1;  // registers allow the early batch only with one column block
   constexpr int GQ = NARROW_HMAX / (RNTHR * 4);  // gamma quads per thread for the LDS copy
-  // EARLY: gamma is copied to LDS once (read there by every k-step of the MFMA loop)
-  const bool gam_lds = EARLY && packed;
+  // one column block: gamma is copied to LDS once (read there by every k-step of the MFMA loop)
+  const bool gam_lds = NCB == 1 && packed;
   // router bias of this thread's output (read after the last barrier)
   float bias_v = 0.f;
   if (do_router && a.bias != nullptr && threadIdx.x < TB * ECBW)
@@ -223,18 +221,16 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
 
   // inverse RMS: wave w owns token tok0 + w; a row is read 8 segments of
   // 64 lanes x 16 bytes at a time, all in flight together (segments past H
-  // are not loaded).  With EARLY, the gamma quads for the LDS copy (H <=
-  // NARROW_HMAX on this path) and the first batch of router loads go out
-  // behind the row's first segments: loads complete in order, so the sum
-  // waits for the row only and the router planes stay in flight across the
-  // barrier.
+  // are not loaded), then the gamma quads for the LDS copy (one column block:
+  // H <= NARROW_HMAX).  The router plane loads go out only after the
+  // barrier: issued earlier they queue ahead of the row loads in the CU's
+  // vector-memory pipe and hold up the RMS (measured: about 1 us per decode
+  // layer).
   {
     const T* row = x + int64_t(min(tok0 + w, a.T - 1)) * H;
     const bool row_valid = tok0 + w < a.T;  // waves past the batch load no row
     constexpr int SEG = 64 * EPL;
-    // segments per batch (4 with EARLY, for registers); the per-lane sum runs
-    // over the segments in order either way, so the result is the same
-    constexpr int RSEG = EARLY ? 4 : 8;
+    constexpr int RSEG = 8;  // segments per batch (the per-lane sum runs over them in order)
     float ss = 0.f;
     for (int j0 = 0; j0 < H; j0 += RSEG * SEG) {
       u32x4 v[RSEG];
@@ -249,9 +245,6 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
         for (int i = 0; i < GQ; ++i) {
           const int h = (int(threadIdx.x) + i * RNTHR) * 4;
           if (h < H) gq[i] = *reinterpret_cast<const f32x4*>(a.gamma + h);
-        }
-        if constexpr (EARLY) {
-          if (nki > 0) issue(0);
         }
 #pragma unroll
         for (int i = 0; i < GQ; ++i) {
@@ -275,7 +268,7 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
   if constexpr (sizeof(T) == 2) {
     if (packed) {
       for (int i0 = 0; i0 < nki; i0 += NBK) {
-        if (i0 > 0 || !EARLY) issue(i0);
+        issue(i0);
 #pragma unroll
         for (int b = 0; b < NBK; ++b) {
           if (i0 + b < nki) {
