@@ -34,7 +34,8 @@ namespace {
 #define ACE_GROUPED_STAGES 2  // depth of the weight register ring (grouped tiles)
 #endif
 #ifndef ACE_WAVES_PER_EU
-#define ACE_WAVES_PER_EU 3    // occupancy target given to the register allocator
+#define ACE_WAVES_PER_EU 3    // occupancy target given to the register allocator (4 to 7 row blocks;
+                              // up to 3 row blocks fit 128 VGPRs with no spill and take 4)
 #endif
 #ifndef ACE_BIG_RB
 #define ACE_BIG_RB 8          // 16-row blocks per tile for batches with >= 512 slots per expert
@@ -181,7 +182,7 @@ __device__ __forceinline__ void find_xcd_tile(int j, int x, int nbc, int E, cons
 
 template <typename T, int RB, int NW, int KIND, int STAGES>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(RB <= 2 ? 4 : (RB >= 16 ? 1 : (RB >= 8 ? 2 : ACE_WAVES_PER_EU)))))
+__attribute__((amdgpu_waves_per_eu(RB <= 3 ? 4 : (RB >= 16 ? 1 : (RB >= 8 ? 2 : ACE_WAVES_PER_EU)))))
 void expert_gemm_kernel(ExpertArgs a) {
   constexpr int EPL = St<T>::EPL;
   constexpr int KS = 4 * EPL;      // k values per k-step
