@@ -833,10 +833,9 @@ hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs
                          hipStream_t s) {
   constexpr int G = ACE_GROUPED_RB, S = ACE_GROUPED_STAGES;
   // moderate batches (up to 64 routed slots per expert on average before
-  // skipping): 48-row gate/up tiles (3 per CU) and 32-row down tiles (4 per
-  // CU); with one m-tile per expert the tile count then fills whole rounds
-  // of the resident slots at the sizes measured (1536 gate/up tiles at
-  // T = 1024, E = 128).  Very large batches (at least 512 slots per expert):
+  // skipping): 48-row gate/up tiles and 32-row down tiles, each 4 per CU
+  // (measured fastest at T = 1024, E = 128: 1536 gate/up and 2048+ down
+  // tiles).  Very large batches (at least 512 slots per expert):
   // 128-row tiles of 8 waves, which halve the L2 traffic per MFMA when the
   // GEMMs become compute-bound.  Between the two: 64-row tiles.
   const bool small_rb = int64_t(T) * k <= int64_t(64) * a.E && G > 2;
