@@ -191,10 +191,21 @@ ace_status moe_expert_forward(const ace_moe_desc* d, int32_t path, const void* h
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * moe_combine -- y[t] = residual[t] + sum over kept slots i = 0..k-1 (in that
- * order) of slot_out[slot_pos[t,i]], accumulated in float32, stored in dtype.
+ * moe_combine -- the layer output as the gate-weighted sum of the routed
+ * experts' maps ("ACE: Adaptive Calibration-Free Expert Skipping for
+ * MoE-based LLMs", picx.dev summary page: Introduction and Theoretical
+ * Foundation, where each token is routed to a few SwiGLU experts f, and
+ * Methodology section 1, where a routed slot's share is its router gate g;
+ * ACE drops the skipped slots' terms, Methodology section 3):
+ *   y[t] = residual[t] + sum over kept slots i = 0..k-1 (in that order) of
+ *          slot_out[slot_pos[t,i]] (= g_{t,i} f_{e_i}(x_t) from
+ *          moe_expert_forward), accumulated in float32, stored in dtype.
  * Skipped slots contribute nothing and the kept gates are not renormalised.
- * In:  slot_pos [T*k] i32; slot_out [T*k, H] f32; residual [T,H] dtype or NULL.
+ * residual is not part of the layer (the pages define none); it lets a stack
+ * of layers add x_{l+1} = x_l + y_l in the same pass.
+ * In:  slot_pos [T*k] i32 (row-major [T,k], -1 = skipped, as moe_dispatch
+ *      writes it); slot_out [T*k, H] f32; residual [T,H] dtype or NULL (may
+ *      equal y: each element is read before it is written).
  * Out: y [T,H] dtype.
  */
 ace_status moe_combine(const ace_moe_desc* d, const int32_t* slot_pos, const float* slot_out, const void* residual,

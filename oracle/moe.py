@@ -20,9 +20,13 @@ Readings where the page is silent (each also listed in the design notes):
 
 Pins (tests/test_oracle_*.py): closed forms for RMSNorm, softmax, SiLU and
 the scalar expert (tests/golden/scalar_expert.json), one-hot router rows,
-crafted top-k ties, the page's invariants for the skip rule, the SwiGLU
-norm bound with SVD spectral norms, a dense all-experts formulation at skip 0,
-and brute-force dispatch invariants.
+crafted top-k ties, the page's invariants for the skip rule, hand-worked
+skip masks for every fusion rule (tests/golden/skip_rule_example.json and,
+for MEAN and SCORE with thresholds of unequal scale,
+tests/golden/fusion_mean_score_example.json), MIN <= MEAN <= MAX ordering and
+the gate-only nature of SCORE, the SwiGLU norm bound with SVD spectral norms,
+a dense all-experts formulation at skip 0, and brute-force dispatch
+invariants.
 """
 from __future__ import annotations
 

@@ -20,7 +20,9 @@ Pins (tests/test_oracle_tables.py): a hand-derived scalar expert, invariance
 of A^GSP to a common scale of all W^down and of A^RCR to a shared translation
 of the router rows (the page's stated property) and to a common scale,
 ‖ΓW^gate W^down‖_F against the trace identity with explicit Gram matrices,
-and the unit layer mean of both tables.
+the unit layer mean of both tables, and RCR closed forms with a gain γ ≠ 1
+(a scalar expert with γ = 2 and a two-channel expert with γ = (2, 1/2)),
+which fail if f(q) leaves Γ out, squares it or averages it.
 """
 from __future__ import annotations
 

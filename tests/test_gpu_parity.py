@@ -694,7 +694,7 @@ def test_packed_router_planes_sum_exactly(dev):
     weights exactly, at the positions the header defines."""
     E, H = 20, 256
     w = (torch.randn(E, H, dtype=torch.float32, device=dev) * 0.02).contiguous()
-    w[3, 5] = 1.0 + 2.0 ** -20  # needs all three planes
+    w[3, 5] = 1.0 + 2.0 ** -9 + 2.0 ** -20  # splits into 1, 2^-9 and 2^-20: all three planes
     d = ace.make_desc(1, H, E, 128, 2, "bf16")
     dst = torch.empty(ace.moe_router_packed_bytes(d), dtype=torch.uint8, device=dev)
     ace.moe_pack_router(d, w, dst)
@@ -709,4 +709,5 @@ def test_packed_router_planes_sum_exactly(dev):
             l = q * 16 + e % 16
             tot = f[0, c, j, l, v] + f[1, c, j, l, v] + f[2, c, j, l, v]
             assert tot == (float(wn[e, k]) if e < E else 0.0), (e, k)
-    assert f[2, 0, 0, 16 * 0 + 3, 5] != 0.0 or True
+    # w[3, 5]: column block 0, k-step 0, lane 16*(5 // 8) + 3, element 5
+    assert (f[0, 0, 0, 3, 5], f[1, 0, 0, 3, 5], f[2, 0, 0, 3, 5]) == (1.0, 2.0 ** -9, 2.0 ** -20)

@@ -217,6 +217,63 @@ def test_skip_rule_golden():
             assert list(keep[0]) == tok["keep_" + fusion], fusion
 
 
+
+def test_fusion_mean_and_score_golden():
+    """Hand-worked MEAN and SCORE cases (Fusion Strategy Ablation, Table 5;
+    the gate-only "Score" baseline of Table 1), with the thresholds of the
+    two views 32x apart so that a mean of raw scores, a sum instead of a
+    mean, or a max/min in place of the mean each decide some slot wrongly."""
+    d = json.load(open(os.path.join(GOLDEN, "fusion_mean_score_example.json")))
+    a_g, a_r = np.array(d["a_gsp"], np.float32), np.array(d["a_rcr"], np.float32)
+    for tok in d["tokens"]:
+        idx = np.array([tok["idx"]], np.int32)
+        g = np.array([tok["gate"]], np.float32)
+        for fusion in ("max", "min", "mean", "gsp", "rcr", "score"):
+            tg = d["tau_score"] if fusion == "score" else d["tau_gsp"]
+            keep = oracle.skip_mask(idx, g, a_g, a_r, tg, d["tau_rcr"], fusion)
+            assert list(keep[0]) == tok["keep_" + fusion], fusion
+
+
+def test_mean_rule_lies_between_min_and_max():
+    """Averaging the two normalised scores: a slot MAX skips (both ratios
+    below one) MEAN skips too, and a slot MEAN skips MIN skips too; MEAN is
+    symmetric in the two views; a zero threshold makes MEAN skip nothing."""
+    rng = np.random.default_rng(17)
+    idx, g, a_g, a_r = _random_slots(rng)
+    for tg, tr in ((0.1, 0.2), (0.05, 0.3), (0.2, 0.06), (0.02, 2.0)):
+        k_max = oracle.skip_mask(idx, g, a_g, a_r, tg, tr, "max")
+        k_mean = oracle.skip_mask(idx, g, a_g, a_r, tg, tr, "mean")
+        k_min = oracle.skip_mask(idx, g, a_g, a_r, tg, tr, "min")
+        assert np.all(k_mean <= k_max) and np.all(k_min <= k_mean)
+        assert np.array_equal(k_mean, oracle.skip_mask(idx, g, a_r, a_g, tr, tg, "mean"))
+        assert k_mean[:, 0].all()
+        sg = (g * a_g[idx]).astype(np.float64)
+        sr = (g * a_r[idx]).astype(np.float64)
+        r = 0.5 * (sg / np.float32(tg) + sr / np.float32(tr))
+        clear = np.abs(r - 1.0) > 1e-6
+        clear[:, 0] = False
+        assert np.array_equal(~k_mean[clear], (r < 1.0)[clear])
+    assert oracle.skip_mask(idx, g, a_g, a_r, 0.0, 0.3, "mean").all()
+    assert oracle.skip_mask(idx, g, a_g, a_r, 0.3, 0.0, "mean").all()
+
+
+def test_score_rule_reads_the_gate_alone():
+    """The "Score" baseline thresholds the router gate itself: changing either
+    table, or the second threshold, changes nothing; the skipped slots are
+    exactly the non-top-1 slots whose gate is below the threshold."""
+    rng = np.random.default_rng(18)
+    idx, g, a_g, a_r = _random_slots(rng)
+    for tau in (0.05, 0.1, 0.2):
+        base = oracle.skip_mask(idx, g, a_g, a_r, tau, 0.1, "score")
+        expect = np.ones_like(base)
+        expect[:, 1:] = ~(g[:, 1:] < np.float32(tau))
+        assert np.array_equal(base, expect)
+        assert 0 < (~base).sum() < base[:, 1:].size
+        for ag2, ar2, tr2 in ((a_g * 100, a_r, 0.1), (a_g, a_r * 1e-3, 0.1), (a_r, a_g, 5.0)):
+            assert np.array_equal(base, oracle.skip_mask(idx, g, ag2.astype(np.float32), ar2.astype(np.float32),
+                                                         tau, tr2, "score"))
+
+
 def _random_slots(rng, T=200, E=16, k=4):
     l = rng.standard_normal((T, E)).astype(np.float32)
     idx = np.stack([oracle.topk_experts(l[t], k) for t in range(T)])

@@ -92,3 +92,39 @@ def test_rcr_scalar_expert_closed_form():
     d = np.array([[[4.0]], [[4.0]]])
     A = oracle.rcr_table(gamma, W, w, u, d, eps=0.0)
     assert np.allclose(A, [1.5, 0.5], rtol=1e-14)
+
+
+def test_rcr_scalar_experts_with_gain_closed_form():
+    """The gain Γ enters f(q) (Methodology section 2 with x = x̄Γ of the
+    Theoretical Foundation: q plays x̄).  H = I = 1, γ = 2, router rows (1) and
+    (-1) -> q = ±1, so the expert sees qγ = ±2.  Both experts have
+    (w_g, w_u, w_d) = (ln 3 / 2, 1, 1): expert 0 gets gate pre-activation
+    ln 3 and up value 2, SiLU(ln 3)·2 = (3/4)·ln 3·2, so ã₀ = 1.5 ln 3;
+    expert 1 gets -ln 3 and -2, SiLU(-ln 3)·(-2) = (-ln 3/4)·(-2), so
+    ã₁ = 0.5 ln 3.  Without γ the two raw values would be SiLU(±ln 3 / 2)·(±1)
+    and their ratio √3 instead of 3."""
+    gamma = np.array([2.0])
+    W = np.array([[1.0], [-1.0]])
+    w = np.full((2, 1, 1), math.log(3.0) / 2.0)
+    one = np.ones((2, 1, 1))
+    Q = oracle.rcr_prototypes(W, eps=0.0)
+    assert np.array_equal(Q, [[1.0], [-1.0]])
+    assert abs(oracle.rcr_raw(Q[0], gamma, w[0], one[0], one[0], eps=0.0) - 1.5 * math.log(3.0)) < 1e-14
+    assert abs(oracle.rcr_raw(Q[1], gamma, w[1], one[1], one[1], eps=0.0) - 0.5 * math.log(3.0)) < 1e-14
+    assert np.allclose(oracle.rcr_table(gamma, W, w, one, one, eps=0.0), [1.5, 0.5], rtol=1e-14)
+
+
+def test_rcr_gain_is_applied_per_channel():
+    """H = 2, I = 1 hand case with an uneven gain γ = (2, 1/2) and q = (1, 1):
+    qΓ = (2, 1/2).  w_g = (ln 3 / 4, ln 3) gives pre-activation ln 3/2 + ln 3/2
+    = ln 3; w_u = (1, 2) gives up value 2 + 1 = 3; SiLU(ln 3)·3 = (9/4) ln 3.
+    w_d = (3, 4)ᵀ: f = (9/4) ln 3·(3, 4), |f| = (45/4) ln 3, |q| = √2.
+    A gain left out or squared changes the pre-activation to (5/4) ln 3, and
+    one replaced by its mean to (25/16) ln 3."""
+    gamma = np.array([2.0, 0.5])
+    q = np.array([1.0, 1.0])
+    wg = np.array([[math.log(3.0) / 4.0, math.log(3.0)]])
+    wu = np.array([[1.0, 2.0]])
+    wd = np.array([[3.0], [4.0]])
+    expect = 45.0 / 4.0 * math.log(3.0) / math.sqrt(2.0)
+    assert abs(oracle.rcr_raw(q, gamma, wg, wu, wd, eps=0.0) - expect) < 1e-13
