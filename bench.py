@@ -157,6 +157,25 @@ class Bench:
         del a, b
         return 2 * (nbytes // 2) / (ms * 1e-3) / 1e9
 
+    def read_ceiling(self, nbytes=4 << 30, reps=10):
+        """Streaming-read rate of moe_hbm_read_probe (one pass over a 4 GiB
+        buffer with 16-byte loads on every compute unit), the best over a few
+        grid sizes: a measured read ceiling beside the datasheet peak."""
+        torch, ace = self.torch, self.ace
+        buf = torch.ones(nbytes // 4, dtype=torch.int32, device=self.dev)
+        ncu = torch.cuda.get_device_properties(self.dev).multi_processor_count
+        best, by_grid = 0.0, {}
+        for per_cu in (2, 4, 8, 16):
+            wg = ncu * per_cu
+            sink = torch.empty(wg, dtype=torch.int32, device=self.dev)
+            ms = timed(torch, lambda i: ace.moe_hbm_read_probe(buf, sink, wg), reps, 2)
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            by_grid[str(wg)] = round(gbs, 1)
+            best = max(best, gbs)
+        del buf
+        return {"GBs": round(best, 1), "bytes": nbytes, "by_workgroups": by_grid,
+                "kernel": "moe_hbm_read_probe (read only, 16-byte loads, 8 in flight per thread)"}
+
     def counts(self, bufs):
         off = bufs.offsets.cpu().numpy().astype(np.int64)
         n_e = np.diff(off)
@@ -278,10 +297,11 @@ def layer_roof(S, T, U, n_kept, ms):
             "roof_us": round(max(b / (HBM_PEAK_GBS * 1e9), f / (BF16_PEAK_TFLOPS * 1e12)) * 1e6, 1)}
 
 
-def extra_prefill(B, name, S, T, rate, steps, warmup, P=None, layer=None):
+def extra_prefill(B, name, S, T, rate, steps, warmup, P=None, layer=None, keep=None):
     """Whole-layer prefill of another workload (weights drawn on the device),
     thresholds by on-device quantile mapping on the batch itself, plus the
-    gate/up kernel alone."""
+    gate/up kernel alone.  ``keep`` (a dict) receives the layer's linear
+    device weights, its input and thresholds, for the oracle's timing leg."""
     torch, ace = B.torch, B.ace
     from workloads.device import make_layer_device, make_tokens_device
     if layer is None:
@@ -289,7 +309,8 @@ def extra_prefill(B, name, S, T, rate, steps, warmup, P=None, layer=None):
         layer = ace.AceMoeLayer(P["gamma"], P["w_router"], P["router_bias"], P["w_gate"], P["w_up"],
                                 P["w_down"], P["a_gsp"], P["a_rcr"], S.k, S.norm_topk, "max",
                                 S.rms_eps).packed()
-        del P["w_gate"], P["w_up"], P["w_down"]
+        if keep is None:
+            del P["w_gate"], P["w_up"], P["w_down"]
     x = make_tokens_device(S, B.dev, seed=0, step=7, T=T) if T != S.T else P["x"]
     b = layer.buffers(T)
     layer.route(x, 0.0, 0.0, b)
@@ -300,16 +321,25 @@ def extra_prefill(B, name, S, T, rate, steps, warmup, P=None, layer=None):
     tg, tr = [float(v) for v in tau_t.cpu()]
     ms = timed(torch, lambda i: layer.forward(x, tg, tr, b), steps, warmup)
     gu = timed(torch, lambda i: layer.experts(T, b, ace.ACE_STAGE_GATEUP), steps, 2)
+    dn = timed(torch, lambda i: layer.experts(T, b, ace.ACE_STAGE_DOWN), steps, 2)
     off = b.offsets.cpu().numpy().astype(np.int64)
     n_kept, U = int(off[-1]), int((np.diff(off) > 0).sum())
     gu_flops = n_kept * 4 * S.H * S.I
-    gu_bytes = U * 2 * S.H * S.I * 2 + T * S.H * 2 + n_kept * S.I * 2
+    gu_bytes = U * 2 * S.H * S.I * 2 + T * S.H * 2
+    dn_bytes = U * S.H * S.I * 2
     out = {"workload": name, "T": T, "H": S.H, "E": S.E, "I": S.I, "k": S.k, "skip_target": rate,
            "skip_realized": round(1 - n_kept / (T * S.k), 5), "active_experts": U, "n_kept": n_kept,
+           "max_rows_per_expert": int(np.diff(off).max()),
            "tokens_per_s": round(T / (ms * 1e-3), 1), "us_per_layer": round(ms * 1e3, 2),
            "gateup_us": round(gu * 1e3, 2), "gateup_tflops": round(gu_flops / (gu * 1e-3) / 1e12, 1),
-           "gateup_GBs": round(gu_bytes / (gu * 1e-3) / 1e9, 1)}
+           "gateup_mfma_frac": round(gu_flops / (gu * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+           "gateup_GBs": round(gu_bytes / (gu * 1e-3) / 1e9, 1),
+           "gateup_hbm_frac": round(gu_bytes / (gu * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "down_us": round(dn * 1e3, 2), "down_GBs": round(dn_bytes / (dn * 1e-3) / 1e9, 1),
+           "down_tflops": round(n_kept * 2 * S.H * S.I / (dn * 1e-3) / 1e12, 1)}
     out.update(layer_roof(S, T, U, n_kept, ms))
+    if keep is not None:
+        keep.update(P=P, x=x, tau=(tg, tr))
     return out
 
 
@@ -324,17 +354,22 @@ def dense_gemm_ceiling(B, M=32768, reps=10):
     return round(2 * M * S.H * 2 * S.I / (ms * 1e-3) / 1e12, 1)
 
 
-def stack48(B, decode_steps=128, M=8):
+def stack48(B, decode_steps=128, M=8, keep=None, keep_layers=(0, 23, 47), keep_tokens=32):
     """48 independent Qwen3-30B-A3B-shaped layers (each with its own Zipf(1.1)
     router prior; 58 GB of bf16 expert weights) with the residual stream:
     per-layer thresholds by on-device quantile mapping at 60% on the layers'
     own prefill inputs, then the 1024-token prefill and decode steps of 8
-    fresh tokens, each step one HIP graph replay of all 48 layers."""
+    fresh tokens, each step one HIP graph replay of all 48 layers.  After the
+    timing, one untimed pass of each reads every layer's active experts U and
+    kept slots n_kept back for the algorithmic bytes.  ``keep`` (a dict)
+    receives, for the layers in keep_layers, their linear device weights,
+    thresholds and the first keep_tokens rows of their prefill input x_l
+    (the GPU's residual stream), for the oracle's timing leg."""
     torch, ace = B.torch, B.ace
     import workloads
     from workloads.device import make_layer_device, make_tokens_device
     S = workloads.CONFIGS["stack48_layer"]
-    layers, x0 = [], None
+    layers, x0, kept_P = [], None, {}
     for l in range(workloads.STACK_LAYERS):
         P = make_layer_device(S, B.dev, seed=0, layer=l, with_x=(l == 0))
         if l == 0:
@@ -342,6 +377,8 @@ def stack48(B, decode_steps=128, M=8):
         layers.append(ace.AceMoeLayer(P["gamma"], P["w_router"], P["router_bias"], P["w_gate"], P["w_up"],
                                       P["w_down"], P["a_gsp"], P["a_rcr"], S.k, S.norm_topk, "max",
                                       S.rms_eps).packed())
+        if keep is not None and l in keep_layers:
+            kept_P[l] = P
         del P
     st = ace.AceMoeStack(layers)
     st.calibrate(x0, 0.6)
@@ -356,17 +393,59 @@ def stack48(B, decode_steps=128, M=8):
 
     dec_ms = timed(torch, step, decode_steps, 8)
     nl = len(layers)
+
+    def per_layer(x, T):
+        """One untimed pass layer by layer: (U, n_kept) of every layer, and
+        the inputs x_l of the kept layers."""
+        cur, U, nk, xl = x, [], [], {}
+        for l, lay in enumerate(layers):
+            if l in kept_P:
+                xl[l] = cur[:keep_tokens].clone()
+            b = bufs[l % 2] if T == S.T else dbufs[l % 2]
+            lay.forward(cur, st.tau[l][0], st.tau[l][1], b, residual=cur)
+            off = b.offsets[:lay.E + 1].cpu().numpy().astype(np.int64)
+            nk.append(int(off[-1]))
+            U.append(int((np.diff(off) > 0).sum()))
+            cur = b.y[:T]
+        return U, nk, xl
+
+    dbufs = st.buffers(M)
+    U_pre, nk_pre, xl = per_layer(x0, S.T)
+    U_dec, nk_dec = [0] * nl, [0] * nl
+    for i in range(4):   # decode steps 0..3: average U and n_kept
+        u, n, _ = per_layer(xs[i], M)
+        U_dec = [a + b for a, b in zip(U_dec, u)]
+        nk_dec = [a + b for a, b in zip(nk_dec, n)]
+    U_dec = [u / 4 for u in U_dec]
+    nk_dec = [n / 4 for n in nk_dec]
+    wl = 3 * S.H * S.I * 2
+    fixed = S.E * S.H * 4 + 8 * S.E
+    pre_bytes = sum(u * wl + fixed + S.T * S.H * 4 for u in U_pre)
+    pre_flops = sum(n * 6 * S.H * S.I + 2 * S.T * S.H * S.E for n in nk_pre)
+    dec_bytes = sum(u * wl + fixed + M * S.H * 4 for u in U_dec)
     skip = [1 - n / (S.T * S.k) for n in st.kept]
     out = {"workload": "48 qwen3_30b_a3b-shaped layers, Zipf(1.1) router priors, residual stream, 60% skip",
            "layers": nl, "weights_GB": round(nl * 3 * S.E * S.H * S.I * 2 / 1e9, 1),
            "prefill_tokens": S.T, "prefill_ms": round(pre_ms, 3),
            "prefill_tokens_per_s": round(S.T / (pre_ms * 1e-3), 1),
            "prefill_us_per_layer": round(pre_ms * 1e3 / nl, 2),
+           "prefill_U_mean_min_max": [round(float(np.mean(U_pre)), 2), min(U_pre), max(U_pre)],
+           "prefill_n_kept_total": int(sum(nk_pre)),
+           "prefill_alg_bytes": int(pre_bytes), "prefill_alg_flops": int(pre_flops),
+           "prefill_hbm_frac": round(pre_bytes / (pre_ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+           "prefill_mfma_frac": round(pre_flops / (pre_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
            "decode_M": M, "decode_steps": decode_steps, "decode_ms_per_step": round(dec_ms, 4),
            "decode_us_per_layer": round(dec_ms * 1e3 / nl, 2),
            "decode_tokens_per_s": round(M / (dec_ms * 1e-3), 1),
+           "decode_U_mean_per_layer": round(float(np.mean(U_dec)), 2),
+           "decode_n_kept_mean_per_layer": round(float(np.mean(nk_dec)), 2),
+           "decode_alg_bytes_per_step": int(dec_bytes),
+           "decode_hbm_frac": round(dec_bytes / (dec_ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+           "decode_U_note": "U and n_kept averaged over decode steps 0-3 (one untimed eager pass each)",
            "calibration_skip_min_max": [round(min(skip), 5), round(max(skip), 5)]}
-    del st, layers, g, bufs
+    if keep is not None:
+        keep.update(S=S, layers={l: dict(P=kept_P[l], x=xl[l], tau=st.tau[l]) for l in kept_P})
+    del st, layers, g, bufs, dbufs
     torch.cuda.empty_cache()
     return out
 
@@ -435,11 +514,7 @@ def cpu_baseline(L, S, tau, ntok, min_seconds=10.0, max_passes=20):
     """The oracle, as it stands, over the first `ntok` tokens of the batch,
     repeated until at least `min_seconds` of host time (at most `max_passes`)."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
+    cores = _blas_threads()
     x = L["x"][:ntok]
     t0 = time.time()
     passes = 0
@@ -451,6 +526,88 @@ def cpu_baseline(L, S, tau, ntok, min_seconds=10.0, max_passes=20):
     return {"value": passes * ntok / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{passes} passes over the first {ntok} of the {S.T} prefill tokens of the same layer and "
                       f"thresholds, {dt:.1f} s of host time"}
+
+
+class _DeviceExperts:
+    """w[e] of a device tensor copied to host on demand (stored form), so the
+    oracle copies only the experts its own routing selects."""
+
+    def __init__(self, t):
+        self.t = t
+
+    def __getitem__(self, e):
+        from workloads.torch_io import from_torch
+        return from_torch(self.t[int(e)])
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return 1
+
+
+def _oracle_pass(x, P, S, tau, host=None):
+    """One call of the oracle's layer forward on the rows x (host, stored
+    form), timed; weights from host arrays (``host``) or fetched from the
+    device tensors of P expert by expert."""
+    import oracle
+    from workloads.torch_io import from_torch
+    if host is None:
+        host = {n: from_torch(P[n]) if P[n] is not None else None for n in
+                ("gamma", "w_router", "router_bias", "a_gsp", "a_rcr")}
+        host.update({n: _DeviceExperts(P[n]) for n in ("w_gate", "w_up", "w_down")})
+    t0 = time.time()
+    r = oracle.moe_layer(x, host["gamma"], host["w_router"], host["router_bias"], host["w_gate"], host["w_up"],
+                         host["w_down"], host["a_gsp"], host["a_rcr"], tau[0], tau[1], S.k, bool(S.norm_topk),
+                         S.rms_eps, S.dtype)
+    return time.time() - t0, int(r["keep"].sum())
+
+
+def cpu_by_config(B, head_tau, glm=None, stack=None, decode_M=8):
+    """The oracle, as it stands, timed on the host cores for each other
+    workload, on bounded samples: the tiny f32 layer (all 64 tokens, its
+    thresholds by the oracle's own quantile mapping at 50%), one decode step
+    of 8 tokens on the headline layer, the first 16 tokens of the
+    GLM-4.5-Air-shaped layer, and the first 32 tokens of the inputs of
+    layers 0, 23 and 47 of the 48-layer stack.  Each time includes the
+    oracle's float64 copies of the experts it touches (its own per-call cache)."""
+    import oracle
+    import workloads
+    from workloads.torch_io import from_torch
+    out = {"cores": int(_blas_threads())}
+    S1 = workloads.CONFIGS["tiny"]
+    L1 = workloads.make_layer(S1)
+    h = oracle.rmsnorm(L1["x"], L1["gamma"], S1.rms_eps, S1.dtype)
+    lg = oracle.router_logits(h, L1["w_router"], None)
+    idx = np.stack([oracle.topk_experts(lg[t], S1.k) for t in range(S1.T)])
+    g = np.stack([oracle.topk_gates(lg[t], idx[t], True) for t in range(S1.T)])
+    tg, tr, _, _ = oracle.quantile_thresholds(idx, g, L1["a_gsp"], L1["a_rcr"], 0.5)
+    dt, nk = _oracle_pass(L1["x"], None, S1, (tg, tr), host=L1)
+    out["tiny_f32_T64"] = {"tokens": S1.T, "seconds": round(dt, 3), "tokens_per_s": round(S1.T / dt, 1),
+                           "n_kept": nk}
+    Sd = workloads.CONFIGS["qwen3_30b_a3b_decode"].with_tokens(decode_M)
+    xd = workloads.make_tokens(Sd, seed=0, step=1)
+    dt, nk = _oracle_pass(xd, None, Sd, head_tau, host=B.L)
+    out[f"decode_M{decode_M}"] = {"tokens": decode_M, "seconds_per_layer_step": round(dt, 3),
+                                  "us_per_layer_step": round(dt * 1e6, 1), "n_kept": nk}
+    if glm:
+        Sg = workloads.CONFIGS["glm45_air_shape"]
+        xg = from_torch(glm["x"][:16])
+        dt, nk = _oracle_pass(xg, glm["P"], Sg, glm["tau"])
+        out["glm45_air_shape_T4096"] = {"tokens": 16, "seconds": round(dt, 3), "tokens_per_s": round(16 / dt, 2),
+                                        "n_kept": nk, "sample": "first 16 of the 4096 prefill tokens"}
+    if stack:
+        Ss = stack["S"]
+        per = {}
+        for l, rec in sorted(stack["layers"].items()):
+            xl = from_torch(rec["x"])
+            dt, nk = _oracle_pass(xl, rec["P"], Ss, rec["tau"])
+            per[str(l)] = {"tokens": int(xl.shape[0]), "seconds": round(dt, 3),
+                           "tokens_per_s": round(xl.shape[0] / dt, 1), "n_kept": nk}
+        out["stack48_layers"] = per
+    return out
 
 
 def measured_traffic(kernel_key):
@@ -502,10 +659,16 @@ def main():
     head = B.prefill(args.skip)
     T = S.T
     value = T / (head["ms"] * 1e-3)
-    # dominant kernel: grouped gate/up GEMM (+SiLU); algorithmic bytes per launch
-    gu_bytes = head["U"] * 2 * S.H * S.I * 2 + T * S.H * 2 + head["n_kept"] * S.I * 2
+    # dominant kernel: grouped gate/up GEMM (+SiLU).  Algorithmic bytes per
+    # launch: the active experts' gate and up weights and the token rows; the
+    # act rows it writes are implementation traffic.  Down: the active
+    # experts' down weights only (act read and float32 slot rows written are
+    # implementation traffic; y is written by the combine).
+    gu_bytes = head["U"] * 2 * S.H * S.I * 2 + T * S.H * 2
+    gu_impl = head["n_kept"] * S.I * 2
     gu_gbs = gu_bytes / (head["gateup_ms"] * 1e-3) / 1e9
-    dn_bytes = head["U"] * S.H * S.I * 2 + head["n_kept"] * (S.I * 2 + S.H * 4)
+    dn_bytes = head["U"] * S.H * S.I * 2
+    dn_impl = head["n_kept"] * (S.I * 2 + S.H * 4)
     layer_bytes = head["U"] * 3 * S.H * S.I * 2 + S.E * S.H * 4 + T * S.H * 4 + 8 * S.E
     layer_flops = head["n_kept"] * 6 * S.H * S.I + 2 * T * S.H * S.E
     res = {
@@ -531,15 +694,18 @@ def main():
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("expert_gemm_gateup_qwen3_30b_a3b_T1024_skip60"),
                      "kernel": "expert_gemm gate/up+SiLU (grouped)", "kernel_ms": round(head["gateup_ms"], 5),
-                     "alg_bytes_per_launch": gu_bytes,
+                     "alg_bytes_per_launch": gu_bytes, "impl_bytes_per_launch": gu_impl,
                      "down_kernel_ms": round(head["down_ms"], 5),
-                     "down_achieved": round(dn_bytes / (head["down_ms"] * 1e-3) / 1e9, 1)},
+                     "down_alg_bytes_per_launch": dn_bytes, "down_impl_bytes_per_launch": dn_impl,
+                     "down_achieved": round(dn_bytes / (head["down_ms"] * 1e-3) / 1e9, 1),
+                     "down_frac": round(dn_bytes / (head["down_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "layer_roofline": {"alg_bytes": layer_bytes, "alg_flops": layer_flops,
                            "hbm_frac": round(layer_bytes / (head["ms"] * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
                            "mfma_frac": round(layer_flops / (head["ms"] * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
                            "us_per_layer": round(head["ms"] * 1e3, 2)},
     }
     res["hbm_copy_ceiling_GBs"] = round(B.copy_ceiling(), 1)
+    res["hbm_read_ceiling"] = B.read_ceiling()
     if not args.no_sweep:
         sweep = {}
         for r in (0.0, 0.5):
@@ -557,21 +723,32 @@ def main():
         res["decode_pool"] = B.decode_pool(head["tau"])
         res["decode_detail"] = {str(m): {k2: (round(v2, 4) if isinstance(v2, float) else v2) for k2, v2 in v.items()}
                                 for m, v in dec.items()}
+    glm_keep = {} if not args.no_cpu_baseline else None
+    stack_keep = {} if not args.no_cpu_baseline else None
     if not args.no_extra:
         import workloads
         res["glm45_air_shape_prefill"] = extra_prefill(B, "glm45_air_shape MoE layer prefill (Zipf router prior)",
                                                        workloads.CONFIGS["glm45_air_shape"], 4096, 0.5,
-                                                       max(10, args.steps // 2), 3)
+                                                       max(10, args.steps // 2), 3, keep=glm_keep)
         res["mfma_bound_T32768"] = extra_prefill(B, "qwen3_30b_a3b layer at T=32768 (MFMA-bound supplement)", S,
                                                  32768, args.skip, 10, 2, P=B.P, layer=B.layers[0])
         res["dense_gemm_ceiling_tflops"] = dense_gemm_ceiling(B)
     if not args.no_stack:
-        res["stack48"] = stack48(B)
+        res["stack48"] = stack48(B, keep=stack_keep)
     if not args.no_tables:
         res["tables_build"] = tables_build(B)
         res["calibration"] = calibration_leg(B)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(B.L, S, head["tau"], args.cpu_tokens)
+        res["cpu_baseline_by_config"] = cpu_by_config(B, head["tau"], glm_keep or None, stack_keep or None)
+    # release device memory before the last line, so that the process ends
+    # promptly once it has printed
+    del B, glm_keep, stack_keep
+    import gc
+    gc.collect()
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)
 
 

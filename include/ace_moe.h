@@ -309,6 +309,17 @@ ace_status moe_build_tables(const ace_moe_desc* d, float eps, const float* gamma
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_hbm_read_probe -- a measuring aid, not a step of the layer: reads
+ * `bytes` (a multiple of 16) of device memory at `buf` once, with 16-byte
+ * loads spread over `workgroups` workgroups of 256 threads (a grid-stride
+ * loop, eight independent loads in flight per thread), and writes one
+ * 32-bit fold of the words read per workgroup to sink [workgroups] (device).
+ * Timing it gives the streaming HBM read rate that the weight-streaming
+ * expert kernels are compared with, beside the datasheet peak.
+ */
+ace_status moe_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups, void* stream);
+
+/*
  * moe_set_kernel_events -- for profiling callers: the next moe_expert_forward
  * on this thread records `start` (a hipEvent_t) on its stream just before the
  * gate/up kernel and `stop` just after it, then forgets both.  NULL clears.

@@ -73,6 +73,30 @@ def rel_l2(a: np.ndarray, b: np.ndarray) -> float:
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
+# The parity bar on layer outputs: relative L2 over the whole output, and a
+# looser bound on every token's own row, so that one wrong row (a bad tile
+# edge, a stale slot) cannot hide inside a large, otherwise correct output.
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+TOKEN_TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def check_y(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "y") -> float:
+    """got, ref: [rows, H] values (float64).  Returns the worst row's error."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape and got.ndim == 2
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    g = rel_l2(got, ref)
+    assert g <= TOL[dtype], f"{what}: rel-L2 {g:.3g} > {TOL[dtype]}"
+    num = np.linalg.norm(got - ref, axis=1)
+    den = np.maximum(np.linalg.norm(ref, axis=1), 1e-300)
+    per = num / den
+    worst = int(np.argmax(per)) if per.size else -1
+    if per.size:
+        assert per[worst] <= TOKEN_TOL[dtype], f"{what}: row {worst} rel-L2 {per[worst]:.3g} > {TOKEN_TOL[dtype]}"
+    return float(per[worst]) if per.size else 0.0
+
+
 def check_routing_shared_logits(L: dict, g: dict, tau_g, tau_r, fusion="max", norm_topk=None):
     """The oracle's top-k, gates and skip mask on the GPU's own float32 logits
     must equal the GPU's bit for bit."""
@@ -98,3 +122,15 @@ def check_dispatch(S, g: dict):
     expect_gate = g["topk_gate"][tok, slot] if n else np.zeros(0, np.float32)
     assert np.array_equal(g["sorted_gate"][:n].view(np.uint32), expect_gate.view(np.uint32))
     return off, tok, slot, pos
+
+
+def heavy_tail_rows(g: dict, n_experts: int = 3, rows: int = 16) -> set:
+    """Tokens of the last rows of the most loaded experts (the last, ragged
+    m-tiles of their segments), from the GPU's own dispatch."""
+    off = g["offsets"].astype(np.int64)
+    n_e = np.diff(off)
+    out = set()
+    for e in np.argsort(-n_e, kind="stable")[:n_experts]:
+        lo = max(int(off[e]), int(off[e + 1]) - rows)
+        out.update(int(t) for t in g["sorted_token"][lo:int(off[e + 1])])
+    return out

@@ -14,11 +14,11 @@ import torch
 import oracle
 import workloads
 import token_adaptive_expert_amd as ace
-from gpu_util import (GpuLayer, check_dispatch, check_routing_shared_logits, oracle_thresholds, rel_l2, values)
+from gpu_util import (TOL, GpuLayer, check_dispatch, check_routing_shared_logits, check_y, heavy_tail_rows,
+                      oracle_thresholds, rel_l2, values)
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-5, "bf16": 1e-2}
 PATHS = [ace.ACE_PATH_GROUPED, ace.ACE_PATH_STREAM]
 
 
@@ -45,16 +45,16 @@ def check_h_and_logits(L, g, logit_atol):
     assert np.max(np.abs(g["logits"].astype(np.float64) - lg_ref)) <= logit_atol
 
 
-def check_slot_outputs(L, g, ref, tol):
-    """Per-slot gate-scaled expert outputs (down GEMM rows) against the oracle."""
-    S = L["shape"]
+def check_slot_outputs(L, g, ref, dtype):
+    """Per-slot gate-scaled expert outputs (down GEMM rows) against the oracle,
+    over all of them and row by row."""
     rows, refs = [], []
     for (t, i), o in ref["slot_out"].items():
         p = g["slot_pos"][t, i]
         rows.append(g["slot_out"][p])
         refs.append(o)
     if rows:
-        assert rel_l2(np.stack(rows), np.stack(refs)) <= tol
+        check_y(np.stack(rows), np.stack(refs), dtype, "slot_out")
 
 
 # ---------------------------------------------------------------- tiny fp32 layer
@@ -77,8 +77,8 @@ def test_tiny_fp32_layer(tiny, dev, path):
     n = math.floor(0.5 * S.T * S.k + 0.5)
     assert abs(int((~keep).sum()) - n) <= 2
     ref = oracle_y(L, g, tg, tr)
-    assert rel_l2(values(g["y"]), ref["y"]) <= TOL["f32"]
-    check_slot_outputs(L, g, ref, TOL["f32"])
+    check_y(values(g["y"]), ref["y"], "f32")
+    check_slot_outputs(L, g, ref, "f32")
 
 
 def test_oracle_logits_fed_to_gpu(tiny, dev):
@@ -105,7 +105,7 @@ def test_fusion_rules(tiny, dev, fusion):
     check_routing_shared_logits(L, g, tau_g, tr, fusion=fusion)
     check_dispatch(L["shape"], g)
     ref = oracle_y(L, g, tau_g, tr, fusion=fusion)
-    assert rel_l2(values(g["y"]), ref["y"]) <= TOL["f32"]
+    check_y(values(g["y"]), ref["y"], "f32")
 
 
 def test_threshold_extremes(tiny, dev):
@@ -115,11 +115,11 @@ def test_threshold_extremes(tiny, dev):
     g0 = gl.run(0.0, 0.0)
     assert g0["keep"].all() and g0["offsets"][-1] == S.T * S.k     # plain top-k MoE
     ref = oracle_y(L, g0, 0.0, 0.0)
-    assert rel_l2(values(g0["y"]), ref["y"]) <= TOL["f32"]
+    check_y(values(g0["y"]), ref["y"], "f32")
     gi = gl.run(float("inf"), float("inf"))
     assert gi["keep"][:, 0].all() and not gi["keep"][:, 1:].any()   # only the top-1 survives
     ref = oracle_y(L, gi, np.inf, np.inf)
-    assert rel_l2(values(gi["y"]), ref["y"]) <= TOL["f32"]
+    check_y(values(gi["y"]), ref["y"], "f32")
     # AND, not OR: one view alone never skips
     ga = gl.run(float("inf"), 0.0)
     assert ga["keep"].all()
@@ -130,7 +130,7 @@ def test_gates_without_topk_renormalisation(tiny, dev):
     g = GpuLayer(L, dev, norm_topk=0).run(tg, tr)
     check_routing_shared_logits(L, g, tg, tr, norm_topk=0)
     ref = oracle_y(L, g, tg, tr, norm_topk=0)
-    assert rel_l2(values(g["y"]), ref["y"]) <= TOL["f32"]
+    check_y(values(g["y"]), ref["y"], "f32")
 
 
 def test_deterministic_and_residual(tiny, dev):
@@ -176,8 +176,8 @@ def test_bf16_shapes(dev, path, case):
     check_routing_shared_logits(L, g, tg, tr)
     check_dispatch(S, g)
     ref = oracle_y(L, g, tg, tr)
-    assert rel_l2(values(g["y"]), ref["y"]) <= TOL["bf16"]
-    check_slot_outputs(L, g, ref, TOL["bf16"])
+    check_y(values(g["y"]), ref["y"], "bf16")
+    check_slot_outputs(L, g, ref, "bf16")
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -194,7 +194,7 @@ def test_one_expert_takes_every_token(dev, path):
     off, _, _, _ = check_dispatch(S, g)
     assert off[4] - off[3] == S.T
     ref = oracle_y(L, g, tg, tr)
-    assert rel_l2(values(g["y"]), ref["y"]) <= TOL["bf16"]
+    check_y(values(g["y"]), ref["y"], "bf16")
 
 
 # ---------------------------------------------------------------- seeded random shapes
@@ -230,15 +230,15 @@ def test_random_shapes(dev, i):
     check_routing_shared_logits(L, g, tg, tr, fusion=fusion)
     check_dispatch(S, g)
     ref = oracle_y(L, g, tg, tr, fusion=fusion)
-    assert rel_l2(values(g["y"]), ref["y"]) <= TOL[S.dtype]
-    check_slot_outputs(L, g, ref, TOL[S.dtype])
+    check_y(values(g["y"]), ref["y"], S.dtype)
+    check_slot_outputs(L, g, ref, S.dtype)
 
 
 @pytest.mark.parametrize("i", range(6))
 def test_random_large_batches(dev, i):
     """Seeded random layers of 1000-4200 tokens (multi-workgroup dispatch, the
     32/64-token router, 64- and 128-row tiles): routing, gates, skip mask and
-    dispatch bit for bit on shared logits; y on sampled tokens."""
+    dispatch bit for bit on shared logits; y on every token."""
     rng = np.random.default_rng(77000 + i)
     E = int(rng.choice([8, 16, 64, 128, 256]))
     k = int(rng.integers(1, min(E, 16) + 1))
@@ -257,9 +257,8 @@ def test_random_large_batches(dev, i):
     g = GpuLayer(L, dev, fusion=fusion, packed=packed).run(tg, tr, path)
     check_routing_shared_logits(L, g, tg, tr, fusion=fusion)
     check_dispatch(S, g)
-    toks = sorted(set([0, 1, T // 2, T - 2, T - 1] + rng.integers(0, T, 12).tolist()))
-    ref = oracle_y(L, g, tg, tr, tokens=toks, fusion=fusion)
-    assert rel_l2(values(g["y"][toks]), ref["y"][toks]) <= TOL[dtype]
+    ref = oracle_y(L, g, tg, tr, fusion=fusion)
+    check_y(values(g["y"]), ref["y"], dtype)
 
 
 # ---------------------------------------------------------------- full Qwen3-30B-A3B-shaped layer
@@ -271,10 +270,10 @@ def qwen():
     return L, tg, tr
 
 
-SAMPLE = [0, 1, 2, 63, 64, 65, 127, 128, 500, 777, 1022, 1023]
-
-
+@pytest.mark.timeout(600)
 def test_qwen3_prefill_full_size(qwen, dev):
+    """The headline layer: y and every slot row against the oracle on all
+    1024 tokens, globally and token by token."""
     L, tg, tr = qwen
     S = L["shape"]
     gl = GpuLayer(L, dev)
@@ -284,8 +283,9 @@ def test_qwen3_prefill_full_size(qwen, dev):
     check_dispatch(S, g)
     skipped = int((~g["keep"]).sum())
     assert abs(skipped / (S.T * S.k) - 0.6) < 0.01
-    ref = oracle_y(L, g, tg, tr, tokens=SAMPLE)
-    assert rel_l2(values(g["y"][SAMPLE]), ref["y"][SAMPLE]) <= TOL["bf16"]
+    ref = oracle_y(L, g, tg, tr)
+    check_y(values(g["y"]), ref["y"], "bf16")
+    check_slot_outputs(L, g, ref, "bf16")
     # the other tiling gives the same layer output
     g2 = gl.run(tg, tr, path=ace.ACE_PATH_STREAM)
     assert rel_l2(values(g2["y"]), values(g["y"])) <= 1e-2
@@ -296,24 +296,32 @@ def test_qwen3_prefill_full_size(qwen, dev):
         assert np.array_equal(gp[name], g[name]), name
 
 
+@pytest.mark.timeout(600)
 def test_qwen3_layer_T32768_sampled(qwen, dev):
     """The MFMA-bound size (T = 32768, 262144 routed slots) in the
     configuration bench.py times (packed weights, pre-split router): the
     64-token router, block-mode dispatch and 128-row tiles.  Top-k, gates,
     skip mask and dispatch bit-exact on every token (shared logits); logits
-    and y on sampled tokens."""
+    and y on 1024+ tokens: the first and last 128, the last 32 rows of the
+    four most loaded experts (their ragged last m-tiles) and random ones."""
     L, tg, tr = qwen
     S = L["shape"].with_tokens(32768)
     Lt = dict(L, x=workloads.make_tokens(S, seed=0, step=7), shape=S)
     g = GpuLayer(Lt, dev, packed=True).run(tg, tr)
     check_routing_shared_logits(Lt, g, tg, tr)
     check_dispatch(S, g)
-    rows = [0, 1, 63, 64, 4095, 4096, 16383, 20000, 32766, 32767]
+    rng = np.random.default_rng(32768)
+    rows = set([0, 1, 63, 64, 4095, 4096, 16383, 20000, 32766, 32767]) | heavy_tail_rows(g, 4, 32)
+    rows |= set(range(128)) | set(range(S.T - 128, S.T))
+    rest = np.setdiff1d(np.arange(S.T), np.array(sorted(rows)))
+    rows |= set(rng.choice(rest, max(0, 1024 - len(rows)), replace=False).tolist())
+    rows = sorted(rows)
+    assert len(rows) >= 1024
     h_ref = oracle.rmsnorm(Lt["x"][rows], L["gamma"], S.rms_eps, S.dtype)
     lg_ref = oracle.router_logits(h_ref, L["w_router"], L["router_bias"]).astype(np.float64)
     assert np.max(np.abs(g["logits"][rows].astype(np.float64) - lg_ref)) <= 2e-3
     ref = oracle_y(Lt, g, tg, tr, tokens=rows)
-    assert rel_l2(values(g["y"][rows]), ref["y"][rows]) <= TOL["bf16"]
+    check_y(values(g["y"][rows]), ref["y"][rows], "bf16")
 
 
 def test_router_variants_batch_invariant(qwen, dev):
@@ -344,12 +352,14 @@ def test_router_variants_batch_invariant(qwen, dev):
     assert np.max(np.abs(full["logits"][rows].astype(np.float64) - lg_ref)) <= 4e-3
 
 
+@pytest.mark.timeout(900)
 def test_glm45_air_shape_full_size(dev):
     """GLM-4.5-Air-shaped layer (H=4096, E=128, I=1408, top-8, bf16, T=4096,
     Zipf(1.1) router prior, lognormal(0,0.7) tables, 50% skip), drawn on the
     device, run in the bench configuration; thresholds from the oracle's own
-    quantile mapping; every token's routing and the dispatch checked, the
-    layer output on sampled tokens."""
+    quantile mapping; every token's routing, the dispatch and the layer
+    output of every token checked (the Zipf-heavy experts hold ~2100 rows,
+    so their m-tiles and ragged last tiles are all covered)."""
     from workloads.device import make_layer_device, to_host
     S = workloads.CONFIGS["glm45_air_shape"]
     P = make_layer_device(S, dev, seed=0)
@@ -362,9 +372,8 @@ def test_glm45_air_shape_full_size(dev):
     check_dispatch(S, g)
     skipped = int((~g["keep"]).sum())
     assert abs(skipped / (S.T * S.k) - 0.5) < 0.01
-    sample = [0, 1, 2, 255, 256, 1000, 2047, 2048, 3000, 4094, 4095]
-    ref = oracle_y(L, g, tg, tr, tokens=sample)
-    assert rel_l2(values(g["y"][sample]), ref["y"][sample]) <= TOL["bf16"]
+    ref = oracle_y(L, g, tg, tr)
+    check_y(values(g["y"]), ref["y"], "bf16")
     # Zipf prior: some experts receive no kept slot and are never read
     n_e = np.diff(g["offsets"].astype(np.int64))
     assert (n_e == 0).sum() > 0
@@ -385,10 +394,10 @@ def test_qwen3_decode_steps(qwen, dev, M):
     check_routing_shared_logits(Ld, g, tg, tr)
     check_dispatch(S, g)
     ref = oracle_y(Ld, g, tg, tr)
-    assert rel_l2(values(g["y"]), ref["y"]) <= TOL["bf16"]
+    check_y(values(g["y"]), ref["y"], "bf16")
     for path in PATHS:
         gp = gl.run(tg, tr, path=path)
-        assert rel_l2(values(gp["y"]), ref["y"]) <= TOL["bf16"]
+        check_y(values(gp["y"]), ref["y"], "bf16")
 
 
 # ---------------------------------------------------------------- fused small-batch forward
@@ -477,7 +486,7 @@ def test_stream_tiling_beyond_its_mtile_table(dev):
     assert int(np.sum((np.diff(off) + 15) // 16)) > 1024
     rows = [0, 1, 999, 2000, 3998, 3999]
     ref = oracle_y(L, g, 0.0, 0.0, tokens=rows)
-    assert rel_l2(values(g["y"][rows]), ref["y"][rows]) <= TOL["bf16"]
+    check_y(values(g["y"][rows]), ref["y"][rows], "bf16")
 
 
 @pytest.mark.parametrize("E,k", [(16, 4), (64, 8), (65, 8), (128, 8), (128, 16), (150, 6), (192, 16), (256, 8), (256, 1)])
@@ -586,7 +595,7 @@ def test_decode_expert_pool(qwen, dev, M, pool):
         assert np.array_equal(g["sorted_token"][:n], tok)
         assert np.array_equal(g["slot_pos"], pos)
         assert np.array_equal(g["sorted_gate"][:n].view(np.uint32), ref["gate"][tok, slot].view(np.uint32))
-        assert rel_l2(values(g["y"]), ref["y"]) <= TOL["bf16"]
+        check_y(values(g["y"]), ref["y"], "bf16")
         U = int((np.diff(off) > 0).sum())
         assert U <= max(pool, len(set(ref["idx"][:, 0].tolist())))
 

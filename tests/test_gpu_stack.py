@@ -31,7 +31,8 @@ import workloads
 from workloads.device import make_layer_device, make_tokens_device
 from workloads.torch_io import from_torch
 import token_adaptive_expert_amd as ace
-from gpu_util import oracle_thresholds, rel_l2, values
+from gpu_util import (check_dispatch, check_routing_shared_logits, check_y, heavy_tail_rows, oracle_thresholds,
+                      rel_l2, values)
 
 pytestmark = pytest.mark.gpu
 
@@ -104,6 +105,56 @@ def test_stack48_prefill_sampled_tokens(stack48):
     assert rel_l2(values(xL[SAMPLE]), refL) <= 0.1
     # the stack moved the tokens: the layers' outputs are not negligible
     assert rel_l2(refL, oracle.as_f64(x0_host[SAMPLE])) > 0.05
+
+
+@pytest.mark.timeout(900)
+def test_stack48_every_layer_grouped(stack48):
+    """Every one of the 48 layers on the grouped path, in the bench
+    configuration (T = 1024 prefill, packed weights and router), fed the GPU's
+    own residual stream x_l.  The oracle takes the same x_l and the GPU's
+    float32 logits: top-k, gates and skip mask bit-exact on all 1024 tokens
+    of every layer, the dispatch on layers 0, 23 and 47, and y_l (the layer
+    alone, without the residual) on at least 64 tokens per layer, including
+    every token in the last 16 rows of the three most loaded experts, within
+    1e-2 overall and 2e-2 per token."""
+    S, params, stack = stack48
+    tg, tr = layer0_thresholds(S, params)
+    T = S.T
+    bufs = stack.buffers(T)
+    alone = stack.layers[0].buffers(T)
+    rng = np.random.default_rng(48)
+    cur = params[0]["x"]
+    worst = 0.0
+    for l, lay in enumerate(stack.layers):
+        P = params[l]
+        print(f"[stack layer {l}]", flush=True)
+        lay.forward(cur, float(tg), float(tr), alone)                      # y_l
+        b = bufs[l % 2]
+        lay.forward(cur, float(tg), float(tr), b, residual=cur)            # x_{l+1}, as the stack runs it
+        torch.cuda.synchronize()
+        g = {n: from_torch(getattr(alone, n)) for n in ("logits", "topk_idx", "topk_gate", "keep", "offsets",
+                                                        "sorted_token", "sorted_gate", "slot_pos", "y")}
+        g["keep"] = g["keep"].astype(bool)
+        assert torch.equal(alone.keep, b.keep) and torch.equal(alone.offsets, b.offsets)
+        x_l = from_torch(cur)
+        L = {"shape": S, "x": x_l, "gamma": from_torch(P["gamma"]), "w_router": from_torch(P["w_router"]),
+             "router_bias": from_torch(P["router_bias"]), "a_gsp": from_torch(P["a_gsp"]),
+             "a_rcr": from_torch(P["a_rcr"])}
+        check_routing_shared_logits(L, g, tg, tr)
+        if l in (0, 23, 47):
+            check_dispatch(S, g)
+        rows = heavy_tail_rows(g, 3, 16) | {0, T - 1}
+        rest = np.setdiff1d(np.arange(T), np.array(sorted(rows)))
+        rows |= set(rng.choice(rest, max(64 - len(rows), 16), replace=False).tolist())
+        rows = sorted(rows)
+        assert len(rows) >= 64
+        r = oracle.moe_layer(x_l[rows], L["gamma"], L["w_router"], L["router_bias"], DeviceRows(P["w_gate"]),
+                             DeviceRows(P["w_up"]), DeviceRows(P["w_down"]), L["a_gsp"], L["a_rcr"], tg, tr, S.k,
+                             S.norm_topk, S.rms_eps, S.dtype, logits=g["logits"][rows])
+        assert np.array_equal(r["keep"], g["keep"][rows])
+        worst = max(worst, check_y(values(g["y"][rows]), r["y"], S.dtype, f"layer {l}"))
+        cur = b.y[:T]
+    print(f"worst per-token rel-L2 over the 48 layers: {worst:.3g}", flush=True)
 
 
 def test_stack48_shared_routing(stack48):

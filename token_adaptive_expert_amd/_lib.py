@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "ACE_OK", 1: "ACE_EINVAL", 2: "ACE_EUNSUPPORTED", 3: "ACE_EWO
 EXPORTS = ["moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_route_skip", "moe_dispatch",
            "moe_expert_forward", "moe_combine", "moe_calibrate_workspace_bytes", "moe_calibrate_thresholds",
            "moe_pack_weights", "moe_router_packed_bytes", "moe_pack_router", "moe_tables_workspace_bytes",
-           "moe_build_tables", "moe_forward", "moe_set_kernel_events"]
+           "moe_build_tables", "moe_forward", "moe_hbm_read_probe", "moe_set_kernel_events"]
 
 
 class AceMoeError(RuntimeError):
@@ -101,6 +101,8 @@ def load() -> ctypes.CDLL:
     lib.moe_forward.restype = ctypes.c_int
     lib.moe_forward.argtypes = [D, I32, P, P, P, P, P, P, P, P, F32, F32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                 P, SZ, P]
+    lib.moe_hbm_read_probe.restype = ctypes.c_int
+    lib.moe_hbm_read_probe.argtypes = [P, SZ, P, I32, P]
     lib.moe_set_kernel_events.restype = ctypes.c_int
     lib.moe_set_kernel_events.argtypes = [P, P]
     _lib = lib
@@ -220,6 +222,12 @@ def moe_forward(desc, path, x, gamma, w_router, router_bias, logits_in, logits_o
                               _ptr(topk_idx), _ptr(topk_gate), _ptr(keep), _ptr(expert_offsets), _ptr(sorted_token),
                               _ptr(sorted_gate), _ptr(slot_pos), _ptr(act), _ptr(slot_out), _ptr(y), _ptr(workspace),
                               int(nbytes), _stream(stream)), "moe_forward")
+
+
+def moe_hbm_read_probe(buf, sink, workgroups, nbytes=None, stream=None):
+    nbytes = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    _check(load().moe_hbm_read_probe(_ptr(buf), int(nbytes), _ptr(sink), int(workgroups), _stream(stream)),
+           "moe_hbm_read_probe")
 
 
 def moe_set_kernel_events(start, stop):

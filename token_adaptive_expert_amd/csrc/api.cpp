@@ -600,6 +600,21 @@ ace_status moe_build_tables(const ace_moe_desc* d, float eps, const float* gamma
   }
 }
 
+ace_status moe_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups, void* stream) {
+  try {
+    REQUIRE(buf);
+    REQUIRE(sink);
+    if (bytes % 16 != 0) return fail(ACE_EINVAL, "bytes=%zu is not a multiple of 16", bytes);
+    if (workgroups < 1 || workgroups > (1 << 20)) return fail(ACE_EINVAL, "workgroups=%d outside [1, 2^20]", workgroups);
+    if (bytes == 0) return ok();
+    hipError_t e = ace::launch_read_probe(buf, bytes, sink, workgroups, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("read probe launch", e);
+    return ok();
+  } catch (...) {
+    return fail(ACE_EHIP, "unexpected host exception in moe_hbm_read_probe");
+  }
+}
+
 ace_status moe_set_kernel_events(void* start, void* stop) {
   if ((start == nullptr) != (stop == nullptr)) return fail(ACE_EINVAL, "start and stop must both be set or both NULL");
   g_ev_start = static_cast<hipEvent_t>(start);

@@ -138,5 +138,8 @@ hipError_t launch_calibrate(CalibArgs a, void* workspace, hipStream_t s);
 size_t tables_workspace_bytes(int E, int H, int I, int dtype, bool minimum);
 // Uses the largest Gram batch that workspace_bytes holds.
 hipError_t launch_tables(int dtype, TablesArgs a, void* workspace, size_t workspace_bytes, hipStream_t s);
+// Streaming-read probe (measuring aid): reads bytes (a multiple of 16) of src,
+// writes one word per workgroup to sink.
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int workgroups, hipStream_t s);
 
 }  // namespace ace
