@@ -231,6 +231,42 @@ ace_status moe_forward(const ace_moe_desc* d, int32_t path, const void* x, const
                        size_t workspace_bytes, void* stream);
 
 /*
+ * moe_forward_static -- moe_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same arguments, results and kernels as moe_forward,
+ * except that the slot activations (act), the float32 slot outputs
+ * (slot_out) and the dispatch workspace live in a static device buffer of
+ * the library instead of caller memory.  Every output that moe_forward
+ * writes to caller memory (h_out, logits_out, topk_idx, topk_gate, keep,
+ * expert_offsets, sorted_token, sorted_gate, slot_pos, y) is written here
+ * too, bit-identical to moe_forward's.
+ *   - Limit: the call needs round256(T*k*I*dtype bytes) + round256(T*k*H*4)
+ *     + round256(dispatch workspace) <= ACE_STATIC_SCRATCH_BYTES (80 MiB;
+ *     e.g. T = 1024 at H = 2048, I = 768, k = 8 in bf16 fits, T = 2048 does
+ *     not).  Larger batches are rejected with ACE_EUNSUPPORTED before anything
+ *     is launched.
+ *   - The buffer is a file-scope __device__ array: each device that runs the
+ *     library holds its own 80 MiB copy until the process ends.  The first
+ *     call on a device (with a non-empty batch) looks its address up once
+ *     (hipGetSymbolAddress, a host query that allocates nothing); make that
+ *     first call outside graph capture.  The call itself never calls hipMalloc,
+ *     hipFree or any allocating routine.
+ *   - Every call on one device shares that device's buffer and it keeps the
+ *     last call's contents; nothing in it needs to start at zero (every
+ *     kernel writes the rows it later reads).  Calls that overlap on one
+ *     device (different streams or threads without ordering) race on the
+ *     buffer and give undefined results: serialise them.
+ */
+#define ACE_STATIC_SCRATCH_BYTES (80u << 20)
+ace_status moe_forward_static(const ace_moe_desc* d, int32_t path, const void* x, const float* gamma,
+                              const float* w_router, const float* router_bias, const float* logits_in,
+                              float* logits_out, const float* a_gsp, const float* a_rcr, float tau_gsp,
+                              float tau_rcr, const void* w_gate, const void* w_up, const void* w_down,
+                              const void* residual, void* h_out, int32_t* topk_idx, float* topk_gate, uint8_t* keep,
+                              int32_t* expert_offsets, int32_t* sorted_token, float* sorted_gate, int32_t* slot_pos,
+                              void* y, void* stream);
+
+/*
  * moe_calibrate_thresholds -- per-layer thresholds (tau_gsp, tau_rcr) by
  * quantile mapping (Efficiency Results, Table 6) for a target skip rate over
  * all T*k routed slots, matched to the given batch's own routing.

@@ -196,3 +196,29 @@ def test_forward_validates_before_launch():
     d0 = m.make_desc(0, 256, 16, 128, 4, "bf16")
     assert lib.moe_forward(ctypes.byref(d0), 0, f, f, f, None, None, f, f, f, 0.0, 0.0, f, f, f, None, f, f, f, f, f,
                            f, f, f, f, f, f, f, 1 << 20, None) == 0
+
+
+def test_forward_static_validates_and_bounds_its_scratch():
+    """moe_forward_static checks every argument and its scratch bound on the
+    host, before it looks up or touches the static device buffer."""
+    m, lib = _lib()
+    f = 0x1000
+    d = m.make_desc(4, 256, 16, 128, 4, "bf16")
+    st = lib.moe_forward_static(ctypes.byref(d), 0, f, f, f, None, None, f, f, f, 0.0, 0.0, f, f, f, None, f, f, f, f,
+                                f, f, f, f, None, None)
+    assert st == 1 and "y is NULL" in lib.moe_last_error().decode()
+    st = lib.moe_forward_static(ctypes.byref(d), 9, f, f, f, None, None, f, f, f, 0.0, 0.0, f, f, f, None, f, f, f, f,
+                                f, f, f, f, f, None)
+    assert st == 1 and "path=9" in lib.moe_last_error().decode()
+    # T = 1024 of the Qwen3-30B-A3B shape fits the 80 MiB buffer; T = 2048 does not
+    d = m.make_desc(2048, 2048, 128, 768, 8, "bf16")
+    st = lib.moe_forward_static(ctypes.byref(d), 0, f, f, f, None, None, f, f, f, 0.0, 0.0, f, f, f, None, f, f, f, f,
+                                f, f, f, f, f, None)
+    assert st == 2 and "static buffer" in lib.moe_last_error().decode()
+    hdr = re.search(r"#define ACE_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m.ACE_STATIC_SCRATCH_BYTES == int(hdr.group(1)) << int(hdr.group(2)) == 80 << 20
+    need_1024 = 8192 * 768 * 2 + 8192 * 2048 * 4 + 256
+    assert need_1024 <= m.ACE_STATIC_SCRATCH_BYTES < 2 * 8192 * 2048 * 4
+    d0 = m.make_desc(0, 256, 16, 128, 4, "bf16")
+    assert lib.moe_forward_static(ctypes.byref(d0), 0, f, f, f, None, None, f, f, f, 0.0, 0.0, f, f, f, None, f, f, f,
+                                  f, f, f, f, f, f, None) == 0

@@ -26,7 +26,9 @@ STATUS_NAMES = {0: "ACE_OK", 1: "ACE_EINVAL", 2: "ACE_EUNSUPPORTED", 3: "ACE_EWO
 EXPORTS = ["moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_route_skip", "moe_dispatch",
            "moe_expert_forward", "moe_combine", "moe_calibrate_workspace_bytes", "moe_calibrate_thresholds",
            "moe_pack_weights", "moe_router_packed_bytes", "moe_pack_router", "moe_tables_workspace_bytes",
-           "moe_build_tables", "moe_forward", "moe_hbm_read_probe", "moe_set_kernel_events"]
+           "moe_build_tables", "moe_forward", "moe_forward_static", "moe_hbm_read_probe", "moe_set_kernel_events"]
+
+ACE_STATIC_SCRATCH_BYTES = 80 << 20
 
 
 class AceMoeError(RuntimeError):
@@ -101,6 +103,9 @@ def load() -> ctypes.CDLL:
     lib.moe_forward.restype = ctypes.c_int
     lib.moe_forward.argtypes = [D, I32, P, P, P, P, P, P, P, P, F32, F32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                 P, SZ, P]
+    lib.moe_forward_static.restype = ctypes.c_int
+    lib.moe_forward_static.argtypes = [D, I32, P, P, P, P, P, P, P, P, F32, F32, P, P, P, P, P, P, P, P, P, P, P, P,
+                                       P, P]
     lib.moe_hbm_read_probe.restype = ctypes.c_int
     lib.moe_hbm_read_probe.argtypes = [P, SZ, P, I32, P]
     lib.moe_set_kernel_events.restype = ctypes.c_int
@@ -222,6 +227,17 @@ def moe_forward(desc, path, x, gamma, w_router, router_bias, logits_in, logits_o
                               _ptr(topk_idx), _ptr(topk_gate), _ptr(keep), _ptr(expert_offsets), _ptr(sorted_token),
                               _ptr(sorted_gate), _ptr(slot_pos), _ptr(act), _ptr(slot_out), _ptr(y), _ptr(workspace),
                               int(nbytes), _stream(stream)), "moe_forward")
+
+
+def moe_forward_static(desc, path, x, gamma, w_router, router_bias, logits_in, logits_out, a_gsp, a_rcr, tau_gsp,
+                       tau_rcr, w_gate, w_up, w_down, residual, h_out, topk_idx, topk_gate, keep, expert_offsets,
+                       sorted_token, sorted_gate, slot_pos, y, stream=None):
+    _check(load().moe_forward_static(ctypes.byref(desc), int(path), _ptr(x), _ptr(gamma), _ptr(w_router),
+                                     _ptr(router_bias), _ptr(logits_in), _ptr(logits_out), _ptr(a_gsp), _ptr(a_rcr),
+                                     float(tau_gsp), float(tau_rcr), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                     _ptr(residual), _ptr(h_out), _ptr(topk_idx), _ptr(topk_gate), _ptr(keep),
+                                     _ptr(expert_offsets), _ptr(sorted_token), _ptr(sorted_gate), _ptr(slot_pos),
+                                     _ptr(y), _stream(stream)), "moe_forward_static")
 
 
 def moe_hbm_read_probe(buf, sink, workgroups, nbytes=None, stream=None):

@@ -7,10 +7,19 @@
 #include <cstdarg>
 #include <cmath>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/ace_moe.h"
 #include "kernels.h"
+
+// Device scratch of moe_forward_static: the slot activations, the float32
+// slot outputs and the dispatch workspace of one call, for callers that
+// cannot allocate.  Each device that runs the library holds its own copy
+// until the process ends.  Host code must never pass `scratch` itself to a
+// kernel (on the host it names a stand-in, not device memory): it uses the
+// address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[ACE_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -114,6 +123,72 @@ static_assert(ACE_FUSED_TOKENS <= ace::FUSED_TMAX, "fused kernel: at most FUSED_
     if ((p) != nullptr && reinterpret_cast<uintptr_t>(p) % 16 != 0)                                  \
       return fail(ACE_EINVAL, "%s is not 16-byte aligned", #p);                                      \
   } while (0)
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept.
+ace_status static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  if (dev < 0 || dev >= kMaxDevices) return fail(ACE_EUNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail("hipGetSymbolAddress(scratch)", e);
+    if (p == nullptr || reinterpret_cast<uintptr_t>(p) % 256 != 0)
+      return fail(ACE_EHIP, "hipGetSymbolAddress(scratch) gave an unusable address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ACE_OK;
+}
+
+// Arguments of moe_forward other than its scratch (act, slot_out, workspace);
+// shared with moe_forward_static.  Every argument is checked before anything
+// is launched.
+ace_status check_forward_args(const ace_moe_desc* d, int32_t path, const void* x, const float* gamma,
+                              const float* w_router, const float* router_bias, const float* logits_in,
+                              const float* logits_out, const float* a_gsp, const float* a_rcr, float tau_gsp,
+                              float tau_rcr, const void* w_gate, const void* w_up, const void* w_down,
+                              const void* residual, const void* h_out, const int32_t* topk_idx,
+                              const float* topk_gate, const uint8_t* keep, const int32_t* expert_offsets,
+                              const int32_t* sorted_token, const float* sorted_gate, const int32_t* slot_pos,
+                              const void* y) {
+  ace_status st = check_desc(d);
+  if (st != ACE_OK) return st;
+  if (path < ACE_PATH_AUTO || path > ACE_PATH_STREAM) return fail(ACE_EINVAL, "path=%d is not an ace_path", path);
+  REQUIRE(x);
+  REQUIRE(gamma);
+  if (logits_in == nullptr) REQUIRE(w_router);
+  REQUIRE(logits_out);
+  if (logits_in == logits_out) return fail(ACE_EINVAL, "logits_in and logits_out must not alias");
+  ALIGNED_OR_NULL(router_bias);
+  ALIGNED_OR_NULL(logits_in);
+  ALIGNED_OR_NULL(residual);
+  REQUIRE(a_gsp);
+  REQUIRE(a_rcr);
+  REQUIRE(w_gate);
+  REQUIRE(w_up);
+  REQUIRE(w_down);
+  REQUIRE(h_out);
+  REQUIRE(topk_idx);
+  REQUIRE(topk_gate);
+  REQUIRE(keep);
+  REQUIRE(expert_offsets);
+  REQUIRE(sorted_token);
+  REQUIRE(sorted_gate);
+  REQUIRE(slot_pos);
+  REQUIRE(y);
+  if (!(tau_gsp >= 0.f) || !(tau_rcr >= 0.f))
+    return fail(ACE_EINVAL, "thresholds must be >= 0 (got %g, %g)", double(tau_gsp), double(tau_rcr));
+  return ACE_OK;
+}
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 }  // namespace
 
@@ -426,37 +501,13 @@ ace_status moe_forward(const ace_moe_desc* d, int32_t path, const void* x, const
                        int32_t* slot_pos, void* act, float* slot_out, void* y, void* workspace,
                        size_t workspace_bytes, void* stream) {
   try {
-    ace_status st = check_desc(d);
+    ace_status st = check_forward_args(d, path, x, gamma, w_router, router_bias, logits_in, logits_out, a_gsp, a_rcr,
+                                       tau_gsp, tau_rcr, w_gate, w_up, w_down, residual, h_out, topk_idx, topk_gate,
+                                       keep, expert_offsets, sorted_token, sorted_gate, slot_pos, y);
     if (st != ACE_OK) return st;
-    if (path < ACE_PATH_AUTO || path > ACE_PATH_STREAM) return fail(ACE_EINVAL, "path=%d is not an ace_path", path);
-    // every argument is checked before anything is launched
-    REQUIRE(x);
-    REQUIRE(gamma);
-    if (logits_in == nullptr) REQUIRE(w_router);
-    REQUIRE(logits_out);
-    if (logits_in == logits_out) return fail(ACE_EINVAL, "logits_in and logits_out must not alias");
-    ALIGNED_OR_NULL(router_bias);
-    ALIGNED_OR_NULL(logits_in);
-    ALIGNED_OR_NULL(residual);
-    REQUIRE(a_gsp);
-    REQUIRE(a_rcr);
-    REQUIRE(w_gate);
-    REQUIRE(w_up);
-    REQUIRE(w_down);
-    REQUIRE(h_out);
-    REQUIRE(topk_idx);
-    REQUIRE(topk_gate);
-    REQUIRE(keep);
-    REQUIRE(expert_offsets);
-    REQUIRE(sorted_token);
-    REQUIRE(sorted_gate);
-    REQUIRE(slot_pos);
     REQUIRE(act);
     REQUIRE(slot_out);
-    REQUIRE(y);
     REQUIRE(workspace);
-    if (!(tau_gsp >= 0.f) || !(tau_rcr >= 0.f))
-      return fail(ACE_EINVAL, "thresholds must be >= 0 (got %g, %g)", double(tau_gsp), double(tau_rcr));
     const size_t need = ace::dispatch_workspace_bytes(std::max(d->T, 1), d->E, d->k);
     if (workspace_bytes < need) return fail(ACE_EWORKSPACE, "workspace_bytes=%zu < %zu needed", workspace_bytes, need);
     if (d->T == 0) return ok();
@@ -551,6 +602,43 @@ ace_status moe_forward(const ace_moe_desc* d, int32_t path, const void* x, const
     return ok();
   } catch (...) {
     return fail(ACE_EHIP, "unexpected host exception in moe_forward");
+  }
+}
+
+ace_status moe_forward_static(const ace_moe_desc* d, int32_t path, const void* x, const float* gamma,
+                              const float* w_router, const float* router_bias, const float* logits_in,
+                              float* logits_out, const float* a_gsp, const float* a_rcr, float tau_gsp,
+                              float tau_rcr, const void* w_gate, const void* w_up, const void* w_down,
+                              const void* residual, void* h_out, int32_t* topk_idx, float* topk_gate, uint8_t* keep,
+                              int32_t* expert_offsets, int32_t* sorted_token, float* sorted_gate, int32_t* slot_pos,
+                              void* y, void* stream) {
+  try {
+    ace_status st = check_forward_args(d, path, x, gamma, w_router, router_bias, logits_in, logits_out, a_gsp, a_rcr,
+                                       tau_gsp, tau_rcr, w_gate, w_up, w_down, residual, h_out, topk_idx, topk_gate,
+                                       keep, expert_offsets, sorted_token, sorted_gate, slot_pos, y);
+    if (st != ACE_OK) return st;
+    const size_t es = d->dtype == ACE_BF16 ? 2 : 4;
+    const size_t rows = size_t(d->T) * size_t(d->k);
+    const size_t act_bytes = round256(rows * size_t(d->I) * es);
+    const size_t out_bytes = round256(rows * size_t(d->H) * 4);
+    const size_t ws_bytes = round256(ace::dispatch_workspace_bytes(std::max(d->T, 1), d->E, d->k));
+    const size_t need = act_bytes + out_bytes + ws_bytes;
+    if (need > size_t(ACE_STATIC_SCRATCH_BYTES))
+      return fail(ACE_EUNSUPPORTED,
+                  "moe_forward_static: T=%d needs %zu bytes of scratch (slot activations, slot outputs, dispatch "
+                  "workspace), more than the %zu of the static buffer; use moe_forward with caller memory",
+                  d->T, need, size_t(ACE_STATIC_SCRATCH_BYTES));
+    if (d->T == 0) return ok();
+    void* base = nullptr;
+    st = static_scratch(&base);
+    if (st != ACE_OK) return st;
+    unsigned char* b = static_cast<unsigned char*>(base);
+    return moe_forward(d, path, x, gamma, w_router, router_bias, logits_in, logits_out, a_gsp, a_rcr, tau_gsp,
+                       tau_rcr, w_gate, w_up, w_down, residual, h_out, topk_idx, topk_gate, keep, expert_offsets,
+                       sorted_token, sorted_gate, slot_pos, b, reinterpret_cast<float*>(b + act_bytes), y,
+                       b + act_bytes + out_bytes, ws_bytes, stream);
+  } catch (...) {
+    return fail(ACE_EHIP, "unexpected host exception in moe_forward_static");
   }
 }
 

@@ -145,6 +145,20 @@ class AceMoeLayer:
                          b.slot_out, b.y, b.workspace, None, stream)
         return b.y[:T]
 
+    def forward_static(self, x, tau_gsp, tau_rcr, b: LayerBuffers, path=_lib.ACE_PATH_AUTO, logits_in=None,
+                       residual=None, stream=None) -> torch.Tensor:
+        """The whole layer through moe_forward_static: the library's static
+        device scratch replaces b.act, b.slot_out and b.workspace (which are
+        left untouched); every other buffer of b receives its output."""
+        T = x.shape[0]
+        if b.T < T:
+            raise ValueError(f"buffers sized for {b.T} tokens, got {T}")
+        _lib.moe_forward_static(self.desc(T), path, x, self.gamma, self.w_router, self.router_bias, logits_in,
+                                b.logits, self.a_gsp, self.a_rcr, tau_gsp, tau_rcr, self.w_gate, self.w_up,
+                                self.w_down, residual, b.h, b.topk_idx, b.topk_gate, b.keep, b.offsets,
+                                b.sorted_token, b.sorted_gate, b.slot_pos, b.y, stream)
+        return b.y[:T]
+
     def forward_steps(self, x, tau_gsp, tau_rcr, b: LayerBuffers | None = None, path=_lib.ACE_PATH_AUTO,
                       logits_in=None, residual=None, stream=None) -> torch.Tensor:
         """The same layer through the four step calls."""
