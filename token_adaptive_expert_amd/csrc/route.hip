@@ -196,24 +196,32 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
   const int nki = w < nks ? (nks - 1 - w) / RW + 1 : 0;  // this wave's k-steps
   u32x4 pl[NBK][NCB][3];
   u32x4 px[NBK];
+  // Loads that some lanes skip are buffer loads whose skipped lanes get an
+  // offset past the buffer (they return zero and touch no memory), so no
+  // load sits in a divergent branch and each wait covers only the loads it
+  // needs.
+  constexpr int OOB = int(0x7FFFFFF0u);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, uint32_t(int64_t(a.T) * H * int(sizeof(T))));
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(wp, packed ? uint32_t(3 * plane_bytes) : 0u);
   auto issue = [&](int i0) {
 #pragma unroll
     for (int b = 0; b < NBK; ++b) {
       const int j = w + RW * min(i0 + b, nki - 1);
       px[b] = u32x4{0u, 0u, 0u, 0u};
-      if (!XL && tt < a.T) px[b] = ld16(xrow + j * KS + q * EPL);  // rows past the batch: no loads
+      if (!XL)  // rows past the batch: no loads
+        px[b] = buf_ld16(xr, tt < a.T && nki > 0 ? (tt * H + j * KS + q * EPL) * int(sizeof(T)) : OOB, 0);
 #pragma unroll
       for (int c = 0; c < NCB; ++c)
 #pragma unroll
-        for (int p = 0; p < 3; ++p) {
-          pl[b][c][p] = u32x4{0u, 0u, 0u, 0u};
-          if (lane_e) pl[b][c][p] = ld16(wp + p * plane_bytes + (int64_t(cb[c]) * nks + j) * 1024 + l * 16);
-        }
+        for (int p = 0; p < 3; ++p)
+          pl[b][c][p] = buf_ld16(pr, lane_e && nki > 0 ? int(p * plane_bytes + (int64_t(cb[c]) * nks + j) * 1024) + l * 16 : OOB, 0);
     }
   };
   constexpr int GQ = NARROW_HMAX / (RNTHR * 4);  // gamma quads per thread for the LDS copy
-  // one column block: gamma is copied to LDS once (read there by every k-step of the MFMA loop)
-  const bool gam_lds = NCB == 1 && packed;
+  // one column block (the small-batch variants, launched only with the
+  // pre-split router): gamma is copied to LDS once (read there by every
+  // k-step of the MFMA loop)
+  constexpr bool gam_lds = NCB == 1;
   // router bias of this thread's output (read after the last barrier)
   float bias_v = 0.f;
   if (do_router && a.bias != nullptr && threadIdx.x < TB * ECBW)
@@ -222,29 +230,44 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
   // inverse RMS: wave w owns token tok0 + w; a row is read 8 segments of
   // 64 lanes x 16 bytes at a time, all in flight together (segments past H
   // are not loaded), then the gamma quads for the LDS copy (one column block:
-  // H <= NARROW_HMAX).  The router plane loads go out only after the
-  // barrier: issued earlier they queue ahead of the row loads in the CU's
-  // vector-memory pipe and hold up the RMS (measured: about 1 us per decode
-  // layer).
+  // H <= NARROW_HMAX).  One column block with every k-step of a wave in one
+  // load batch (the decode variant): the router plane loads go out while the
+  // rows are in flight, but only after a bare barrier that follows every
+  // wave's row and gamma loads, so that they queue behind those in the CU's
+  // vector-memory pipe (planes issued first hold up the RMS); the RMS waits
+  // for the rows alone and the planes arrive during it.
+  // (XL: H <= 2048, so nks <= 64 = RW * NBK and every wave has at most NBK k-steps)
+  constexpr bool early_planes = NCB == 1 && XL;
   {
-    const T* row = x + int64_t(min(tok0 + w, a.T - 1)) * H;
-    const bool row_valid = tok0 + w < a.T;  // waves past the batch load no row
+    const int row_t = __builtin_amdgcn_readfirstlane(tok0 + w);
+    const bool row_valid = row_t < a.T;  // waves past the batch load no row
     constexpr int SEG = 64 * EPL;
-    constexpr int RSEG = 8;  // segments per batch (the per-lane sum runs over them in order)
+    // segments per batch (the per-lane sum runs over them in order); with
+    // the rows in LDS (H <= 2048) one batch of 4 covers the row
+    constexpr int RSEG = XL ? 4 : 8;
+    const __amdgpu_buffer_rsrc_t gr = make_rsrc(a.gamma, uint32_t(H * 4));
     float ss = 0.f;
     for (int j0 = 0; j0 < H; j0 += RSEG * SEG) {
       u32x4 v[RSEG];
 #pragma unroll
       for (int b = 0; b < RSEG; ++b) {
+        const int col = j0 + b * SEG + l * EPL;
         v[b] = u32x4{0u, 0u, 0u, 0u};
-        if (row_valid && j0 + b * SEG < H) v[b] = ld16(row + min(j0 + b * SEG + l * EPL, H - EPL));
+        if (row_valid && j0 + b * SEG < H)  // wave-uniform
+          v[b] = buf_ld16(xr, col < H ? (row_t * H + col) * int(sizeof(T)) : OOB, 0);
       }
       if (j0 == 0 && gam_lds) {
         f32x4 gq[GQ];
 #pragma unroll
         for (int i = 0; i < GQ; ++i) {
           const int h = (int(threadIdx.x) + i * RNTHR) * 4;
-          if (h < H) gq[i] = *reinterpret_cast<const f32x4*>(a.gamma + h);
+          gq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (__builtin_amdgcn_readfirstlane(h) < H)  // waves wholly past H load nothing
+            gq[i] = __builtin_bit_cast(f32x4, buf_ld16(gr, h < H ? h * 4 : OOB, 0));
+        }
+        if (early_planes) {
+          __builtin_amdgcn_s_barrier();  // every wave's row and gamma loads are issued
+          issue(0);                      // (waves without k-steps load nothing)
         }
 #pragma unroll
         for (int i = 0; i < GQ; ++i) {
@@ -268,7 +291,7 @@ __global__ __launch_bounds__(RNTHR) void norm_router_kernel(RouteArgs a) {
   if constexpr (sizeof(T) == 2) {
     if (packed) {
       for (int i0 = 0; i0 < nki; i0 += NBK) {
-        issue(i0);
+        if (!early_planes || i0 > 0) issue(i0);
 #pragma unroll
         for (int b = 0; b < NBK; ++b) {
           if (i0 + b < nki) {
