@@ -40,6 +40,24 @@ namespace {
 #ifndef ACE_BIG_RB
 #define ACE_BIG_RB 8          // 16-row blocks per tile for batches with >= 512 slots per expert
 #endif
+#ifndef ACE_BIG_NW
+#define ACE_BIG_NW 4          // waves per tile of that tier
+#endif
+#ifndef ACE_BIG_NGW
+#define ACE_BIG_NGW 4         // 16-row weight groups per wave of that tier (4 MFMAs per staged A fragment)
+#endif
+#ifndef ACE_BIG_CK
+#define ACE_BIG_CK 2          // k-steps per chunk of that tier (keeps its weight ring within 64 VGPRs)
+#endif
+#ifndef ACE_BIG_SLOTS
+#define ACE_BIG_SLOTS 256     // routed slots per expert (on average) from which the big tier is used
+#endif
+#ifndef ACE_MID_NGW
+#define ACE_MID_NGW 4         // weight groups per wave of the 64-row tier
+#endif
+#ifndef ACE_MID_CK
+#define ACE_MID_CK 2          // k-steps per chunk of the 64-row tier
+#endif
 #ifndef ACE_SMALL_RB_GATEUP
 #define ACE_SMALL_RB_GATEUP 3 // 16-row blocks per gate/up tile for moderate batches (<= 64 slots per expert)
 #endif
@@ -60,7 +78,6 @@ namespace {
 #define ACE_LDS_PITCH 272     // padded LDS row pitch of the staged slot rows
 #endif
 
-constexpr int ROWB = 256;        // bytes of one row per chunk
 constexpr int NXCD = 8;          // XCDs of an MI355X; only tile placement depends on it
 constexpr int EMAX_EXP = 256;    // largest expert count
 constexpr int LDS_PITCH = ACE_LDS_PITCH;
@@ -180,20 +197,27 @@ __device__ __forceinline__ void find_xcd_tile(int j, int x, int nbc, int E, cons
   rows = min(BM, s_off[e + 1] - row0);
 }
 
-template <typename T, int RB, int NW, int KIND, int STAGES>
+template <typename T, int RB, int NW, int KIND, int STAGES, int NGW = 2, int CK = 4>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(RB <= 3 ? 4 : (RB >= 16 ? 1 : (RB >= 8 ? 2 : ACE_WAVES_PER_EU)))))
 void expert_gemm_kernel(ExpertArgs a) {
+  static_assert(NGW % 2 == 0 && (CK == 2 || CK == 4), "weight groups per wave: even; k-steps per chunk: 2 or 4");
   constexpr int EPL = St<T>::EPL;
   constexpr int KS = 4 * EPL;      // k values per k-step
-  constexpr int KC = 4 * KS;       // k values per chunk
+  constexpr int KC = CK * KS;      // k values per chunk
+  constexpr int ROWBC = CK * 64;   // bytes of one staged row per chunk
+  constexpr int PITCH = CK == 4 ? LDS_PITCH : ROWBC + 16;  // padded LDS row pitch (no bank conflicts)
   constexpr int BM = 16 * RB;
   constexpr int NTHR = NW * 64;
-  constexpr int UNITS = BM * (ROWB / 16);   // 16-byte units of one staged chunk
+  constexpr int UNITS = BM * (ROWBC / 16);  // 16-byte units of one staged chunk
   constexpr int UPT = (UNITS + NTHR - 1) / NTHR;
-  constexpr int ROWS_PER_WG = (KIND == 0) ? NW * 16 : NW * 32;  // output columns per tile
+  // output columns per wave and per tile: gate/up, NGW/2 groups of 16
+  // intermediate units (their gate and their up rows); down, NGW groups of
+  // 16 output columns
+  constexpr int COLS_W = (KIND == 0) ? 8 * NGW : 16 * NGW;
+  constexpr int ROWS_PER_WG = NW * COLS_W;
 
-  __shared__ __attribute__((aligned(16))) uint8_t s_x[2][BM * LDS_PITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t s_x[2][BM * PITCH];
   __shared__ int32_t s_pref[257];
   __shared__ int32_t s_off[257];
 
@@ -240,25 +264,29 @@ void expert_gemm_kernel(ExpertArgs a) {
     // byte wv + ws[g] + j * wstep.  Linear layout: row n0 + l%16, k offset
     // (l/16)*EPL.  Packed layout: fragment j of the group is one contiguous
     // 1 KB block in lane order.  Both 16-row groups of a wave are uniform.
-    const int col0 = __builtin_amdgcn_readfirstlane((KIND == 0) ? nb * ROWS_PER_WG + w * 16
-                                                                : nb * ROWS_PER_WG + w * 32);
-    const int n0[2] = {col0, (KIND == 0) ? col0 : col0 + 16};
+    const int col0 = __builtin_amdgcn_readfirstlane(nb * ROWS_PER_WG + w * COLS_W);
+    // weight group g: gate/up, g < NGW/2 the gate rows of units col0 + 16g
+    // and g >= NGW/2 the up rows of the same units; down, the rows of output
+    // columns col0 + 16g
+    int n0[NGW];
+#pragma unroll
+    for (int g = 0; g < NGW; ++g) n0[g] = (KIND == 0) ? col0 + 16 * (g % (NGW / 2)) : col0 + 16 * g;
     const int64_t ebytes = int64_t(N) * K * int(sizeof(T));  // one expert's matrix
     const char* wm0 = reinterpret_cast<const char*>(a.W0) + int64_t(e) * ebytes;
     const char* wm1 = reinterpret_cast<const char*>((KIND == 0) ? a.W1 : a.W0) + int64_t(e) * ebytes;
     const __amdgpu_buffer_rsrc_t wr0 = make_rsrc(wm0, uint32_t(ebytes));
     const __amdgpu_buffer_rsrc_t wr1 = make_rsrc(wm1, uint32_t(ebytes));
-    int wv, ws[2], wstep;
+    int wv, ws[NGW], wstep;
     if (a.packed) {
       const int ksteps = K / KS;
       wv = l * 16;
 #pragma unroll
-      for (int g = 0; g < 2; ++g) ws[g] = (n0[g] / 16) * ksteps * 1024;
+      for (int g = 0; g < NGW; ++g) ws[g] = (n0[g] / 16) * ksteps * 1024;
       wstep = 1024;
     } else {
       wv = (r16 * K + q * EPL) * int(sizeof(T));
 #pragma unroll
-      for (int g = 0; g < 2; ++g) ws[g] = n0[g] * K * int(sizeof(T));
+      for (int g = 0; g < NGW; ++g) ws[g] = n0[g] * K * int(sizeof(T));
       wstep = KS * int(sizeof(T));
     }
 
@@ -266,13 +294,13 @@ void expert_gemm_kernel(ExpertArgs a) {
     // multiplied, the next STAGES-1 chunks are in flight.  The first chunks'
     // loads go out before the slot rows' sources are read (they depend only
     // on the tile), so the tile's start pays one memory latency, not two.
-    u32x4 wA[2][4], wB[2][4], wC[2][4];
-    auto load_w = [&](u32x4 (&dst)[2][4], int c) {
+    u32x4 wA[NGW][CK], wB[NGW][CK], wC[NGW][CK];
+    auto load_w = [&](u32x4 (&dst)[NGW][CK], int c) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        dst[0][s] = buf_ld16(wr0, wv, ws[0] + (c * 4 + s) * wstep);
-        dst[1][s] = buf_ld16(wr1, wv, ws[1] + (c * 4 + s) * wstep);
-      }
+      for (int s = 0; s < CK; ++s)
+#pragma unroll
+        for (int g = 0; g < NGW; ++g)
+          dst[g][s] = buf_ld16((KIND == 0 && g >= NGW / 2) ? wr1 : wr0, wv, ws[g] + (c * CK + s) * wstep);
     };
     load_w(wA, 0);
     if (STAGES == 3 && nch > 1) load_w(wB, 1);
@@ -287,16 +315,18 @@ void expert_gemm_kernel(ExpertArgs a) {
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const int unit = min(tid + u * NTHR, UNITS - 1);
-      const int r = unit >> 4, seg = unit & 15;
-      xoff[u] = r * LDS_PITCH + seg * 16;
+      const int r = unit / (ROWBC / 16), seg = unit % (ROWBC / 16);
+      xoff[u] = r * PITCH + seg * 16;
       const int rr = min(r, rows - 1);
       const int src_row = (KIND == 0) ? a.sorted_token[row0 + rr] : row0 + rr;
       xsrc[u] = src_row * K * int(sizeof(T)) + seg * 16;
     }
 
-    f32x4 acc[RB][2];
+    f32x4 acc[RB][NGW];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) acc[rb][0] = acc[rb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int g = 0; g < NGW; ++g) acc[rb][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     u32x4 xr[UPT];
     auto load_x = [&](int c) {
@@ -312,18 +342,17 @@ void expert_gemm_kernel(ExpertArgs a) {
     // One chunk.  Loads are issued X first, then weights: the X rows must land
     // before the barrier, and the in-order completion counter then lets the
     // weight loads of the later chunk stay in flight across it.
-    auto step = [&](u32x4 (&cur)[2][4], u32x4 (&ahead)[2][4], int c) {
+    auto step = [&](u32x4 (&cur)[NGW][CK], u32x4 (&ahead)[NGW][CK], int c) {
       if (c + 1 < nch) load_x(c + 1);
       if (c + STAGES - 1 < nch) load_w(ahead, c + STAGES - 1);
       const int buf = c & 1;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < CK; ++s) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          const u32x4 af =
-              *reinterpret_cast<const u32x4*>(&s_x[buf][(rb * 16 + r16) * LDS_PITCH + s * 64 + q * 16]);
-          acc[rb][0] = mma_step<T>(af, cur[0][s], acc[rb][0]);
-          acc[rb][1] = mma_step<T>(af, cur[1][s], acc[rb][1]);
+          const u32x4 af = *reinterpret_cast<const u32x4*>(&s_x[buf][(rb * 16 + r16) * PITCH + s * 64 + q * 16]);
+#pragma unroll
+          for (int g = 0; g < NGW; ++g) acc[rb][g] = mma_step<T>(af, cur[g][s], acc[rb][g]);
         }
       }
       if (c + 1 < nch) store_x(buf ^ 1);
@@ -356,13 +385,16 @@ void expert_gemm_kernel(ExpertArgs a) {
           if (r < rows) {
             const int64_t p = row0 + r;
             if (KIND == 0) {
-              const float v = silu(acc[rb][0][j]) * acc[rb][1][j];
-              reinterpret_cast<T*>(a.out)[p * N + col0 + r16] = St<T>::from_f32(v);
+#pragma unroll
+              for (int g = 0; g < NGW / 2; ++g) {
+                const float v = silu(acc[rb][g][j]) * acc[rb][g + NGW / 2][j];
+                reinterpret_cast<T*>(a.out)[p * N + col0 + 16 * g + r16] = St<T>::from_f32(v);
+              }
             } else {
-              const float g = a.sorted_gate[p];
+              const float gt = a.sorted_gate[p];
               float* o = reinterpret_cast<float*>(a.out) + p * N + col0 + r16;
-              o[0] = g * acc[rb][0][j];
-              o[16] = g * acc[rb][1][j];
+#pragma unroll
+              for (int g = 0; g < NGW; ++g) o[16 * g] = gt * acc[rb][g][j];
             }
           }
         }
@@ -780,10 +812,10 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const T* __restrict__
   st16(dst + u * EPL, ld16(src + row * K + k));
 }
 
-template <typename T, int RB, int NW, int KIND, int STAGES>
+template <typename T, int RB, int NW, int KIND, int STAGES, int NGW = 2, int CK = 4>
 hipError_t launch_one(const ExpertArgs& a, int ntok, int k, hipStream_t s) {
   constexpr int BM = 16 * RB;
-  constexpr int ROWS_PER_WG = (KIND == 0) ? NW * 16 : NW * 32;
+  constexpr int ROWS_PER_WG = (KIND == 0) ? NW * 8 * NGW : NW * 16 * NGW;
   const int64_t slots = int64_t(ntok) * k;
   const int64_t mt_bound = (slots + BM - 1) / BM + std::min<int64_t>(a.E, slots);
   const int64_t nbc = a.N / ROWS_PER_WG;
@@ -792,7 +824,8 @@ hipError_t launch_one(const ExpertArgs& a, int ntok, int k, hipStream_t s) {
   constexpr bool COLS = ACE_XCD_COLUMNS == 2 || (ACE_XCD_COLUMNS == 1 && KIND == 1);
   const int64_t per_xcd_bound = COLS ? (nbc + NXCD - 1) / NXCD * mt_bound : (mt_bound * nbc + NXCD - 1) / NXCD;
   const int64_t grid = std::max<int64_t>(NXCD, std::min<int64_t>(per_xcd_bound * NXCD, int64_t(1) << 30));
-  hipLaunchKernelGGL((expert_gemm_kernel<T, RB, NW, KIND, STAGES>), dim3(unsigned(grid)), dim3(NW * 64), 0, s, a);
+  hipLaunchKernelGGL((expert_gemm_kernel<T, RB, NW, KIND, STAGES, NGW, CK>), dim3(unsigned(grid)), dim3(NW * 64), 0, s,
+                     a);
   return hipGetLastError();
 }
 
@@ -839,18 +872,24 @@ hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs
   // 128-row tiles of 8 waves, which halve the L2 traffic per MFMA when the
   // GEMMs become compute-bound.  Between the two: 64-row tiles.
   const bool small_rb = int64_t(T) * k <= int64_t(64) * a.E && G > 2;
-  // (the 8-wave down tile covers 256 output columns: H must be a multiple of 256)
-  const bool big_rb = int64_t(T) * k >= int64_t(512) * a.E && a.N % (kind == 0 ? 128 : 256) == 0;
+  // (the big tile covers ACE_BIG_NW * 8 * ACE_BIG_NGW units or 16 * that many
+  // output columns: N must be a multiple)
+  const bool big_rb = int64_t(T) * k >= int64_t(ACE_BIG_SLOTS) * a.E &&
+                      a.N % ((kind == 0 ? 8 : 16) * ACE_BIG_NW * ACE_BIG_NGW) == 0;
   if (dtype == 1) {
     if (stream_path)
       return kind == 0 ? launch_splitk<bf16_t, 0>(a, T, k, num_cu, s) : launch_splitk<bf16_t, 1>(a, T, k, num_cu, s);
     constexpr int NG = ACE_GATEUP_NW, ND = ACE_DOWN_NW;
     if (big_rb)
-      return kind == 0 ? launch_one<bf16_t, ACE_BIG_RB, 8, 0, 2>(a, T, k, s)
-                       : launch_one<bf16_t, ACE_BIG_RB, 8, 1, 2>(a, T, k, s);
+      return kind == 0 ? launch_one<bf16_t, ACE_BIG_RB, ACE_BIG_NW, 0, 2, ACE_BIG_NGW, ACE_BIG_CK>(a, T, k, s)
+                       : launch_one<bf16_t, ACE_BIG_RB, ACE_BIG_NW, 1, 2, ACE_BIG_NGW, ACE_BIG_CK>(a, T, k, s);
     if (small_rb)
       return kind == 0 ? launch_one<bf16_t, ACE_SMALL_RB_GATEUP, NG, 0, S>(a, T, k, s)
                        : launch_one<bf16_t, ACE_SMALL_RB_DOWN, ND, 1, S>(a, T, k, s);
+    constexpr int MID_NGW = ACE_MID_NGW, MID_CK = ACE_MID_CK;
+    if (a.N % ((kind == 0 ? 8 : 16) * (kind == 0 ? NG : ND) * MID_NGW) == 0)
+      return kind == 0 ? launch_one<bf16_t, G, NG, 0, S, MID_NGW, MID_CK>(a, T, k, s)
+                       : launch_one<bf16_t, G, ND, 1, S, MID_NGW, MID_CK>(a, T, k, s);
     return kind == 0 ? launch_one<bf16_t, G, NG, 0, S>(a, T, k, s)
                      : launch_one<bf16_t, G, ND, 1, S>(a, T, k, s);
   }
