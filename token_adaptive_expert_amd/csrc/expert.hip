@@ -49,8 +49,26 @@ namespace {
 #ifndef ACE_BIG_CK
 #define ACE_BIG_CK 2          // k-steps per chunk of that tier (keeps its weight ring within 64 VGPRs)
 #endif
+#ifndef ACE_BIG_STAGES
+#define ACE_BIG_STAGES 2      // weight register ring depth of the big tier
+#endif
+#ifndef ACE_BIG_WPE
+#define ACE_BIG_WPE 0         // occupancy target of the big tier (0: from the tile height)
+#endif
 #ifndef ACE_BIG_SLOTS
 #define ACE_BIG_SLOTS 256     // routed slots per expert (on average) from which the big tier is used
+#endif
+#ifndef ACE_SMALL_NGW_GATEUP
+#define ACE_SMALL_NGW_GATEUP 2  // weight groups per wave of the small gate/up tier
+#endif
+#ifndef ACE_SMALL_CK_GATEUP
+#define ACE_SMALL_CK_GATEUP 4
+#endif
+#ifndef ACE_SMALL_NGW_DOWN
+#define ACE_SMALL_NGW_DOWN 2    // weight groups per wave of the small down tier
+#endif
+#ifndef ACE_SMALL_CK_DOWN
+#define ACE_SMALL_CK_DOWN 4
 #endif
 #ifndef ACE_MID_NGW
 #define ACE_MID_NGW 4         // weight groups per wave of the 64-row tier
@@ -197,9 +215,11 @@ __device__ __forceinline__ void find_xcd_tile(int j, int x, int nbc, int E, cons
   rows = min(BM, s_off[e + 1] - row0);
 }
 
-template <typename T, int RB, int NW, int KIND, int STAGES, int NGW = 2, int CK = 4>
+// WPE: occupancy target (waves per SIMD) given to the register allocator; 0
+// picks it from the tile height.
+template <typename T, int RB, int NW, int KIND, int STAGES, int NGW = 2, int CK = 4, int WPE = 0>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(RB <= 3 ? 4 : (RB >= 16 ? 1 : (RB >= 8 ? 2 : ACE_WAVES_PER_EU)))))
+__attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : (RB <= 3 ? 4 : (RB >= 16 ? 1 : (RB >= 8 ? 2 : ACE_WAVES_PER_EU))))))
 void expert_gemm_kernel(ExpertArgs a) {
   static_assert(NGW % 2 == 0 && (CK == 2 || CK == 4), "weight groups per wave: even; k-steps per chunk: 2 or 4");
   constexpr int EPL = St<T>::EPL;
@@ -812,7 +832,7 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const T* __restrict__
   st16(dst + u * EPL, ld16(src + row * K + k));
 }
 
-template <typename T, int RB, int NW, int KIND, int STAGES, int NGW = 2, int CK = 4>
+template <typename T, int RB, int NW, int KIND, int STAGES, int NGW = 2, int CK = 4, int WPE = 0>
 hipError_t launch_one(const ExpertArgs& a, int ntok, int k, hipStream_t s) {
   constexpr int BM = 16 * RB;
   constexpr int ROWS_PER_WG = (KIND == 0) ? NW * 8 * NGW : NW * 16 * NGW;
@@ -824,8 +844,8 @@ hipError_t launch_one(const ExpertArgs& a, int ntok, int k, hipStream_t s) {
   constexpr bool COLS = ACE_XCD_COLUMNS == 2 || (ACE_XCD_COLUMNS == 1 && KIND == 1);
   const int64_t per_xcd_bound = COLS ? (nbc + NXCD - 1) / NXCD * mt_bound : (mt_bound * nbc + NXCD - 1) / NXCD;
   const int64_t grid = std::max<int64_t>(NXCD, std::min<int64_t>(per_xcd_bound * NXCD, int64_t(1) << 30));
-  hipLaunchKernelGGL((expert_gemm_kernel<T, RB, NW, KIND, STAGES, NGW, CK>), dim3(unsigned(grid)), dim3(NW * 64), 0, s,
-                     a);
+  hipLaunchKernelGGL((expert_gemm_kernel<T, RB, NW, KIND, STAGES, NGW, CK, WPE>), dim3(unsigned(grid)), dim3(NW * 64),
+                     0, s, a);
   return hipGetLastError();
 }
 
@@ -881,8 +901,16 @@ hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs
       return kind == 0 ? launch_splitk<bf16_t, 0>(a, T, k, num_cu, s) : launch_splitk<bf16_t, 1>(a, T, k, num_cu, s);
     constexpr int NG = ACE_GATEUP_NW, ND = ACE_DOWN_NW;
     if (big_rb)
-      return kind == 0 ? launch_one<bf16_t, ACE_BIG_RB, ACE_BIG_NW, 0, 2, ACE_BIG_NGW, ACE_BIG_CK>(a, T, k, s)
-                       : launch_one<bf16_t, ACE_BIG_RB, ACE_BIG_NW, 1, 2, ACE_BIG_NGW, ACE_BIG_CK>(a, T, k, s);
+      return kind == 0
+                 ? launch_one<bf16_t, ACE_BIG_RB, ACE_BIG_NW, 0, ACE_BIG_STAGES, ACE_BIG_NGW, ACE_BIG_CK, ACE_BIG_WPE>(a, T,
+                                                                                                               k, s)
+                 : launch_one<bf16_t, ACE_BIG_RB, ACE_BIG_NW, 1, ACE_BIG_STAGES, ACE_BIG_NGW, ACE_BIG_CK, ACE_BIG_WPE>(a, T,
+                                                                                                               k, s);
+    constexpr int SG = ACE_SMALL_NGW_GATEUP, SGC = ACE_SMALL_CK_GATEUP;
+    constexpr int SD = ACE_SMALL_NGW_DOWN, SDC = ACE_SMALL_CK_DOWN;
+    if (small_rb && a.N % ((kind == 0 ? 8 * NG * SG : 16 * ND * SD)) == 0)
+      return kind == 0 ? launch_one<bf16_t, ACE_SMALL_RB_GATEUP, NG, 0, S, SG, SGC>(a, T, k, s)
+                       : launch_one<bf16_t, ACE_SMALL_RB_DOWN, ND, 1, S, SD, SDC>(a, T, k, s);
     if (small_rb)
       return kind == 0 ? launch_one<bf16_t, ACE_SMALL_RB_GATEUP, NG, 0, S>(a, T, k, s)
                        : launch_one<bf16_t, ACE_SMALL_RB_DOWN, ND, 1, S>(a, T, k, s);
