@@ -176,6 +176,27 @@ class Bench:
         return {"GBs": round(best, 1), "bytes": nbytes, "by_workgroups": by_grid,
                 "kernel": "moe_hbm_read_probe (read only, 16-byte loads, 8 in flight per thread)"}
 
+    def launch_floor(self, n=64, reps=20):
+        """Time per kernel of a HIP graph of n back-to-back launches of a
+        near-empty kernel (moe_hbm_read_probe on 16 bytes, one workgroup): the
+        fixed cost every dependent launch of a layer pays."""
+        torch, ace = self.torch, self.ace
+        buf = torch.zeros(4, dtype=torch.int32, device=self.dev)
+        sink = torch.empty(1, dtype=torch.int32, device=self.dev)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(n):
+                ace.moe_hbm_read_probe(buf, sink, 1)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                ace.moe_hbm_read_probe(buf, sink, 1)
+        ms = timed(torch, lambda i: g.replay(), reps, 3)
+        return round(ms * 1e3 / n, 3)
+
     def counts(self, bufs):
         off = bufs.offsets.cpu().numpy().astype(np.int64)
         n_e = np.diff(off)
@@ -706,6 +727,7 @@ def main():
     }
     res["hbm_copy_ceiling_GBs"] = round(B.copy_ceiling(), 1)
     res["hbm_read_ceiling"] = B.read_ceiling()
+    res["graph_launch_floor_us"] = B.launch_floor()
     if not args.no_sweep:
         sweep = {}
         for r in (0.0, 0.5):
