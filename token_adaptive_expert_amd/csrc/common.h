@@ -91,6 +91,15 @@ __device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, int voff, in
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// 16-byte buffer load straight into LDS (no registers): lane l's 16 bytes from
+// byte offset voff (per lane) + soff (uniform) land at lds + 16*l, lds being
+// wave-uniform.  Completion is counted by vmcnt like any vector memory load.
+// (A plain function, not a template, so that the host pass of a kernel
+// template that calls it still emits the kernel's launch stub.)
+__device__ __forceinline__ void buf_ld16_lds(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }

@@ -6,16 +6,18 @@
 // and scaled by its router gate.
 //
 // Work unit ("tile"): one expert, up to BM = 16*RB of its sorted slot rows,
-// and NW*32 of its weight rows.  Each wave owns 32 weight rows (two 16-row
-// groups): for gate/up the 16 gate rows and the 16 up rows of the same
-// intermediate units, so SiLU(gate)*up is formed in registers; for down two
-// adjacent groups of 16 output columns.  The contraction runs in chunks of
-// 256 bytes per row (4 k-steps of one 16-byte lane load each):
+// and NW*16*NGW of its weight rows.  Each wave owns NGW 16-row weight groups:
+// for gate/up the gate rows and the up rows of the same 8*NGW intermediate
+// units, so SiLU(gate)*up is formed in registers; for down NGW adjacent
+// groups of 16 output columns.  The contraction runs in chunks of CK k-steps
+// (one 16-byte lane load each, 64*CK bytes of a row):
 //   - weight fragments are loaded straight from HBM into registers in MFMA
 //     operand layout (each weight byte is read once per tile), one chunk
 //     ahead of the MFMAs;
 //   - the slot rows (gathered token rows of h, or act rows) are staged
-//     through LDS, double-buffered, and shared by all waves of the tile.
+//     through LDS and shared by all waves of the tile: through registers
+//     into two LDS buffers, or (128-row tiles) by direct-to-LDS buffer loads
+//     into a ring of three buffers, two chunks ahead of the MFMAs.
 // Every workgroup derives the tile list from expert_offsets (experts with no
 // kept slot produce no tile, so their weights are never read) and takes the
 // tile of its index.
@@ -54,6 +56,12 @@ namespace {
 #endif
 #ifndef ACE_BIG_WPE
 #define ACE_BIG_WPE 0         // occupancy target of the big tier (0: from the tile height)
+#endif
+#ifndef ACE_BIG_XB
+#define ACE_BIG_XB 3          // LDS buffers of the big tier's direct-to-LDS row staging (0: staged through registers)
+#endif
+#ifndef ACE_BIG_AF
+#define ACE_BIG_AF 2          // MFMA operand fragments per LDS read group of the direct-to-LDS staging
 #endif
 #ifndef ACE_BIG_SLOTS
 #define ACE_BIG_SLOTS 256     // routed slots per expert (on average) from which the big tier is used
@@ -215,9 +223,60 @@ __device__ __forceinline__ void find_xcd_tile(int j, int x, int nbc, int E, cons
   rows = min(BM, s_off[e + 1] - row0);
 }
 
+// s_waitcnt on the vector memory counter alone: vmcnt = N (6 bits: 3:0 and
+// 15:14), expcnt and lgkmcnt at their maxima (no wait).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// Workgroup barrier that orders LDS only: this wave's LDS operations
+// complete, then s_barrier.  Unlike __syncthreads() it does not wait for the
+// vector memory loads in flight (__syncthreads' fence waits for every
+// direct-to-LDS load, also those of later chunks); the caller waits for the
+// direct-to-LDS loads the next chunk needs before calling it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Compile-time loop: f(integral_constant<int, i>) for i = 0 .. N-1.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// LDS reads of MFMA operands staged by direct-to-LDS loads.  The compiler
+// cannot tell which LDS buffer a direct-to-LDS load writes, so before any LDS
+// read it issued itself it waits for every such load in flight (vmcnt(0)),
+// which would drain the staging ring each chunk.  These reads are issued from
+// inline assembly instead, each group waiting for its own data (lgkmcnt(0))
+// before the block ends; the caller has waited (vmcnt) for the loads that
+// filled the buffer and passed a barrier.  NR reads of 16 bytes at byte
+// addresses addr + OFF + i*STRIDE of LDS.
+template <int NR, int OFF, int STRIDE>
+__device__ __forceinline__ void lds_read_group(uint32_t addr, u32x4 (&v)[NR]) {
+  static_assert(NR == 1 || NR == 2 || NR == 4, "1, 2 or 4 reads per group");
+  static_assert(OFF >= 0 && OFF + (NR - 1) * STRIDE < 65536, "16-bit LDS offsets");
+  if constexpr (NR == 1) {
+    asm volatile("ds_read_b128 %0, %1 offset:%2\n\ts_waitcnt lgkmcnt(0)" : "=v"(v[0]) : "v"(addr), "i"(OFF));
+  } else if constexpr (NR == 2) {
+    asm volatile("ds_read_b128 %0, %2 offset:%3\n\tds_read_b128 %1, %2 offset:%4\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1])
+                 : "v"(addr), "i"(OFF), "i"(OFF + STRIDE));
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:%5\n\tds_read_b128 %1, %4 offset:%6\n\t"
+        "ds_read_b128 %2, %4 offset:%7\n\tds_read_b128 %3, %4 offset:%8\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(addr), "i"(OFF), "i"(OFF + STRIDE), "i"(OFF + 2 * STRIDE), "i"(OFF + 3 * STRIDE));
+  }
+}
+
 // WPE: occupancy target (waves per SIMD) given to the register allocator; 0
-// picks it from the tile height.
-template <typename T, int RB, int NW, int KIND, int STAGES, int NGW = 2, int CK = 4, int WPE = 0>
+// picks it from the tile height.  XB > 0: the slot rows are staged with
+// direct-to-LDS loads into XB buffers instead of through registers.
+template <typename T, int RB, int NW, int KIND, int STAGES, int NGW = 2, int CK = 4, int WPE = 0, int XB = 0>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : (RB <= 3 ? 4 : (RB >= 16 ? 1 : (RB >= 8 ? 2 : ACE_WAVES_PER_EU))))))
 void expert_gemm_kernel(ExpertArgs a) {
@@ -236,8 +295,14 @@ void expert_gemm_kernel(ExpertArgs a) {
   // 16 output columns
   constexpr int COLS_W = (KIND == 0) ? 8 * NGW : 16 * NGW;
   constexpr int ROWS_PER_WG = NW * COLS_W;
+  // direct-to-LDS staging (XB > 0): XB buffers of unpadded 128-byte rows
+  constexpr bool DMA = XB > 0;
+  static_assert(!DMA || (CK == 2 && XB >= 3 && STAGES == 2 && BM % (8 * NW) == 0),
+                "direct-to-LDS staging: 2 k-steps per chunk, 3+ buffers, 2 weight stages, whole 1 KB blocks per wave");
+  constexpr int NXB = DMA ? XB : 2;
+  constexpr int XBYTES = DMA ? BM * ROWBC : BM * PITCH;
 
-  __shared__ __attribute__((aligned(16))) uint8_t s_x[2][BM * PITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t s_x[NXB][XBYTES];
   __shared__ int32_t s_pref[257];
   __shared__ int32_t s_off[257];
 
@@ -325,73 +390,155 @@ void expert_gemm_kernel(ExpertArgs a) {
     load_w(wA, 0);
     if (STAGES == 3 && nch > 1) load_w(wB, 1);
 
-    // staged-row sources of this thread's units (byte offsets into A).  Rows
-    // past the tile's last slot row re-read that row: their MFMA output rows
-    // are never stored (an output row depends only on its own input row), and
-    // keeping every load unconditional keeps the loop body one block.
-    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.A, uint32_t(int64_t(a.A_rows) * K * int(sizeof(T))));
-    int xsrc[UPT];
-    int xoff[UPT];
-#pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int unit = min(tid + u * NTHR, UNITS - 1);
-      const int r = unit / (ROWBC / 16), seg = unit % (ROWBC / 16);
-      xoff[u] = r * PITCH + seg * 16;
-      const int rr = min(r, rows - 1);
-      const int src_row = (KIND == 0) ? a.sorted_token[row0 + rr] : row0 + rr;
-      xsrc[u] = src_row * K * int(sizeof(T)) + seg * 16;
-    }
-
     f32x4 acc[RB][NGW];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int g = 0; g < NGW; ++g) acc[rb][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 xr[UPT];
-    auto load_x = [&](int c) {
-      const int koff = c * KC * int(sizeof(T));
+    // Rows past the tile's last slot row re-read that row: their MFMA output
+    // rows are never stored (an output row depends only on its own input
+    // row), and keeping every load unconditional keeps the loop body one block.
+    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.A, uint32_t(int64_t(a.A_rows) * K * int(sizeof(T))));
+    if constexpr (DMA) {
+      // Direct-to-LDS staging.  A 16-byte buffer load with the LDS flag puts
+      // lane p's 16 bytes at a wave-uniform LDS base + 16p, so the chunk's
+      // rows go from memory to LDS without passing through registers, and
+      // XB - 1 chunks can be in flight.  Row R of a staged chunk is 128
+      // unpadded bytes at R*128, its 16-byte segment g in slot g ^ sw(R),
+      // sw(R) = (R & 7) ^ ((R >> 3) & 1): the 16 rows of one MFMA operand read
+      // then fall in distinct bank groups (for 8- and for 16-lane phases).
+      // Load j of wave w fills the 1 KB block b = j*NW + w (rows 8b..8b+7);
+      // lane p writes slot p%8 of row 8b + p/8 and so reads that row's
+      // segment (p%8) ^ sw.
+      constexpr int DPW = BM / 8 / NW;  // 1 KB blocks per wave and chunk
+      constexpr int NWL = NGW * CK;     // weight loads per wave and chunk
+      int dsrc[DPW];
 #pragma unroll
-      for (int u = 0; u < UPT; ++u) xr[u] = buf_ld16(xrs, xsrc[u], koff);
-    };
-    auto store_x = [&](int buf) {
-#pragma unroll
-      for (int u = 0; u < UPT; ++u)
-        if (UNITS % NTHR == 0 || tid + u * NTHR < UNITS) *reinterpret_cast<u32x4*>(&s_x[buf][xoff[u]]) = xr[u];
-    };
-    // One chunk.  Loads are issued X first, then weights: the X rows must land
-    // before the barrier, and the in-order completion counter then lets the
-    // weight loads of the later chunk stay in flight across it.
-    auto step = [&](u32x4 (&cur)[NGW][CK], u32x4 (&ahead)[NGW][CK], int c) {
-      if (c + 1 < nch) load_x(c + 1);
-      if (c + STAGES - 1 < nch) load_w(ahead, c + STAGES - 1);
-      const int buf = c & 1;
-#pragma unroll
-      for (int s = 0; s < CK; ++s) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const u32x4 af = *reinterpret_cast<const u32x4*>(&s_x[buf][(rb * 16 + r16) * PITCH + s * 64 + q * 16]);
-#pragma unroll
-          for (int g = 0; g < NGW; ++g) acc[rb][g] = mma_step<T>(af, cur[g][s], acc[rb][g]);
-        }
+      for (int j = 0; j < DPW; ++j) {
+        const int blk = j * NW + w;
+        const int r = 8 * blk + (l >> 3);
+        const int seg = (l & 7) ^ (l >> 3) ^ (blk & 1);
+        const int rr = min(r, rows - 1);
+        const int src_row = (KIND == 0) ? a.sorted_token[row0 + rr] : row0 + rr;
+        dsrc[j] = src_row * K * int(sizeof(T)) + seg * 16;
       }
-      if (c + 1 < nch) store_x(buf ^ 1);
-      __syncthreads();
-    };
-
-    load_x(0);
-    store_x(0);
-    __syncthreads();
-    if constexpr (STAGES == 3) {
-      for (int c = 0; c < nch; c += 3) {
-        step(wA, wC, c);
-        if (c + 1 < nch) step(wB, wA, c + 1);
-        if (c + 2 < nch) step(wC, wB, c + 2);
-      }
-    } else {
+      // stage chunk c into the buffer of step slot (slot % XB)
+      auto issue_x = [&](int c, int slot) {
+        uint8_t* dst = s_x[slot % XB] + w * 1024;
+#pragma unroll
+        for (int j = 0; j < DPW; ++j)
+          buf_ld16_lds(xrs, dst + j * NW * 1024, dsrc[j], c * KC * int(sizeof(T)));
+      };
+      // MFMA operand reads: row rb*16 + r16, k-step s of the chunk = segment
+      // 4s + q; AF fragments (row blocks) per read group
+      constexpr int AF = ACE_BIG_AF;
+      static_assert(RB % AF == 0, "row blocks per read group must divide the row blocks");
+      const uint32_t lds_base = uint32_t(uintptr_t((__attribute__((address_space(3))) uint8_t*)(&s_x[0][0])));
+      const int sw = (r16 & 7) ^ (r16 >> 3);
+      const uint32_t rd0 = uint32_t(r16 * ROWBC + ((q ^ sw) << 4));
+      const uint32_t rd1 = uint32_t(r16 * ROWBC + ((q ^ sw ^ 4) << 4));
+      // Every step loads one chunk of weights and stages one chunk of rows
+      // (past the last chunk: the last one again, a cache hit, into registers
+      // or a buffer no later step of the tile reads), so the loads this wave
+      // issues after chunk c + 1's rows are the same at every step: the
+      // weight loads and the staged rows of the XB - 2 steps that follow.
+      // The vector memory counter completes in issue order, so "chunk c + 1
+      // has landed" is "at most that many loads outstanding".  (The first
+      // step of a 4-deep ring has the prologue's last chunk in their place.)
+      auto step = [&](u32x4 (&cur)[NGW][CK], u32x4 (&ahead)[NGW][CK], int c) {
+        load_w(ahead, min(c + 1, nch - 1));
+        issue_x(min(c + XB - 1, nch - 1), c + XB - 1);
+        __builtin_amdgcn_sched_barrier(0);  // the loads go out before the MFMAs
+        const uint32_t xb = lds_base + uint32_t(c % XB) * XBYTES;
+        static_for<CK>([&](auto s) {
+          const uint32_t ad = xb + (s == 0 ? rd0 : rd1);
+          static_for<RB / AF>([&](auto i) {
+            u32x4 af[AF];
+            lds_read_group<AF, int(i) * AF * 16 * ROWBC, 16 * ROWBC>(ad, af);
+#pragma unroll
+            for (int f = 0; f < AF; ++f)
+#pragma unroll
+              for (int g = 0; g < NGW; ++g)
+                acc[int(i) * AF + f][g] = mma_step<T>(af[f], cur[g][int(s)], acc[int(i) * AF + f][g]);
+          });
+        });
+        if (XB >= 4 && c == 0)
+          wait_vmcnt<(XB - 3) * DPW + NWL + DPW>();
+        else
+          wait_vmcnt<(XB - 2) * (NWL + DPW)>();
+        lds_barrier();
+      };
+      for (int c = 0; c < XB - 1; ++c) issue_x(min(c, nch - 1), c);
+      wait_vmcnt<(XB - 2) * DPW>();
+      lds_barrier();
       for (int c = 0; c < nch; c += 2) {
         step(wA, wB, c);
         if (c + 1 < nch) step(wB, wA, c + 1);
+      }
+    } else {
+      // staged-row sources of this thread's units (byte offsets into A)
+      int xsrc[UPT];
+      int xoff[UPT];
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        const int unit = min(tid + u * NTHR, UNITS - 1);
+        const int r = unit / (ROWBC / 16), seg = unit % (ROWBC / 16);
+        xoff[u] = r * PITCH + seg * 16;
+        const int rr = min(r, rows - 1);
+        const int src_row = (KIND == 0) ? a.sorted_token[row0 + rr] : row0 + rr;
+        xsrc[u] = src_row * K * int(sizeof(T)) + seg * 16;
+      }
+
+      u32x4 xr[UPT];
+      auto load_x = [&](int c) {
+        const int koff = c * KC * int(sizeof(T));
+#pragma unroll
+        for (int u = 0; u < UPT; ++u) xr[u] = buf_ld16(xrs, xsrc[u], koff);
+      };
+      auto store_x = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < UPT; ++u)
+          if (UNITS % NTHR == 0 || tid + u * NTHR < UNITS) *reinterpret_cast<u32x4*>(&s_x[buf][xoff[u]]) = xr[u];
+      };
+      // One chunk.  Loads are issued X first, then weights: the X rows must land
+      // before the barrier, and the in-order completion counter then lets the
+      // weight loads of the later chunk stay in flight across it.  Every step
+      // issues both (past the last chunk: the last chunk again, a cache hit):
+      // with loads skipped on some paths the compiler's counter waits have to
+      // hold on every path and so drain the loads just issued.
+      auto step = [&](u32x4 (&cur)[NGW][CK], u32x4 (&ahead)[NGW][CK], int c) {
+        load_x(min(c + 1, nch - 1));
+        load_w(ahead, min(c + STAGES - 1, nch - 1));
+        __builtin_amdgcn_sched_barrier(0);  // the loads go out before the MFMAs
+        const int buf = c & 1;
+#pragma unroll
+        for (int s = 0; s < CK; ++s) {
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            const u32x4 af = *reinterpret_cast<const u32x4*>(&s_x[buf][(rb * 16 + r16) * PITCH + s * 64 + q * 16]);
+#pragma unroll
+            for (int g = 0; g < NGW; ++g) acc[rb][g] = mma_step<T>(af, cur[g][s], acc[rb][g]);
+          }
+        }
+        store_x(buf ^ 1);
+        __syncthreads();
+      };
+
+      load_x(0);
+      store_x(0);
+      __syncthreads();
+      if constexpr (STAGES == 3) {
+        for (int c = 0; c < nch; c += 3) {
+          step(wA, wC, c);
+          if (c + 1 < nch) step(wB, wA, c + 1);
+          if (c + 2 < nch) step(wC, wB, c + 2);
+        }
+      } else {
+        for (int c = 0; c < nch; c += 2) {
+          step(wA, wB, c);
+          if (c + 1 < nch) step(wB, wA, c + 1);
+        }
       }
     }
 
@@ -421,6 +568,8 @@ void expert_gemm_kernel(ExpertArgs a) {
       }
     }
   }
+  // the last steps' direct-to-LDS loads land before the workgroup's LDS is released
+  if constexpr (DMA) wait_vmcnt<0>();
 }
 
 // Small-batch ("stream") path: split-K inside the workgroup.  A tile is one
@@ -832,7 +981,7 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const T* __restrict__
   st16(dst + u * EPL, ld16(src + row * K + k));
 }
 
-template <typename T, int RB, int NW, int KIND, int STAGES, int NGW = 2, int CK = 4, int WPE = 0>
+template <typename T, int RB, int NW, int KIND, int STAGES, int NGW = 2, int CK = 4, int WPE = 0, int XB = 0>
 hipError_t launch_one(const ExpertArgs& a, int ntok, int k, hipStream_t s) {
   constexpr int BM = 16 * RB;
   constexpr int ROWS_PER_WG = (KIND == 0) ? NW * 8 * NGW : NW * 16 * NGW;
@@ -844,8 +993,8 @@ hipError_t launch_one(const ExpertArgs& a, int ntok, int k, hipStream_t s) {
   constexpr bool COLS = ACE_XCD_COLUMNS == 2 || (ACE_XCD_COLUMNS == 1 && KIND == 1);
   const int64_t per_xcd_bound = COLS ? (nbc + NXCD - 1) / NXCD * mt_bound : (mt_bound * nbc + NXCD - 1) / NXCD;
   const int64_t grid = std::max<int64_t>(NXCD, std::min<int64_t>(per_xcd_bound * NXCD, int64_t(1) << 30));
-  hipLaunchKernelGGL((expert_gemm_kernel<T, RB, NW, KIND, STAGES, NGW, CK, WPE>), dim3(unsigned(grid)), dim3(NW * 64),
-                     0, s, a);
+  hipLaunchKernelGGL((expert_gemm_kernel<T, RB, NW, KIND, STAGES, NGW, CK, WPE, XB>), dim3(unsigned(grid)),
+                     dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -902,10 +1051,10 @@ hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs
     constexpr int NG = ACE_GATEUP_NW, ND = ACE_DOWN_NW;
     if (big_rb)
       return kind == 0
-                 ? launch_one<bf16_t, ACE_BIG_RB, ACE_BIG_NW, 0, ACE_BIG_STAGES, ACE_BIG_NGW, ACE_BIG_CK, ACE_BIG_WPE>(a, T,
-                                                                                                               k, s)
-                 : launch_one<bf16_t, ACE_BIG_RB, ACE_BIG_NW, 1, ACE_BIG_STAGES, ACE_BIG_NGW, ACE_BIG_CK, ACE_BIG_WPE>(a, T,
-                                                                                                               k, s);
+                 ? launch_one<bf16_t, ACE_BIG_RB, ACE_BIG_NW, 0, ACE_BIG_STAGES, ACE_BIG_NGW, ACE_BIG_CK, ACE_BIG_WPE,
+                              ACE_BIG_XB>(a, T, k, s)
+                 : launch_one<bf16_t, ACE_BIG_RB, ACE_BIG_NW, 1, ACE_BIG_STAGES, ACE_BIG_NGW, ACE_BIG_CK, ACE_BIG_WPE,
+                              ACE_BIG_XB>(a, T, k, s);
     constexpr int SG = ACE_SMALL_NGW_GATEUP, SGC = ACE_SMALL_CK_GATEUP;
     constexpr int SD = ACE_SMALL_NGW_DOWN, SDC = ACE_SMALL_CK_DOWN;
     if (small_rb && a.N % ((kind == 0 ? 8 * NG * SG : 16 * ND * SD)) == 0)
