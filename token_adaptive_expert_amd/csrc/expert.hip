@@ -63,6 +63,10 @@ namespace {
 #ifndef ACE_BIG_AF
 #define ACE_BIG_AF 2          // MFMA operand fragments per LDS read group of the direct-to-LDS staging
 #endif
+#ifndef ACE_BIG_CCR
+#define ACE_BIG_CCR 1         // big gate/up tier: compiler-issued LDS reads from three separate arrays
+                              // (0: inline-assembly read groups from one ring, as the down projection)
+#endif
 #ifndef ACE_BIG_SLOTS
 #define ACE_BIG_SLOTS 256     // routed slots per expert (on average) from which the big tier is used
 #endif
@@ -237,6 +241,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 // direct-to-LDS loads the next chunk needs before calling it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Direct-to-LDS staging of one chunk by one wave: its DPW 1 KB blocks at
+// dst + j*NW KB from per-lane byte offsets src[j] + soff.
+template <int DPW, int NW>
+__device__ __forceinline__ void stage_rows(__amdgpu_buffer_rsrc_t r, uint8_t* dst, const int* src,
+                                           int soff) {
+#pragma unroll
+  for (int j = 0; j < DPW; ++j) buf_ld16_lds(r, dst + j * NW * 1024, src[j], soff);
+}
+// 16-byte LDS read issued by the compiler (it inserts the counter waits)
+__device__ __forceinline__ u32x4 lds_rd16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
 // Compile-time loop: f(integral_constant<int, i>) for i = 0 .. N-1.
 template <int N, int I = 0, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -297,12 +312,14 @@ void expert_gemm_kernel(ExpertArgs a) {
   constexpr int ROWS_PER_WG = NW * COLS_W;
   // direct-to-LDS staging (XB > 0): XB buffers of unpadded 128-byte rows
   constexpr bool DMA = XB > 0;
-  static_assert(!DMA || (CK == 2 && XB >= 3 && STAGES == 2 && BM % (8 * NW) == 0),
-                "direct-to-LDS staging: 2 k-steps per chunk, 3+ buffers, 2 weight stages, whole 1 KB blocks per wave");
+  static_assert(!DMA || (CK == 2 && XB >= 3 && BM % (8 * NW) == 0),
+                "direct-to-LDS staging: 2 k-steps per chunk, 3+ buffers, whole 1 KB blocks per wave");
   constexpr int NXB = DMA ? XB : 2;
   constexpr int XBYTES = DMA ? BM * ROWBC : BM * PITCH;
+  constexpr bool CCR = DMA && ACE_BIG_CCR && KIND == 0;
+  static_assert(!CCR || (XB == 3 && STAGES == 2), "compiler-issued reads: three buffers, two weight stages");
 
-  __shared__ __attribute__((aligned(16))) uint8_t s_x[NXB][XBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_x[CCR ? 1 : NXB][CCR ? 16 : XBYTES];
   __shared__ int32_t s_pref[257];
   __shared__ int32_t s_off[257];
 
@@ -388,7 +405,7 @@ void expert_gemm_kernel(ExpertArgs a) {
           dst[g][s] = buf_ld16((KIND == 0 && g >= NGW / 2) ? wr1 : wr0, wv, ws[g] + (c * CK + s) * wstep);
     };
     load_w(wA, 0);
-    if (STAGES == 3 && nch > 1) load_w(wB, 1);
+    if (STAGES == 3) load_w(wB, min(1, nch - 1));
 
     f32x4 acc[RB][NGW];
 #pragma unroll
@@ -403,14 +420,13 @@ void expert_gemm_kernel(ExpertArgs a) {
     if constexpr (DMA) {
       // Direct-to-LDS staging.  A 16-byte buffer load with the LDS flag puts
       // lane p's 16 bytes at a wave-uniform LDS base + 16p, so the chunk's
-      // rows go from memory to LDS without passing through registers, and
-      // XB - 1 chunks can be in flight.  Row R of a staged chunk is 128
-      // unpadded bytes at R*128, its 16-byte segment g in slot g ^ sw(R),
-      // sw(R) = (R & 7) ^ ((R >> 3) & 1): the 16 rows of one MFMA operand read
-      // then fall in distinct bank groups (for 8- and for 16-lane phases).
-      // Load j of wave w fills the 1 KB block b = j*NW + w (rows 8b..8b+7);
-      // lane p writes slot p%8 of row 8b + p/8 and so reads that row's
-      // segment (p%8) ^ sw.
+      // rows go from memory to LDS without passing through registers.  Row R
+      // of a staged chunk is 128 unpadded bytes at R*128, its 16-byte segment
+      // g in slot g ^ sw(R), sw(R) = (R & 7) ^ ((R >> 3) & 1): the 16 rows of
+      // one MFMA operand read then fall in distinct bank groups (for 8- and
+      // for 16-lane phases).  Load j of wave w fills the 1 KB block
+      // b = j*NW + w (rows 8b..8b+7); lane p writes slot p%8 of row 8b + p/8
+      // and so reads that row's segment (p%8) ^ sw.
       constexpr int DPW = BM / 8 / NW;  // 1 KB blocks per wave and chunk
       constexpr int NWL = NGW * CK;     // weight loads per wave and chunk
       int dsrc[DPW];
@@ -423,58 +439,126 @@ void expert_gemm_kernel(ExpertArgs a) {
         const int src_row = (KIND == 0) ? a.sorted_token[row0 + rr] : row0 + rr;
         dsrc[j] = src_row * K * int(sizeof(T)) + seg * 16;
       }
-      // stage chunk c into the buffer of step slot (slot % XB)
-      auto issue_x = [&](int c, int slot) {
-        uint8_t* dst = s_x[slot % XB] + w * 1024;
-#pragma unroll
-        for (int j = 0; j < DPW; ++j)
-          buf_ld16_lds(xrs, dst + j * NW * 1024, dsrc[j], c * KC * int(sizeof(T)));
-      };
-      // MFMA operand reads: row rb*16 + r16, k-step s of the chunk = segment
-      // 4s + q; AF fragments (row blocks) per read group
-      constexpr int AF = ACE_BIG_AF;
-      static_assert(RB % AF == 0, "row blocks per read group must divide the row blocks");
-      const uint32_t lds_base = uint32_t(uintptr_t((__attribute__((address_space(3))) uint8_t*)(&s_x[0][0])));
+      // MFMA operand reads: row rb*16 + r16, k-step s of the chunk = segment 4s + q
       const int sw = (r16 & 7) ^ (r16 >> 3);
-      const uint32_t rd0 = uint32_t(r16 * ROWBC + ((q ^ sw) << 4));
-      const uint32_t rd1 = uint32_t(r16 * ROWBC + ((q ^ sw ^ 4) << 4));
+      const int rd[2] = {r16 * ROWBC + ((q ^ sw) << 4), r16 * ROWBC + ((q ^ sw ^ 4) << 4)};
       // Every step loads one chunk of weights and stages one chunk of rows
       // (past the last chunk: the last one again, a cache hit, into registers
       // or a buffer no later step of the tile reads), so the loads this wave
-      // issues after chunk c + 1's rows are the same at every step: the
-      // weight loads and the staged rows of the XB - 2 steps that follow.
-      // The vector memory counter completes in issue order, so "chunk c + 1
-      // has landed" is "at most that many loads outstanding".  (The first
-      // step of a 4-deep ring has the prologue's last chunk in their place.)
-      auto step = [&](u32x4 (&cur)[NGW][CK], u32x4 (&ahead)[NGW][CK], int c) {
-        load_w(ahead, min(c + 1, nch - 1));
-        issue_x(min(c + XB - 1, nch - 1), c + XB - 1);
-        __builtin_amdgcn_sched_barrier(0);  // the loads go out before the MFMAs
-        const uint32_t xb = lds_base + uint32_t(c % XB) * XBYTES;
-        static_for<CK>([&](auto s) {
-          const uint32_t ad = xb + (s == 0 ? rd0 : rd1);
-          static_for<RB / AF>([&](auto i) {
-            u32x4 af[AF];
-            lds_read_group<AF, int(i) * AF * 16 * ROWBC, 16 * ROWBC>(ad, af);
+      // issues between two points are the same at every step.  The vector
+      // memory counter completes in issue order, so "chunk c + 1 has landed"
+      // is "at most the loads issued after it are outstanding".
+      if constexpr (CCR) {
+        // Three separate LDS arrays (each array's accesses carry their own
+        // alias scope, so the compiler can tell a read of one array from a
+        // load into another), the MFMA operands read by compiler-issued LDS
+        // loads one fragment ahead of their MFMAs.  The compiler waits
+        // before a chunk's first read for every direct-to-LDS load issued
+        // before that step, so rows are staged one chunk ahead (chunk c + 2
+        // is loaded during step c and waited for at the start of step c + 2,
+        // with chunk c + 1's rows landing meanwhile).
+        __shared__ __attribute__((aligned(16))) uint8_t s_r0[XBYTES];
+        __shared__ __attribute__((aligned(16))) uint8_t s_r1[XBYTES];
+        __shared__ __attribute__((aligned(16))) uint8_t s_r2[XBYTES];
+        auto buf = [&](auto b) -> uint8_t* {
+          if constexpr (int(b) == 0) return s_r0;
+          else if constexpr (int(b) == 1) return s_r1;
+          else return s_r2;
+        };
+        // step c: weights of chunk c + 1, rows of chunk c + 2 into array
+        // (B + 2) % 3, the MFMAs of chunk c from array B = c % 3
+        auto step = [&](auto B, u32x4 (&cur)[NGW][CK], u32x4 (&ahead)[NGW][CK], int c) {
+          load_w(ahead, min(c + 1, nch - 1));
+          stage_rows<DPW, NW>(xrs, buf(std::integral_constant<int, (int(B) + 2) % 3>{}) + w * 1024, dsrc,
+                              min(c + 2, nch - 1) * KC * int(sizeof(T)));
+          __builtin_amdgcn_sched_barrier(0);  // the loads go out before the MFMAs
+          const uint8_t* xb = buf(B);
+          constexpr int NF = CK * RB;  // operand fragments of the chunk, k-step major
+          u32x4 af[2];
+          af[0] = lds_rd16(xb + rd[0]);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // (groups: 0x100 LDS read, 0x008 MFMA)
+          static_for<NF>([&](auto f) {
+            constexpr int s = int(f) / RB, rb = int(f) % RB;
+            if constexpr (int(f) + 1 < NF)
+              af[(int(f) + 1) & 1] = lds_rd16(xb + ((int(f) + 1) % RB) * 16 * ROWBC + rd[(int(f) + 1) / RB]);
 #pragma unroll
-            for (int f = 0; f < AF; ++f)
-#pragma unroll
-              for (int g = 0; g < NGW; ++g)
-                acc[int(i) * AF + f][g] = mma_step<T>(af[f], cur[g][int(s)], acc[int(i) * AF + f][g]);
+            for (int g = 0; g < NGW; ++g) acc[rb][g] = mma_step<T>(af[int(f) & 1], cur[g][s], acc[rb][g]);
+            // in this order: the next fragment's read, then this fragment's MFMAs
+            if constexpr (int(f) + 1 < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NGW, 0);
           });
-        });
-        if (XB >= 4 && c == 0)
-          wait_vmcnt<(XB - 3) * DPW + NWL + DPW>();
-        else
-          wait_vmcnt<(XB - 2) * (NWL + DPW)>();
+          wait_vmcnt<NWL + DPW>();  // chunk c + 1's rows: only step c's loads may be outstanding
+          lds_barrier();
+        };
+        stage_rows<DPW, NW>(xrs, s_r0 + w * 1024, dsrc, 0);
+        stage_rows<DPW, NW>(xrs, s_r1 + w * 1024, dsrc, min(1, nch - 1) * KC * int(sizeof(T)));
+        wait_vmcnt<DPW>();
         lds_barrier();
-      };
-      for (int c = 0; c < XB - 1; ++c) issue_x(min(c, nch - 1), c);
-      wait_vmcnt<(XB - 2) * DPW>();
-      lds_barrier();
-      for (int c = 0; c < nch; c += 2) {
-        step(wA, wB, c);
-        if (c + 1 < nch) step(wB, wA, c + 1);
+        using B0 = std::integral_constant<int, 0>;
+        using B1 = std::integral_constant<int, 1>;
+        using B2 = std::integral_constant<int, 2>;
+        for (int c = 0; c < nch; c += 6) {  // array c % 3, weight ring c % 2
+          step(B0{}, wA, wB, c);
+          if (c + 1 < nch) step(B1{}, wB, wA, c + 1);
+          if (c + 2 < nch) step(B2{}, wA, wB, c + 2);
+          if (c + 3 < nch) step(B0{}, wB, wA, c + 3);
+          if (c + 4 < nch) step(B1{}, wA, wB, c + 4);
+          if (c + 5 < nch) step(B2{}, wB, wA, c + 5);
+        }
+      } else {
+        // A ring of XB buffers in one array, rows staged XB - 1 chunks ahead
+        // and the MFMA operands read by inline-assembly groups (the
+        // compiler cannot tell which buffer of the array a direct-to-LDS
+        // load writes, so before an LDS read of its own it would wait for
+        // every such load in flight).  At the end of step c, chunk c + 1's
+        // rows have landed once only the loads of the XB - 2 later steps
+        // (weights, rows) are outstanding; for the first step of a 4-deep
+        // ring, the prologue's last chunk stands in for one of them.
+        constexpr int AF = ACE_BIG_AF;
+        static_assert(RB % AF == 0, "row blocks per read group must divide the row blocks");
+        const uint32_t lds_base = uint32_t(uintptr_t((__attribute__((address_space(3))) uint8_t*)(&s_x[0][0])));
+        // stage chunk c into the buffer of step slot (slot % XB)
+        auto issue_x = [&](int c, int slot) {
+          stage_rows<DPW, NW>(xrs, s_x[slot % XB] + w * 1024, dsrc, c * KC * int(sizeof(T)));
+        };
+        auto step = [&](u32x4 (&cur)[NGW][CK], u32x4 (&ahead)[NGW][CK], int c) {
+          load_w(ahead, min(c + STAGES - 1, nch - 1));
+          issue_x(min(c + XB - 1, nch - 1), c + XB - 1);
+          __builtin_amdgcn_sched_barrier(0);  // the loads go out before the MFMAs
+          const uint32_t xb = lds_base + uint32_t(c % XB) * XBYTES;
+          static_for<CK>([&](auto s) {
+            const uint32_t ad = xb + uint32_t(rd[int(s)]);
+            static_for<RB / AF>([&](auto i) {
+              u32x4 af[AF];
+              lds_read_group<AF, int(i) * AF * 16 * ROWBC, 16 * ROWBC>(ad, af);
+#pragma unroll
+              for (int f = 0; f < AF; ++f)
+#pragma unroll
+                for (int g = 0; g < NGW; ++g)
+                  acc[int(i) * AF + f][g] = mma_step<T>(af[f], cur[g][int(s)], acc[int(i) * AF + f][g]);
+            });
+          });
+          if (XB >= 4 && c == 0)
+            wait_vmcnt<(XB - 3) * DPW + NWL + DPW>();
+          else
+            wait_vmcnt<(XB - 2) * (NWL + DPW)>();
+          lds_barrier();
+        };
+        for (int c = 0; c < XB - 1; ++c) issue_x(min(c, nch - 1), c);
+        wait_vmcnt<(XB - 2) * DPW>();
+        lds_barrier();
+        if constexpr (STAGES == 3) {
+          for (int c = 0; c < nch; c += 3) {
+            step(wA, wC, c);
+            if (c + 1 < nch) step(wB, wA, c + 1);
+            if (c + 2 < nch) step(wC, wB, c + 2);
+          }
+        } else {
+          for (int c = 0; c < nch; c += 2) {
+            step(wA, wB, c);
+            if (c + 1 < nch) step(wB, wA, c + 1);
+          }
+        }
       }
     } else {
       // staged-row sources of this thread's units (byte offsets into A)
@@ -1072,8 +1156,9 @@ hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs
   }
   if (stream_path)
     return kind == 0 ? launch_splitk<float, 0>(a, T, k, num_cu, s) : launch_splitk<float, 1>(a, T, k, num_cu, s);
-  return kind == 0 ? launch_one<float, G, 4, 0, S>(a, T, k, s)
-                   : launch_one<float, G, 4, 1, S>(a, T, k, s);
+  // (float32 layers: two waves per SIMD, so the tile's registers fit without spilling)
+  return kind == 0 ? launch_one<float, G, 4, 0, S, 2, 4, 2>(a, T, k, s)
+                   : launch_one<float, G, 4, 1, S, 2, 4, 2>(a, T, k, s);
 }
 
 }  // namespace ace
