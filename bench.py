@@ -683,13 +683,13 @@ def main():
     # dominant kernel: grouped gate/up GEMM (+SiLU).  Algorithmic bytes per
     # launch: the active experts' gate and up weights and the token rows; the
     # act rows it writes are implementation traffic.  Down: the active
-    # experts' down weights only (act read and float32 slot rows written are
+    # experts' down weights only (act read and bf16 slot rows written are
     # implementation traffic; y is written by the combine).
     gu_bytes = head["U"] * 2 * S.H * S.I * 2 + T * S.H * 2
     gu_impl = head["n_kept"] * S.I * 2
     gu_gbs = gu_bytes / (head["gateup_ms"] * 1e-3) / 1e9
     dn_bytes = head["U"] * S.H * S.I * 2
-    dn_impl = head["n_kept"] * (S.I * 2 + S.H * 4)
+    dn_impl = head["n_kept"] * (S.I * 2 + S.H * 2)
     layer_bytes = head["U"] * 3 * S.H * S.I * 2 + S.E * S.H * 4 + T * S.H * 4 + 8 * S.E
     layer_flops = head["n_kept"] * 6 * S.H * S.I + 2 * T * S.H * S.E
     res = {

@@ -15,9 +15,9 @@
  *     rejected with ACE_EINVAL naming it.
  *     The library never allocates, frees or synchronises; every call only
  *     enqueues kernels on `stream` (a hipStream_t, NULL = default stream).
- *   - Activations (x, h, act, y) and expert weights use desc->dtype
- *     (ACE_F32: float, ACE_BF16: bf16 bit patterns, 2 bytes).  Router
- *     weights, logits, gates, tables and slot outputs are float32.
+ *   - Activations (x, h, act, slot outputs, y) and expert weights use
+ *     desc->dtype (ACE_F32: float, ACE_BF16: bf16 bit patterns, 2 bytes).
+ *     Router weights, logits, gates and tables are float32.
  *   - Expert weights follow the nn.Linear layout (out x in, K contiguous):
  *     w_gate, w_up: [E, I, H]; w_down: [E, H, I].  The page's H x I matrix
  *     W^gate is w_gate[e] transposed.
@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define ACE_MOE_ABI_VERSION 2
+#define ACE_MOE_ABI_VERSION 3
 
 typedef enum {
   ACE_OK = 0,
@@ -178,16 +178,17 @@ ace_status moe_dispatch(const ace_moe_desc* d, const int32_t* topk_idx, const fl
  * equation f, Theoretical Foundation), gate-weighted.  For sorted row p of
  * expert e with token t = sorted_token[p]:
  *   act[p]      = SiLU(h[t] . w_gate[e]^T) * (h[t] . w_up[e]^T)   (dtype)
- *   slot_out[p] = sorted_gate[p] * (act[p] . w_down[e]^T)          (float32)
+ *   slot_out[p] = sorted_gate[p] * (act[p] . w_down[e]^T)          (dtype)
+ * Both are accumulated in float32 and rounded once to dtype on store.
  * Only rows p < expert_offsets[E] are written; only experts with at least
  * one kept slot have their weights read.
  * In:  h [T,H] dtype (from moe_route_skip); weights as above.
- * Out: act [T*k, I] dtype (scratch rows); slot_out [T*k, H] f32.
+ * Out: act [T*k, I] dtype (scratch rows); slot_out [T*k, H] dtype.
  * workspace: >= moe_workspace_bytes(d) bytes.
  */
 ace_status moe_expert_forward(const ace_moe_desc* d, int32_t path, const void* h, const void* w_gate,
                               const void* w_up, const void* w_down, const int32_t* expert_offsets,
-                              const int32_t* sorted_token, const float* sorted_gate, void* act, float* slot_out,
+                              const int32_t* sorted_token, const float* sorted_gate, void* act, void* slot_out,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -204,11 +205,11 @@ ace_status moe_expert_forward(const ace_moe_desc* d, int32_t path, const void* h
  * residual is not part of the layer (the pages define none); it lets a stack
  * of layers add x_{l+1} = x_l + y_l in the same pass.
  * In:  slot_pos [T*k] i32 (row-major [T,k], -1 = skipped, as moe_dispatch
- *      writes it); slot_out [T*k, H] f32; residual [T,H] dtype or NULL (may
+ *      writes it); slot_out [T*k, H] dtype; residual [T,H] dtype or NULL (may
  *      equal y: each element is read before it is written).
  * Out: y [T,H] dtype.
  */
-ace_status moe_combine(const ace_moe_desc* d, const int32_t* slot_pos, const float* slot_out, const void* residual,
+ace_status moe_combine(const ace_moe_desc* d, const int32_t* slot_pos, const void* slot_out, const void* residual,
                        void* y, void* stream);
 
 /*
@@ -227,23 +228,23 @@ ace_status moe_forward(const ace_moe_desc* d, int32_t path, const void* x, const
                        const float* a_rcr, float tau_gsp, float tau_rcr, const void* w_gate, const void* w_up,
                        const void* w_down, const void* residual, void* h_out, int32_t* topk_idx, float* topk_gate,
                        uint8_t* keep, int32_t* expert_offsets, int32_t* sorted_token, float* sorted_gate,
-                       int32_t* slot_pos, void* act, float* slot_out, void* y, void* workspace,
+                       int32_t* slot_pos, void* act, void* slot_out, void* y, void* workspace,
                        size_t workspace_bytes, void* stream);
 
 /*
  * moe_forward_static -- moe_forward for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid allocation): the same arguments, results and kernels as moe_forward,
- * except that the slot activations (act), the float32 slot outputs
- * (slot_out) and the dispatch workspace live in a static device buffer of
+ * except that the slot activations (act), the slot outputs (slot_out) and
+ * the dispatch workspace live in a static device buffer of
  * the library instead of caller memory.  Every output that moe_forward
  * writes to caller memory (h_out, logits_out, topk_idx, topk_gate, keep,
  * expert_offsets, sorted_token, sorted_gate, slot_pos, y) is written here
  * too, bit-identical to moe_forward's.
- *   - Limit: the call needs round256(T*k*I*dtype bytes) + round256(T*k*H*4)
- *     + round256(dispatch workspace) <= ACE_STATIC_SCRATCH_BYTES (80 MiB;
- *     e.g. T = 1024 at H = 2048, I = 768, k = 8 in bf16 fits, T = 2048 does
- *     not).  Larger batches are rejected with ACE_EUNSUPPORTED before anything
+ *   - Limit: the call needs round256(T*k*I*dtype bytes) +
+ *     round256(T*k*H*dtype bytes) + round256(dispatch workspace) <=
+ *     ACE_STATIC_SCRATCH_BYTES (80 MiB; e.g. T = 1024 and T = 1536 at
+ *     H = 2048, I = 768, k = 8 in bf16 fit, T = 2048 does not).  Larger batches are rejected with ACE_EUNSUPPORTED before anything
  *     is launched.
  *   - The buffer is a file-scope __device__ array: each device that runs the
  *     library holds its own 80 MiB copy until the process ends.  The first

@@ -35,7 +35,8 @@ def test_library_exports_every_declared_symbol():
     for f in header_functions():
         assert hasattr(lib, f), f
     assert set(header_functions()) <= set(m._lib.EXPORTS)
-    assert m.moe_abi_version() == 2
+    version = re.search(r"#define ACE_MOE_ABI_VERSION (\d+)", open(HEADER).read())
+    assert m.moe_abi_version() == int(version.group(1)) == m._lib.ABI_VERSION
 
 
 def test_desc_layout_matches_header():

@@ -51,7 +51,7 @@ def check_slot_outputs(L, g, ref, dtype):
     rows, refs = [], []
     for (t, i), o in ref["slot_out"].items():
         p = g["slot_pos"][t, i]
-        rows.append(g["slot_out"][p])
+        rows.append(values(g["slot_out"][p]))
         refs.append(o)
     if rows:
         check_y(np.stack(rows), np.stack(refs), dtype, "slot_out")

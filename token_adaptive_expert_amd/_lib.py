@@ -59,6 +59,7 @@ def make_desc(T, H, E, I, k, dtype, norm_topk=1, fusion="max", rms_eps=1e-6, wei
                    int(weight_layout), int(router_layout), int(expert_pool))
 
 
+ABI_VERSION = 3  # ACE_MOE_ABI_VERSION of include/ace_moe.h that these bindings follow
 _lib = None
 
 
@@ -74,6 +75,9 @@ def load() -> ctypes.CDLL:
     D = ctypes.POINTER(MoeDesc)
     lib.moe_abi_version.restype = ctypes.c_int
     lib.moe_abi_version.argtypes = []
+    if lib.moe_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {lib.moe_abi_version()}, these bindings need {ABI_VERSION}: "
+                          "rebuild it with `python -m token_adaptive_expert_amd.build`")
     lib.moe_last_error.restype = ctypes.c_char_p
     lib.moe_last_error.argtypes = []
     lib.moe_workspace_bytes.restype = SZ

@@ -298,7 +298,7 @@ ace_status moe_dispatch(const ace_moe_desc* d, const int32_t* topk_idx, const fl
 
 ace_status moe_expert_forward(const ace_moe_desc* d, int32_t path, const void* h, const void* w_gate,
                               const void* w_up, const void* w_down, const int32_t* expert_offsets,
-                              const int32_t* sorted_token, const float* sorted_gate, void* act, float* slot_out,
+                              const int32_t* sorted_token, const float* sorted_gate, void* act, void* slot_out,
                               void* workspace, size_t workspace_bytes, void* stream) {
   try {
     ace_status st = check_desc(d);
@@ -375,7 +375,7 @@ ace_status moe_expert_forward(const ace_moe_desc* d, int32_t path, const void* h
   }
 }
 
-ace_status moe_combine(const ace_moe_desc* d, const int32_t* slot_pos, const float* slot_out, const void* residual,
+ace_status moe_combine(const ace_moe_desc* d, const int32_t* slot_pos, const void* slot_out, const void* residual,
                        void* y, void* stream) {
   try {
     ace_status st = check_desc(d);
@@ -498,7 +498,7 @@ ace_status moe_forward(const ace_moe_desc* d, int32_t path, const void* x, const
                        const float* a_rcr, float tau_gsp, float tau_rcr, const void* w_gate, const void* w_up,
                        const void* w_down, const void* residual, void* h_out, int32_t* topk_idx, float* topk_gate,
                        uint8_t* keep, int32_t* expert_offsets, int32_t* sorted_token, float* sorted_gate,
-                       int32_t* slot_pos, void* act, float* slot_out, void* y, void* workspace,
+                       int32_t* slot_pos, void* act, void* slot_out, void* y, void* workspace,
                        size_t workspace_bytes, void* stream) {
   try {
     ace_status st = check_forward_args(d, path, x, gamma, w_router, router_bias, logits_in, logits_out, a_gsp, a_rcr,
@@ -620,7 +620,7 @@ ace_status moe_forward_static(const ace_moe_desc* d, int32_t path, const void* x
     const size_t es = d->dtype == ACE_BF16 ? 2 : 4;
     const size_t rows = size_t(d->T) * size_t(d->k);
     const size_t act_bytes = round256(rows * size_t(d->I) * es);
-    const size_t out_bytes = round256(rows * size_t(d->H) * 4);
+    const size_t out_bytes = round256(rows * size_t(d->H) * es);
     const size_t ws_bytes = round256(ace::dispatch_workspace_bytes(std::max(d->T, 1), d->E, d->k));
     const size_t need = act_bytes + out_bytes + ws_bytes;
     if (need > size_t(ACE_STATIC_SCRATCH_BYTES))
@@ -635,7 +635,7 @@ ace_status moe_forward_static(const ace_moe_desc* d, int32_t path, const void* x
     unsigned char* b = static_cast<unsigned char*>(base);
     return moe_forward(d, path, x, gamma, w_router, router_bias, logits_in, logits_out, a_gsp, a_rcr, tau_gsp,
                        tau_rcr, w_gate, w_up, w_down, residual, h_out, topk_idx, topk_gate, keep, expert_offsets,
-                       sorted_token, sorted_gate, slot_pos, b, reinterpret_cast<float*>(b + act_bytes), y,
+                       sorted_token, sorted_gate, slot_pos, b, b + act_bytes, y,
                        b + act_bytes + out_bytes, ws_bytes, stream);
   } catch (...) {
     return fail(ACE_EHIP, "unexpected host exception in moe_forward_static");

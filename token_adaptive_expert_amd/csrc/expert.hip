@@ -643,9 +643,9 @@ void expert_gemm_kernel(ExpertArgs a) {
               }
             } else {
               const float gt = a.sorted_gate[p];
-              float* o = reinterpret_cast<float*>(a.out) + p * N + col0 + r16;
+              T* o = reinterpret_cast<T*>(a.out) + p * N + col0 + r16;
 #pragma unroll
-              for (int g = 0; g < NGW; ++g) o[16 * g] = gt * acc[rb][g][j];
+              for (int g = 0; g < NGW; ++g) o[16 * g] = St<T>::from_f32(gt * acc[rb][g][j]);
             }
           }
         }
@@ -788,9 +788,9 @@ __global__ __launch_bounds__(SK_NW * 64) __attribute__((amdgpu_waves_per_eu(4)))
           reinterpret_cast<T*>(a.out)[p * N + col0 + c] = St<T>::from_f32(silu(v[0]) * v[1]);
         } else {
           const float gt = a.sorted_gate[p];
-          float* o = reinterpret_cast<float*>(a.out) + p * N + col0 + c;
+          T* o = reinterpret_cast<T*>(a.out) + p * N + col0 + c;
 #pragma unroll
-          for (int gg = 0; gg < NGRP; ++gg) o[16 * gg] = gt * v[gg];
+          for (int gg = 0; gg < NGRP; ++gg) o[16 * gg] = St<T>::from_f32(gt * v[gg]);
         }
       }
     }

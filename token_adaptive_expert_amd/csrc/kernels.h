@@ -44,7 +44,7 @@ struct ExpertArgs {
   const int32_t* offsets;     // [E+1]
   const int32_t* sorted_token;
   const float* sorted_gate;
-  void* out;                  // gate/up: act [*, I] (dtype); down: slot_out [*, H] f32
+  void* out;                  // gate/up: act [*, I]; down: slot_out [*, H] (both dtype)
   int K;                      // contraction length: H (gate/up) or I (down)
   int N;                      // weight rows per expert: I (gate/up) or H (down)
   int E;
@@ -73,7 +73,7 @@ struct FusedArgs {
 
 struct CombineArgs {
   const int32_t* slot_pos;
-  const float* slot_out;
+  const void* slot_out;       // [*, H] dtype
   const void* residual;
   void* y;
   int T, H, k;

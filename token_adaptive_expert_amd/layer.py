@@ -53,7 +53,7 @@ class LayerBuffers:
             sorted_gate=torch.empty(slots, dtype=torch.float32, **z),
             slot_pos=torch.empty(T, k, dtype=torch.int32, **z),
             act=torch.empty(slots, I, dtype=dtype, **z),
-            slot_out=torch.empty(slots, H, dtype=torch.float32, **z),
+            slot_out=torch.empty(slots, H, dtype=dtype, **z),
             workspace=torch.empty(ws, dtype=torch.uint8, **z),
             y=torch.empty(T, H, dtype=dtype, **z),
         )
