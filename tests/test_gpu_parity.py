@@ -163,10 +163,15 @@ def _bf16_case(T, H, E, I, k, rate, cfg_id, bias=None):
     dict(T=33, H=128, E=256, I=128, k=16, rate=0.6, cfg_id=103),
     dict(T=70, H=384, E=8, I=384, k=1, rate=0.0, cfg_id=104),
     dict(T=130, H=512, E=40, I=640, k=8, rate=0.7, cfg_id=105),
-    # >= 512 routed slots per expert: the 128-row, 8-wave tiles (ragged last tile)
+    # >= 256 routed slots per expert: the 128-row tiles with direct-to-LDS
+    # staging (ragged last tile)
     dict(T=520, H=256, E=8, I=256, k=8, rate=0.5, cfg_id=107),
     # same load with H not a multiple of 256: that tier falls back to 64-row tiles
     dict(T=520, H=384, E=8, I=128, k=8, rate=0.3, cfg_id=108),
+    # chunk counts that end inside the unrolled step sequences: gate/up 8, down 10
+    # (both on the 128-row tiles), and gate/up 2
+    dict(T=600, H=512, E=8, I=640, k=8, rate=0.4, cfg_id=109),
+    dict(T=600, H=128, E=8, I=256, k=8, rate=0.4, cfg_id=110),
 ])
 def test_bf16_shapes(dev, path, case):
     L, tg, tr = _bf16_case(**case)
