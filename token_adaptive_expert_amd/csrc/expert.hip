@@ -40,7 +40,7 @@ namespace {
                               // up to 3 row blocks fit 128 VGPRs with no spill and take 4)
 #endif
 #ifndef ACE_BIG_RB
-#define ACE_BIG_RB 8          // 16-row blocks per tile for batches with >= 512 slots per expert
+#define ACE_BIG_RB 8          // 16-row blocks per tile for batches with >= ACE_BIG_SLOTS slots per expert
 #endif
 #ifndef ACE_BIG_NW
 #define ACE_BIG_NW 4          // waves per tile of that tier
@@ -104,11 +104,22 @@ namespace {
 #define ACE_XCD_COLUMNS 1     // (expert, n-block) columns dealt round-robin over the XCDs: 0 never,
                               // 1 for the down projection (measured faster there), 2 for both kinds
 #endif
+#ifndef ACE_BIG_XCD_COLUMNS
+#define ACE_BIG_XCD_COLUMNS 0 // the same for the 128-row tier (measured faster with contiguous parts)
+#endif
 #ifndef ACE_LDS_PITCH
 #define ACE_LDS_PITCH 272     // padded LDS row pitch of the staged slot rows
 #endif
 
 constexpr int NXCD = 8;          // XCDs of an MI355X; only tile placement depends on it
+
+// Whether tiles of RB row blocks and kind KIND deal their columns over the
+// XCDs (else: the expert-major tile list in contiguous per-XCD parts).
+template <int RB, int KIND>
+constexpr bool columns_dealt() {
+  constexpr int mode = RB >= ACE_BIG_RB ? ACE_BIG_XCD_COLUMNS : ACE_XCD_COLUMNS;
+  return mode == 2 || (mode == 1 && KIND == 1);
+}
 constexpr int EMAX_EXP = 256;    // largest expert count
 constexpr int LDS_PITCH = ACE_LDS_PITCH;
 
@@ -329,7 +340,7 @@ void expert_gemm_kernel(ExpertArgs a) {
   const int nch = K / KC;
   const int nb_count = N / ROWS_PER_WG;
 
-  constexpr bool COLS = ACE_XCD_COLUMNS == 2 || (ACE_XCD_COLUMNS == 1 && KIND == 1);
+  constexpr bool COLS = columns_dealt<RB, KIND>();
   const int xcd = int(blockIdx.x % NXCD);
   if (COLS)
     build_xcd_tile_list<BM>(a, xcd, nb_count, s_pref, s_off);
@@ -341,11 +352,13 @@ void expert_gemm_kernel(ExpertArgs a) {
 
   // Tile placement: workgroup id i runs on XCD i % NXCD (round-robin
   // dispatch) and takes the (i / NXCD)-th tile of that XCD's list.  With
-  // column dealing (the down projection by default) an XCD's list holds every
-  // 8th (expert, n-block) column, each column's m-tiles consecutive, so every
-  // XCD streams a share of every expert and a column's weights are reused
-  // from one L2.  Otherwise (gate/up) the expert-major list is cut into NXCD
-  // contiguous parts, so that the n-blocks of one m-tile share its slot rows.  One
+  // column dealing (the down projection of the 32- to 64-row tiers by
+  // default) an XCD's list holds every 8th (expert, n-block) column, each
+  // column's m-tiles consecutive, so every XCD streams a share of every
+  // expert and a column's weights are reused from one L2.  Otherwise (gate/up;
+  // both kinds on the 128-row tiles) the expert-major list is cut into NXCD
+  // contiguous parts, so that an expert's tiles share its weights and slot
+  // rows on one XCD.  One
   // tile per workgroup; the hardware dispatcher refills a compute unit as soon
   // as one of its tiles finishes, which balances uneven per-CU bandwidth.
   const int per_xcd = COLS ? ntiles : (ntiles + NXCD - 1) / NXCD;
@@ -1074,7 +1087,7 @@ hipError_t launch_one(const ExpertArgs& a, int ntok, int k, hipStream_t s) {
   const int64_t nbc = a.N / ROWS_PER_WG;
   // the grid covers the largest possible tile count of any XCD (times NXCD);
   // workgroups past their XCD's actual count exit at once
-  constexpr bool COLS = ACE_XCD_COLUMNS == 2 || (ACE_XCD_COLUMNS == 1 && KIND == 1);
+  constexpr bool COLS = columns_dealt<RB, KIND>();
   const int64_t per_xcd_bound = COLS ? (nbc + NXCD - 1) / NXCD * mt_bound : (mt_bound * nbc + NXCD - 1) / NXCD;
   const int64_t grid = std::max<int64_t>(NXCD, std::min<int64_t>(per_xcd_bound * NXCD, int64_t(1) << 30));
   hipLaunchKernelGGL((expert_gemm_kernel<T, RB, NW, KIND, STAGES, NGW, CK, WPE, XB>), dim3(unsigned(grid)),
@@ -1121,9 +1134,10 @@ hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs
   // moderate batches (up to 64 routed slots per expert on average before
   // skipping): 48-row gate/up tiles and 32-row down tiles, each 4 per CU
   // (measured fastest at T = 1024, E = 128: 1536 gate/up and 2048+ down
-  // tiles).  Very large batches (at least 512 slots per expert):
-  // 128-row tiles of 8 waves, which halve the L2 traffic per MFMA when the
-  // GEMMs become compute-bound.  Between the two: 64-row tiles.
+  // tiles).  Large batches (at least ACE_BIG_SLOTS = 256 slots per expert):
+  // 128-row tiles of 4 waves with 64 weight rows each, which cut the L2
+  // traffic per MFMA when the GEMMs become compute-bound.  Between the two:
+  // 64-row tiles.
   const bool small_rb = int64_t(T) * k <= int64_t(64) * a.E && G > 2;
   // (the big tile covers ACE_BIG_NW * 8 * ACE_BIG_NGW units or 16 * that many
   // output columns: N must be a multiple)
