@@ -61,7 +61,7 @@ namespace {
 #define ACE_BIG_XB 3          // LDS buffers of the big tier's direct-to-LDS row staging (0: staged through registers)
 #endif
 #ifndef ACE_BIG_AF
-#define ACE_BIG_AF 2          // MFMA operand fragments per LDS read group of the direct-to-LDS staging
+#define ACE_BIG_AF 2          // MFMA operand fragments per inline-assembly LDS read group (one-ring staging)
 #endif
 #ifndef ACE_BIG_CCR
 #define ACE_BIG_CCR 1         // big gate/up tier: compiler-issued LDS reads from three separate arrays
