@@ -406,31 +406,32 @@ __global__ __launch_bounds__(RNTHR) void norm_router_wide_kernel(RouteArgs a, in
   float bias_v = 0.f;
   if (a.bias != nullptr && threadIdx.x < TB * ECBW) bias_v = a.bias[min(cbk * ECBW + int(threadIdx.x) % ECBW, E - 1)];
 
-  // inverse RMS: wave w owns tokens tok0 + w + 16*m, two rows in flight
+  // inverse RMS: wave w owns tokens tok0 + w + 16*m, all MT rows in flight,
+  // 4 segments of 512 values per row and batch (each row's sum runs over its
+  // segments in order, as in the other router variants)
   {
-    constexpr int SEG = 64 * EPL;
+    constexpr int SEG = 64 * EPL, NSEG = 4;
+    float ss[MT];
 #pragma unroll
-    for (int m0 = 0; m0 < MT; m0 += 2) {
-      float ss[2] = {0.f, 0.f};
-      for (int j0 = 0; j0 < H; j0 += 8 * SEG) {
-        u32x4 v[2][8];
+    for (int m = 0; m < MT; ++m) ss[m] = 0.f;
+    for (int j0 = 0; j0 < H; j0 += NSEG * SEG) {
+      u32x4 v[MT][NSEG];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const bf16_t* row = x + int64_t(min(tok0 + w + 16 * (m0 + m), a.T - 1)) * H;
+      for (int m = 0; m < MT; ++m) {
+        const bf16_t* row = x + int64_t(min(tok0 + w + 16 * m, a.T - 1)) * H;
 #pragma unroll
-          for (int b = 0; b < 8; ++b) v[m][b] = ld16(row + min(j0 + b * SEG + l * EPL, H - EPL));
-        }
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int b = 0; b < 8; ++b)
-            if (j0 + b * SEG + l * EPL < H) ss[m] += sumsq16<bf16_t>(v[m][b]);
+        for (int b = 0; b < NSEG; ++b) v[m][b] = ld16(row + min(j0 + b * SEG + l * EPL, H - EPL));
       }
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const float t = wave_sum_dpp(ss[m]);
-        if (l == 0) s_inv[w + 16 * (m0 + m)] = 1.0f / sqrtf(t / float(H) + a.eps);
-      }
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int b = 0; b < NSEG; ++b)
+          if (j0 + b * SEG + l * EPL < H) ss[m] += sumsq16<bf16_t>(v[m][b]);
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const float t = wave_sum_dpp(ss[m]);
+      if (l == 0) s_inv[w + 16 * m] = 1.0f / sqrtf(t / float(H) + a.eps);
     }
   }
   __syncthreads();
