@@ -385,7 +385,7 @@ __global__ __launch_bounds__(RNTHR) void norm_router_wide_kernel(RouteArgs a, in
   constexpr int ECBW = 32;
   constexpr int EPL = 8, KS = 32;
   __shared__ float s_inv[TBW];
-  __shared__ float s_part[RW][TB][ECBW + 1];
+  __shared__ float s_part[RW][TBW][ECBW + 1];
   const int E = a.E, H = a.H;
   const int ncb = (E + ECBW - 1) / ECBW;
   const int L = blockIdx.x;
@@ -404,7 +404,7 @@ __global__ __launch_bounds__(RNTHR) void norm_router_wide_kernel(RouteArgs a, in
   const int64_t plane_bytes = int64_t(CB) * nks * 1024;
   const int nki = w < nks ? (nks - 1 - w) / RW + 1 : 0;
   float bias_v = 0.f;
-  if (a.bias != nullptr && threadIdx.x < TB * ECBW) bias_v = a.bias[min(cbk * ECBW + int(threadIdx.x) % ECBW, E - 1)];
+  if (a.bias != nullptr) bias_v = a.bias[min(cbk * ECBW + int(threadIdx.x) % ECBW, E - 1)];
 
   // inverse RMS: wave w owns tokens tok0 + w + 16*m, all MT rows in flight,
   // 4 segments of 512 values per row and batch (each row's sum runs over its
@@ -485,25 +485,25 @@ __global__ __launch_bounds__(RNTHR) void norm_router_wide_kernel(RouteArgs a, in
     }
   }
 
-  // class partials summed in wave order, one 16-token block at a time
+  // class partials summed in wave order, all MT token blocks at once (the
+  // partials of the 16·MT tokens fit in LDS; thread u sums entries u,
+  // u + RNTHR, ..., whose expert column is the same, u % ECBW)
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    if (m > 0) __syncthreads();
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) s_part[w][4 * q + j][16 * c + r16] = acc[m][c][j];
-    __syncthreads();
-    if (threadIdx.x < TB * ECBW) {
-      const int u = threadIdx.x;
-      const int tl = u / ECBW, c = u % ECBW, e = cbk * ECBW + c, to = tok0 + 16 * m + tl;
-      if (to < a.T && e < E) {
-        float v = s_part[0][tl][c];
+      for (int c = 0; c < 2; ++c) s_part[w][16 * m + 4 * q + j][16 * c + r16] = acc[m][c][j];
+  __syncthreads();
+  static_assert(RNTHR % ECBW == 0, "a thread's entries share one expert column");
+  for (int u = threadIdx.x; u < TBW * ECBW; u += RNTHR) {
+    const int tl = u / ECBW, c = u % ECBW, e = cbk * ECBW + c, to = tok0 + tl;
+    if (to < a.T && e < E) {
+      float v = s_part[0][tl][c];
 #pragma unroll
-        for (int ww = 1; ww < RW; ++ww) v += s_part[ww][tl][c];
-        if (a.bias) v += bias_v;
-        a.logits_out[int64_t(to) * E + e] = v;
-      }
+      for (int ww = 1; ww < RW; ++ww) v += s_part[ww][tl][c];
+      if (a.bias) v += bias_v;
+      a.logits_out[int64_t(to) * E + e] = v;
     }
   }
 }
