@@ -357,6 +357,56 @@ def test_router_variants_batch_invariant(qwen, dev):
     assert np.max(np.abs(full["logits"][rows].astype(np.float64) - lg_ref)) <= 4e-3
 
 
+def _route_only(x, gamma, packed, bias, E, dev):
+    T, H = x.shape
+    d = ace._lib.make_desc(T, H, E, 128, 8, torch.bfloat16, router_layout=ace._lib.ACE_LAYOUT_PACKED)
+    z = dict(device=dev)
+    logits = torch.empty(T, E, dtype=torch.float32, **z)
+    h = torch.empty(T, H, dtype=torch.bfloat16, **z)
+    ones = torch.ones(E, dtype=torch.float32, **z)
+    ace._lib.moe_route_skip(d, x, gamma, packed, bias, None, logits, ones, ones, 0.0, 0.0, h,
+                            torch.empty(T, 8, dtype=torch.int32, **z), torch.empty(T, 8, dtype=torch.float32, **z),
+                            torch.empty(T, 8, dtype=torch.uint8, **z))
+    torch.cuda.synchronize()
+    return h.view(torch.int16).cpu().numpy(), logits.cpu().numpy()
+
+
+@pytest.mark.parametrize("H,E,with_bias", [(2048, 128, True), (2048, 80, False), (4096, 128, False),
+                                           (4096, 72, True)])
+def test_router_two_kernel_batch_invariant(dev, H, E, with_bias):
+    """From 4096 tokens at H = 2048 the RMSNorm and the router product run as
+    two kernels (h first, then the logits from h; at H = 4096 the 64-token
+    variant serves 4133 tokens); a token's h and logits must equal, bit for
+    bit, those of the variants that smaller batches take (32 tokens per
+    workgroup, 16 tokens, 16-expert sub-blocks), with a ragged last token
+    block and, for E = 80 and 72, expert column blocks past E; sampled rows
+    also against the oracle."""
+    g = torch.Generator().manual_seed(H + E)
+    T = 4096 + 37
+    x = (torch.randn(T, H, generator=g) * 1.5).to(torch.bfloat16)
+    gamma = torch.rand(H, generator=g) + 0.5
+    w_r = torch.randn(E, H, generator=g) * 0.03
+    bias = (torch.randn(E, generator=g) * 0.1) if with_bias else None
+    xd, gd, wd = x.to(dev), gamma.to(dev), w_r.to(dev)
+    bd = bias.to(dev) if bias is not None else None
+    d1 = ace._lib.make_desc(1, H, E, 128, 8, torch.bfloat16)
+    packed = torch.empty(ace._lib.moe_router_packed_bytes(d1), dtype=torch.uint8, device=dev)
+    ace._lib.moe_pack_router(d1, wd, packed)
+    h_full, lg_full = _route_only(xd, gd, packed, bd, E, dev)
+    for Tp in (2050, 1000, 5):
+        h_p, lg_p = _route_only(xd[:Tp].contiguous(), gd, packed, bd, E, dev)
+        assert np.array_equal(h_p, h_full[:Tp]), Tp
+        assert np.array_equal(lg_p.view(np.uint32), lg_full[:Tp].view(np.uint32)), Tp
+    rows = [0, 63, 64, 1000, 4095, 4096, T - 1]
+    xh = x[rows].float().numpy().astype(np.float64)
+    h_ref = oracle.rmsnorm(xh, gamma.numpy().astype(np.float64), 1e-6, "bf16")
+    h_gpu = torch.from_numpy(h_full[rows]).view(torch.bfloat16).float().numpy()
+    assert np.all(np.abs(h_gpu - h_ref) <= np.abs(h_ref) * 2.0 ** -7 + 1e-30)
+    b64 = bias.numpy().astype(np.float64) if bias is not None else None
+    lg_ref = oracle.router_logits(h_ref, w_r.numpy().astype(np.float64), b64)
+    assert np.max(np.abs(lg_full[rows].astype(np.float64) - lg_ref)) <= 4e-3
+
+
 @pytest.mark.timeout(900)
 def test_glm45_air_shape_full_size(dev):
     """GLM-4.5-Air-shaped layer (H=4096, E=128, I=1408, top-8, bf16, T=4096,

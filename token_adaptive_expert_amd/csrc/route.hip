@@ -29,6 +29,15 @@ constexpr int XL_PITCH = XL_HMAX + 8;  // bf16 elements per LDS row
 #ifndef ACE_ROUTER_WIDE_NBK4
 #define ACE_ROUTER_WIDE_NBK4 1     // k-steps per load batch of the 64-token variant
 #endif
+#ifndef ACE_ROUTER_H_T
+#define ACE_ROUTER_H_T 4096        // batch from which the RMS and the router product run as two kernels
+#endif
+#ifndef ACE_ROUTER_H_PA
+#define ACE_ROUTER_H_PA 4          // k-steps of router planes in flight per wave (two-kernel router)
+#endif
+#ifndef ACE_ROUTER_H_SD
+#define ACE_ROUTER_H_SD 2          // classes of h fragments staged ahead (two-kernel router)
+#endif
 #ifndef ACE_ROUTER_NARROW_WG
 #define ACE_ROUTER_NARROW_WG 64    // workgroups aimed at by the small-batch variant's expert sub-blocks
 #endif
@@ -508,6 +517,199 @@ __global__ __launch_bounds__(RNTHR) void norm_router_wide_kernel(RouteArgs a, in
   }
 }
 
+// Workgroup barrier that orders LDS only (this wave's LDS operations
+// complete, then s_barrier): unlike __syncthreads() it leaves the router
+// plane loads in flight.
+__device__ __forceinline__ void lds_only_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Large batches, H a multiple of 512 (bf16, pre-split router; launched at
+// H = 2048): the RMSNorm and the router product as two kernels, each step
+// the one of the other variants.  Kernel 1a: one wave per row, lane l holding x values 8l .. 8l+7
+// of every 512-value segment, the per-lane sum over the segments in order,
+// the same 64-lane reduction, h = make_h; x is read and h written once, at
+// the streaming rate (R rows of a wave in flight together).
+template <int NSEG, int R>
+__global__ __launch_bounds__(256) void rms_h_kernel(RouteArgs a) {
+  constexpr int EPL = 8, SEG = 64 * EPL;
+  const int H = a.H;  // == NSEG * SEG (checked by the launcher)
+  const int l = lane_id();
+  const int nw = int(gridDim.x) * 4;
+  const int gw = int(blockIdx.x) * 4 + wave_id();
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, uint32_t(a.T * H * 2));
+  const __amdgpu_buffer_rsrc_t gr = make_rsrc(a.gamma, uint32_t(H * 4));
+  f32x4 g[NSEG][2];
+#pragma unroll
+  for (int s = 0; s < NSEG; ++s) {
+    g[s][0] = __builtin_bit_cast(f32x4, buf_ld16(gr, (s * SEG + l * EPL) * 4, 0));
+    g[s][1] = __builtin_bit_cast(f32x4, buf_ld16(gr, (s * SEG + l * EPL) * 4 + 16, 0));
+  }
+  bf16_t* hout = reinterpret_cast<bf16_t*>(a.h_out);
+  for (int r0 = gw * R; r0 < a.T; r0 += nw * R) {
+    u32x4 v[R][NSEG];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = min(r0 + r, a.T - 1);
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s) v[r][s] = buf_ld16(xr, (row * H + s * SEG + l * EPL) * 2, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float ss = 0.f;
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s) ss += sumsq16<bf16_t>(v[r][s]);
+      const float inv = 1.0f / sqrtf(wave_sum_dpp(ss) / float(H) + a.eps);
+      if (r0 + r < a.T) {
+        bf16_t* hrow = hout + int64_t(r0 + r) * H + l * EPL;
+#pragma unroll
+        for (int s = 0; s < NSEG; ++s) st16(hrow + s * SEG, make_h<bf16_t>(v[r][s], inv, g[s]));
+      }
+    }
+  }
+}
+
+// Kernel 1b: the router product from h for 16·MT tokens x 4·NCW column
+// blocks of 16 experts (one wave per NCW column blocks).  The logit of the
+// other variants is the sum, in class order, of 16 class partials, class c
+// being the MFMA chain (planes 0, 1, 2 per k-step) over k-steps c, c+16, ...
+// in order, started from zero.  Here each wave walks the classes in turn
+// for its own outputs and keeps that sum in registers (total = partial for
+// class 0, total + partial after), so no partials go through LDS and the
+// result is the same bit for bit.  The h fragments of a class (16·MT tokens
+// x NKI k-steps) are staged in LDS fragment by fragment (lane order, so the
+// operand reads are contiguous), loaded SD classes ahead into registers; the
+// router plane fragments go straight into registers, PA k-steps ahead.  At
+// T = 32768 this pair takes ~130 µs where the one-kernel variant took ~215:
+// that one read x twice, in phases that every workgroup went through in
+// step (1 workgroup per compute unit, 8 rounds).
+template <int MT, int NKI, int NCW, int PA, int SD>
+__global__ __launch_bounds__(256, 2) void router_from_h_kernel(RouteArgs a) {
+  constexpr int NW = 4, KS = 32, EPL = 8;
+  constexpr int NKS = 16 * NKI;      // k-steps of a row
+  constexpr int TT = 16 * MT;        // tokens of the workgroup
+  constexpr int FR = MT * NKI;       // h fragments (1 KB) of a class
+  constexpr int FPW = FR / NW;       // staged by each wave
+  static_assert(FR % NW == 0, "the class's fragments split evenly over the waves");
+  static_assert(NKI % PA == 0, "the plane ring index is the k-step's index in its class modulo PA");
+  static_assert(16 % SD == 0, "the class loop runs in groups of SD");
+  __shared__ u32x4 s_a[2][FR * 64];
+  const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id();
+  const int q = l >> 4, r16 = l & 15;
+  const int H = a.H, E = a.E;
+  const int tok0 = int(blockIdx.x) * TT;
+  const int nrows = min(TT, a.T - tok0);
+  const int CB = (E + 15) / 16;
+  int cb[NCW];
+#pragma unroll
+  for (int n = 0; n < NCW; ++n) cb[n] = min((int(blockIdx.y) * NW + w) * NCW + n, CB - 1);
+  const int plane_bytes = CB * NKS * 1024;
+  const __amdgpu_buffer_rsrc_t hr =
+      make_rsrc(reinterpret_cast<const bf16_t*>(a.h_out) + int64_t(tok0) * H, uint32_t(nrows * H * 2));
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.w_router, uint32_t(3 * plane_bytes));
+
+  // staging: fragment f = w + NW·i is (token block f / NKI, k-step f % NKI of
+  // the class); lane (r16, q) fetches 8 h values of token 16·(f/NKI) + r16.
+  // The fragments of class c + SD are requested while class c runs (held in
+  // registers), and stored to LDS at the end of class c + SD - 1.
+  int ho[FPW];
+#pragma unroll
+  for (int i = 0; i < FPW; ++i) {
+    const int f = w + NW * i;
+    ho[i] = (min(16 * (f / NKI) + r16, nrows - 1) * H + q * EPL) * 2;
+  }
+  u32x4 st[SD][FPW];
+  auto stage_load = [&](int slot, int c) {
+#pragma unroll
+    for (int i = 0; i < FPW; ++i) st[slot][i] = buf_ld16(hr, ho[i], (c + 16 * ((w + NW * i) % NKI)) * KS * 2);
+  };
+  auto stage_store = [&](int slot, int buf) {
+#pragma unroll
+    for (int i = 0; i < FPW; ++i) s_a[buf][(w + NW * i) * 64 + l] = st[slot][i];
+  };
+  u32x4 pl[PA][NCW][3];
+  auto issue = [&](int c, int s) {  // k-step s of class c (a clamped repeat past the last)
+    const int idx = min(c * NKI + s, NKS - 1);
+    const int j = idx / NKI + 16 * (idx % NKI);
+#pragma unroll
+    for (int n = 0; n < NCW; ++n)
+#pragma unroll
+      for (int p = 0; p < 3; ++p) pl[s % PA][n][p] = buf_ld16(pr, l * 16, p * plane_bytes + (cb[n] * NKS + j) * 1024);
+  };
+
+#pragma unroll
+  for (int d = 0; d < SD; ++d) stage_load(d, d);  // class k is held in slot k % SD
+  stage_store(0, 0);
+#pragma unroll
+  for (int s = 0; s < PA; ++s) issue(0, s);
+  lds_only_barrier();
+  f32x4 tot[MT][NCW];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int n = 0; n < NCW; ++n) tot[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < 16; c0 += SD) {
+#pragma unroll
+    for (int d = 0; d < SD; ++d) {
+      const int c = c0 + d;
+      // slot d held class c, already in LDS, and now receives class c + SD
+      // (past the last class: a repeat of it, never stored where it is read)
+      stage_load(d, min(c + SD, 15));
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 acc[MT][NCW];
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int n = 0; n < NCW; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NKI; ++s) {
+        u32x4 hf[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) hf[m] = s_a[c & 1][(m * NKI + s) * 64 + l];
+        // plane fragment (n, p) feeds the MT MFMAs of column block n (each
+        // accumulator still takes planes 0, 1, 2 in order), then is reloaded
+        // at once with k-step s + PA's fragment: loads go out one per MT
+        // MFMAs instead of in a burst (pinned by the group barriers)
+        const int idx = min(c * NKI + s + PA, NKS - 1);
+        const int jn = idx / NKI + 16 * (idx % NKI);
+#pragma unroll
+        for (int n = 0; n < NCW; ++n)
+#pragma unroll
+          for (int p = 0; p < 3; ++p) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[m][n] = mfma_bf16(hf[m], pl[s % PA][n][p], acc[m][n]);
+            pl[s % PA][n][p] = buf_ld16(pr, l * 16, p * plane_bytes + (cb[n] * NKS + jn) * 1024);
+          }
+#pragma unroll
+        for (int g = 0; g < 3 * NCW; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);  // MT MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one vector-memory read
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int n = 0; n < NCW; ++n) tot[m][n] = c == 0 ? acc[m][n] : tot[m][n] + acc[m][n];  // no 0 + (-0)
+      stage_store((d + 1) % SD, (c + 1) & 1);
+      lds_only_barrier();
+    }
+  }
+
+#pragma unroll
+  for (int n = 0; n < NCW; ++n) {
+    const int e = cb[n] * 16 + r16;
+    const bool e_ok = (int(blockIdx.y) * NW + w) * NCW + n < CB && e < E;
+    const float bv = a.bias != nullptr && e_ok ? a.bias[e] : 0.f;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tl = 16 * m + 4 * q + j;
+        float v = tot[m][n][j];
+        if (a.bias) v += bv;
+        if (e_ok && tl < nrows) a.logits_out[int64_t(tok0 + tl) * E + e] = v;
+      }
+  }
+}
+
 // Kernel 2: top-k, gates and skip mask, one wave per token (topk_slots).
 __global__ __launch_bounds__(NTHR) void topk_skip_kernel(RouteArgs a) {
   constexpr int NWV = NTHR / 64;
@@ -594,7 +796,16 @@ hipError_t launch_route(int dtype, const RouteArgs& a, hipStream_t s, bool with_
       dtype == 1 && a.router_packed && a.logits_in == nullptr && gx <= ACE_ROUTER_NARROW_GX && a.H <= NARROW_HMAX;
   // large batches with the pre-split router: 32 or 64 tokens per workgroup
   const bool wide = dtype == 1 && a.router_packed && a.logits_in == nullptr && a.T >= ACE_ROUTER_WIDE_T;
-  if (wide) {
+  // from ACE_ROUTER_H_T tokens at H = 2048: RMS + h, then the router product
+  // from h (32-bit buffer offsets: the batch's x fits in 2 GB).  At
+  // H = 4096 the two kernels measured no faster than the wide one.
+  const bool two = wide && a.T >= ACE_ROUTER_H_T && a.H == 2048 && int64_t(a.T) * a.H * 2 < (int64_t(1) << 31);
+  if (two) {
+    const unsigned CB = unsigned((a.E + 15) / 16);
+    hipLaunchKernelGGL((rms_h_kernel<4, 4>), dim3(unsigned((a.T + 15) / 16)), block, 0, s, a);
+    hipLaunchKernelGGL((router_from_h_kernel<4, 4, 2, ACE_ROUTER_H_PA, ACE_ROUTER_H_SD>),
+                       dim3(unsigned((a.T + 63) / 64), (CB + 7) / 8), block, 0, s, a);
+  } else if (wide) {
     const int mt = a.T >= ACE_ROUTER_WIDE_MT4_T ? 4 : 2;
     const int gxw = (a.T + TB * mt - 1) / (TB * mt);
     const unsigned nwg = unsigned((gxw + 7) / 8 * 8 * ((a.E + 31) / 32));
@@ -636,3 +847,4 @@ hipError_t launch_route(int dtype, const RouteArgs& a, hipStream_t s, bool with_
 }
 
 }  // namespace ace
+
