@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--no-tables", action="store_true", help="skip timing the offline table builder")
     p.add_argument("--no-stack", action="store_true", help="skip the 48-layer stack")
     p.add_argument("--decode-m", type=int, nargs="+", help="decode batch sizes to run (default: all)")
-    p.add_argument("--only", choices=["decode", "glm", "t32k", "stack", "tables", "calib"],
+    p.add_argument("--only", choices=["decode", "glm", "t32k", "stack", "tables", "calib", "probes"],
                    help="run that leg alone and print its result (for profiling runs), not the contract line")
     p.add_argument("--no-extra", action="store_true",
                    help="skip the GLM-4.5-Air-shaped layer, the T=32768 run and the dense GEMM ceiling")
@@ -175,6 +175,34 @@ class Bench:
         del buf
         return {"GBs": round(best, 1), "bytes": nbytes, "by_workgroups": by_grid,
                 "kernel": "moe_hbm_read_probe (read only, 16-byte loads, 8 in flight per thread)"}
+
+    def l2_load_rates(self, rounds=2048, reps=5):
+        """Load rate from L2 per compute unit (moe_l2_load_probe on a 2 MiB
+        buffer, 6 loads of 1 KB in flight per wave), alone and with 4 bf16
+        MFMAs per loaded KB (the router's ratio), the blocks of a round
+        consecutive or at the router planes' 64 KB / 512 KB spacing; 2 and 3
+        workgroups of 4 waves per CU.  B/clk at the 2.4 GHz peak engine
+        clock; MFMA busy = MFMA cycles (16 per 16x16x32 bf16 MFMA) over the
+        SIMDs' cycles."""
+        torch, ace = self.torch, self.ace
+        buf = torch.randint(0, 255, (2 << 20,), dtype=torch.uint8, device=self.dev)
+        ncu = torch.cuda.get_device_properties(self.dev).multi_processor_count
+        out = []
+        for mfma in (0, 4):
+            for stride in (0, 1):
+                for per_cu in (2, 3):
+                    wg = ncu * per_cu
+                    sink = torch.empty(wg * 4, dtype=torch.int32, device=self.dev)
+                    it = max(1, rounds // per_cu)
+                    ms = timed(torch, lambda i: ace.moe_l2_load_probe(buf, sink, wg, it, 6, mfma, stride), reps, 2)
+                    cyc = ms * 1e-3 * 2.4e9
+                    loads = wg * 4 * it * 6
+                    out.append({"mfma_per_KB": mfma, "stride_mode": stride, "wg_per_cu": per_cu,
+                                "B_per_clk_per_cu": round(loads * 1024 / ncu / cyc, 1),
+                                "TBs": round(loads * 1024 / (ms * 1e-3) / 1e12, 1),
+                                "mfma_busy": round(loads * mfma * 16 / (4 * ncu) / cyc, 3)})
+        del buf
+        return out
 
     def launch_floor(self, n=64, reps=20):
         """Time per kernel of a HIP graph of n back-to-back launches of a
@@ -673,6 +701,8 @@ def main():
             out = stack48(B)
         elif args.only == "calib":
             out = calibration_leg(B)
+        elif args.only == "probes":
+            out = {"l2_load_probe": B.l2_load_rates(), "hbm_read_ceiling": B.read_ceiling()}
         else:
             out = tables_build(B)
         print(json.dumps({"only": args.only, "result": out}), flush=True)
@@ -728,6 +758,7 @@ def main():
     res["hbm_copy_ceiling_GBs"] = round(B.copy_ceiling(), 1)
     res["hbm_read_ceiling"] = B.read_ceiling()
     res["graph_launch_floor_us"] = B.launch_floor()
+    res["l2_load_probe"] = B.l2_load_rates()
     if not args.no_sweep:
         sweep = {}
         for r in (0.0, 0.5):

@@ -357,6 +357,21 @@ ace_status moe_build_tables(const ace_moe_desc* d, float eps, const float* gamma
 ace_status moe_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups, void* stream);
 
 /*
+ * moe_l2_load_probe -- a measuring aid, not a step of the layer: each wave of
+ * `workgroups` workgroups of 256 threads runs `rounds` rounds of `loads`
+ * (6 or 8) 1 KB loads (lane l reads 16 bytes at 16 l of a block) from `buf`
+ * (`bytes` a power of two in [2 MiB, 1 GiB], small enough to stay in L2 at
+ * 2 MiB), the next round's loads issued before this round's blocks are
+ * used; each block feeds `mfma_per_load` (0, 4 or 8) bf16 MFMAs as their B
+ * operand.  stride_mode 0: a round's blocks are consecutive; 1: block j sits
+ * at (j % 3) * 512 KB + (j / 3) * 64 KB past the round's base.  Each wave
+ * writes one 32-bit fold to sink [workgroups * 4] (device).  Timing it gives
+ * the load rate a compute unit sustains from L2 with and without MFMAs.
+ */
+ace_status moe_l2_load_probe(const void* buf, size_t bytes, int32_t rounds, int32_t loads, int32_t mfma_per_load,
+                             int32_t stride_mode, uint32_t* sink, int32_t workgroups, void* stream);
+
+/*
  * moe_set_kernel_events -- for profiling callers: the next moe_expert_forward
  * on this thread records `start` (a hipEvent_t) on its stream just before the
  * gate/up kernel and `stop` just after it, then forgets both.  NULL clears.

@@ -223,3 +223,23 @@ def test_forward_static_validates_and_bounds_its_scratch():
     d0 = m.make_desc(0, 256, 16, 128, 4, "bf16")
     assert lib.moe_forward_static(ctypes.byref(d0), 0, f, f, f, None, None, f, f, f, 0.0, 0.0, f, f, f, None, f, f, f,
                                   f, f, f, f, f, f, None) == 0
+
+
+def test_probe_arguments_validated_before_launch():
+    m, lib = _lib()
+    f = 0x1000
+    mib2 = 2 << 20
+    # moe_l2_load_probe(buf, bytes, rounds, loads, mfma_per_load, stride_mode, sink, workgroups, stream)
+    for args, needle in (((f, 3 << 20, 8, 6, 0, 0, f, 8, None), "bytes="),
+                         ((f, 1 << 20, 8, 6, 0, 0, f, 8, None), "bytes="),
+                         ((f, mib2, 8, 7, 0, 0, f, 8, None), "loads=7"),
+                         ((f, mib2, 8, 6, 2, 0, f, 8, None), "mfma_per_load=2"),
+                         ((f, mib2, 8, 6, 4, 2, f, 8, None), "stride_mode=2"),
+                         ((f, mib2, 0, 6, 4, 0, f, 8, None), "rounds=0"),
+                         ((f, mib2, 8, 6, 4, 0, f, 0, None), "workgroups=0"),
+                         ((None, mib2, 8, 6, 4, 0, f, 8, None), "buf is NULL"),
+                         ((f, mib2, 8, 6, 4, 0, None, 8, None), "sink is NULL")):
+        assert lib.moe_l2_load_probe(*args) == 1, args
+        assert needle in lib.moe_last_error().decode(), (needle, lib.moe_last_error())
+    assert lib.moe_hbm_read_probe(f, 24, f, 4, None) == 1
+    assert lib.moe_hbm_read_probe(f, 32, f, 0, None) == 1

@@ -8,7 +8,7 @@ from ._lib import (ACE_BF16, ACE_F32, ACE_PATH_AUTO, ACE_PATH_GROUPED, ACE_PATH_
                    moe_dispatch, moe_expert_forward, moe_pack_router, moe_pack_weights, moe_router_packed_bytes,
                    moe_last_error, moe_route_skip, moe_set_kernel_events, moe_workspace_bytes,
                    moe_build_tables, moe_tables_workspace_bytes, moe_forward, moe_forward_static,
-                   ACE_STATIC_SCRATCH_BYTES, moe_hbm_read_probe)
+                   ACE_STATIC_SCRATCH_BYTES, moe_hbm_read_probe, moe_l2_load_probe)
 from .layer import AceMoeLayer, LayerBuffers, build_tables
 from .stack import AceMoeStack
 
@@ -17,4 +17,4 @@ __all__ = ["ACE_BF16", "ACE_F32", "ACE_PATH_AUTO", "ACE_PATH_GROUPED", "ACE_PATH
            "ACE_LAYOUT_LINEAR", "ACE_LAYOUT_PACKED", "load", "make_desc", "moe_pack_router", "moe_pack_weights", "moe_router_packed_bytes", "moe_abi_version", "moe_calibrate_thresholds", "moe_calibrate_workspace_bytes", "moe_combine", "moe_dispatch", "moe_expert_forward",
            "moe_last_error", "moe_route_skip", "moe_set_kernel_events", "moe_workspace_bytes", "AceMoeLayer",
            "LayerBuffers", "moe_build_tables", "moe_tables_workspace_bytes", "build_tables", "AceMoeStack", "moe_forward",
-           "moe_forward_static", "ACE_STATIC_SCRATCH_BYTES", "moe_hbm_read_probe"]
+           "moe_forward_static", "ACE_STATIC_SCRATCH_BYTES", "moe_hbm_read_probe", "moe_l2_load_probe"]

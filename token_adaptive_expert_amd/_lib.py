@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "ACE_OK", 1: "ACE_EINVAL", 2: "ACE_EUNSUPPORTED", 3: "ACE_EWO
 EXPORTS = ["moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_route_skip", "moe_dispatch",
            "moe_expert_forward", "moe_combine", "moe_calibrate_workspace_bytes", "moe_calibrate_thresholds",
            "moe_pack_weights", "moe_router_packed_bytes", "moe_pack_router", "moe_tables_workspace_bytes",
-           "moe_build_tables", "moe_forward", "moe_forward_static", "moe_hbm_read_probe", "moe_set_kernel_events"]
+           "moe_build_tables", "moe_forward", "moe_forward_static", "moe_hbm_read_probe", "moe_l2_load_probe", "moe_set_kernel_events"]
 
 ACE_STATIC_SCRATCH_BYTES = 80 << 20
 
@@ -112,6 +112,8 @@ def load() -> ctypes.CDLL:
                                        P, P]
     lib.moe_hbm_read_probe.restype = ctypes.c_int
     lib.moe_hbm_read_probe.argtypes = [P, SZ, P, I32, P]
+    lib.moe_l2_load_probe.restype = ctypes.c_int
+    lib.moe_l2_load_probe.argtypes = [P, SZ, I32, I32, I32, I32, P, I32, P]
     lib.moe_set_kernel_events.restype = ctypes.c_int
     lib.moe_set_kernel_events.argtypes = [P, P]
     _lib = lib
@@ -242,6 +244,14 @@ def moe_forward_static(desc, path, x, gamma, w_router, router_bias, logits_in, l
                                      _ptr(residual), _ptr(h_out), _ptr(topk_idx), _ptr(topk_gate), _ptr(keep),
                                      _ptr(expert_offsets), _ptr(sorted_token), _ptr(sorted_gate), _ptr(slot_pos),
                                      _ptr(y), _stream(stream)), "moe_forward_static")
+
+
+def moe_l2_load_probe(buf, sink, workgroups, rounds, loads=6, mfma_per_load=0, stride_mode=0, nbytes=None,
+                      stream=None):
+    nbytes = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    _check(load().moe_l2_load_probe(_ptr(buf), int(nbytes), int(rounds), int(loads), int(mfma_per_load),
+                                    int(stride_mode), _ptr(sink), int(workgroups), _stream(stream)),
+           "moe_l2_load_probe")
 
 
 def moe_hbm_read_probe(buf, sink, workgroups, nbytes=None, stream=None):

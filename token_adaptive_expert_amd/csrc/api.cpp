@@ -688,6 +688,28 @@ ace_status moe_build_tables(const ace_moe_desc* d, float eps, const float* gamma
   }
 }
 
+ace_status moe_l2_load_probe(const void* buf, size_t bytes, int32_t rounds, int32_t loads, int32_t mfma_per_load,
+                             int32_t stride_mode, uint32_t* sink, int32_t workgroups, void* stream) {
+  try {
+    REQUIRE(buf);
+    REQUIRE(sink);
+    if (bytes < (size_t(2) << 20) || bytes > (size_t(1) << 30) || (bytes & (bytes - 1)) != 0)
+      return fail(ACE_EINVAL, "bytes=%zu is not a power of two in [2 MiB, 1 GiB]", bytes);
+    if (loads != 6 && loads != 8) return fail(ACE_EINVAL, "loads=%d is not 6 or 8", loads);
+    if (mfma_per_load != 0 && mfma_per_load != 4 && mfma_per_load != 8)
+      return fail(ACE_EINVAL, "mfma_per_load=%d is not 0, 4 or 8", mfma_per_load);
+    if (stride_mode != 0 && stride_mode != 1) return fail(ACE_EINVAL, "stride_mode=%d is not 0 or 1", stride_mode);
+    if (rounds < 1 || rounds > (1 << 24)) return fail(ACE_EINVAL, "rounds=%d outside [1, 2^24]", rounds);
+    if (workgroups < 1 || workgroups > (1 << 20)) return fail(ACE_EINVAL, "workgroups=%d outside [1, 2^20]", workgroups);
+    hipError_t e = ace::launch_l2_probe(buf, bytes, rounds, loads, mfma_per_load, stride_mode, sink, workgroups,
+                                        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("l2 probe launch", e);
+    return ok();
+  } catch (...) {
+    return fail(ACE_EHIP, "unexpected host exception in moe_l2_load_probe");
+  }
+}
+
 ace_status moe_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups, void* stream) {
   try {
     REQUIRE(buf);

@@ -141,5 +141,7 @@ hipError_t launch_tables(int dtype, TablesArgs a, void* workspace, size_t worksp
 // Streaming-read probe (measuring aid): reads bytes (a multiple of 16) of src,
 // writes one word per workgroup to sink.
 hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int workgroups, hipStream_t s);
+hipError_t launch_l2_probe(const void* buf, size_t bytes, int rounds, int loads, int mfma_per_load, int stride_mode,
+                           uint32_t* sink, int workgroups, hipStream_t s);
 
 }  // namespace ace
