@@ -85,6 +85,9 @@ namespace {
 #ifndef ACE_MID_NGW
 #define ACE_MID_NGW 4         // weight groups per wave of the 64-row tier
 #endif
+#ifndef ACE_MID_DOWN_WPE
+#define ACE_MID_DOWN_WPE 2    // occupancy target of the 64-row tier's down projection (2 waves per SIMD: no spill)
+#endif
 #ifndef ACE_MID_CK
 #define ACE_MID_CK 2          // k-steps per chunk of the 64-row tier
 #endif
@@ -1164,7 +1167,7 @@ hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs
     constexpr int MID_NGW = ACE_MID_NGW, MID_CK = ACE_MID_CK;
     if (a.N % ((kind == 0 ? 8 : 16) * (kind == 0 ? NG : ND) * MID_NGW) == 0)
       return kind == 0 ? launch_one<bf16_t, G, NG, 0, S, MID_NGW, MID_CK>(a, T, k, s)
-                       : launch_one<bf16_t, G, ND, 1, S, MID_NGW, MID_CK>(a, T, k, s);
+                       : launch_one<bf16_t, G, ND, 1, S, MID_NGW, MID_CK, ACE_MID_DOWN_WPE>(a, T, k, s);
     return kind == 0 ? launch_one<bf16_t, G, NG, 0, S>(a, T, k, s)
                      : launch_one<bf16_t, G, ND, 1, S>(a, T, k, s);
   }
