@@ -202,6 +202,28 @@ def test_one_expert_takes_every_token(dev, path):
     check_y(values(g["y"]), ref["y"], "bf16")
 
 
+@pytest.mark.parametrize("packed", [False, True])
+def test_big_tier_light_and_full_tiles(dev, packed):
+    """A skewed router at >= 256 routed slots per expert (the 128-row tier):
+    experts with a handful of kept rows (the light path: only their row
+    blocks, a deeper weight ring), experts of 33 to 128 rows and experts of
+    several m-tiles (full tiles, ragged last tiles) in one launch.  Routing
+    and dispatch bit for bit; y and every slot row within the bf16 bars."""
+    E = 32
+    r = np.random.default_rng(5).permutation(E) + 1
+    bias = (-0.4 * np.log(r)).astype(np.float32)
+    L, tg, tr = _bf16_case(T=1100, H=256, E=E, I=256, k=8, rate=0.5, cfg_id=111, bias=bias)
+    S = L["shape"]
+    g = GpuLayer(L, dev, packed=packed).run(tg, tr)
+    check_routing_shared_logits(L, g, tg, tr)
+    off, _, _, _ = check_dispatch(S, g)
+    n_e = np.diff(off.astype(np.int64))
+    assert np.sum((n_e >= 1) & (n_e <= 32)) >= 4 and np.sum(n_e > 256) >= 2, n_e
+    ref = oracle_y(L, g, tg, tr)
+    check_y(values(g["y"]), ref["y"], "bf16")
+    check_slot_outputs(L, g, ref, "bf16")
+
+
 # ---------------------------------------------------------------- seeded random shapes
 def _random_case(i):
     rng = np.random.default_rng(9000 + i)

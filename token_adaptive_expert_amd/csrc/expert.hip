@@ -18,6 +18,10 @@
 //     through LDS and shared by all waves of the tile: through registers
 //     into two LDS buffers, or (128-row tiles) by direct-to-LDS buffer loads
 //     into a ring of three buffers, two chunks ahead of the MFMAs.
+// In the 128-row gate/up tier a tile of at most 32 slot rows (an expert with
+// few kept slots, or the ragged last m-tile of a larger one) multiplies only
+// its own row blocks and spends the freed accumulator registers on a deeper
+// weight ring; its outputs have the same bits as in a full tile.
 // Every workgroup derives the tile list from expert_offsets (experts with no
 // kept slot produce no tile, so their weights are never read) and takes the
 // tile of its index.
@@ -66,6 +70,13 @@ namespace {
 #ifndef ACE_BIG_CCR
 #define ACE_BIG_CCR 1         // big gate/up tier: compiler-issued LDS reads from three separate arrays
                               // (0: inline-assembly read groups from one ring, as the down projection)
+#endif
+#ifndef ACE_LIGHT_RB
+#define ACE_LIGHT_RB 2        // big gate/up tier: tiles of at most 16*ACE_LIGHT_RB rows take the light
+                              // path (only their row blocks' MFMAs, a deeper weight ring); 0: off
+#endif
+#ifndef ACE_LIGHT_STAGES
+#define ACE_LIGHT_STAGES 3    // weight register ring depth of the light path (chunks)
 #endif
 #ifndef ACE_BIG_SLOTS
 #define ACE_BIG_SLOTS 256     // routed slots per expert (on average) from which the big tier is used
@@ -332,8 +343,27 @@ void expert_gemm_kernel(ExpertArgs a) {
   constexpr int XBYTES = DMA ? BM * ROWBC : BM * PITCH;
   constexpr bool CCR = DMA && ACE_BIG_CCR && KIND == 0;
   static_assert(!CCR || (XB == 3 && STAGES == 2), "compiler-issued reads: three buffers, two weight stages");
+  // Light path of the compiler-read tier: a tile with at most LBM slot rows
+  // (an expert with few kept slots, or the last m-tile of a larger one)
+  // multiplies only its LRB row blocks, so its time goes to the weight
+  // stream; the registers the other row blocks' accumulators would hold
+  // carry a deeper weight ring instead (LS chunks, LS - 1 in flight).
+  constexpr int LRB = ACE_LIGHT_RB > 0 ? ACE_LIGHT_RB : 1;
+  constexpr bool LIGHT = CCR && ACE_LIGHT_RB > 0 && LRB < RB;
+  constexpr int LBM = 16 * (LIGHT ? LRB : 1);
+  constexpr int LS = ACE_LIGHT_STAGES;
+  static_assert(!LIGHT || (LBM % (8 * NW) == 0 && LS >= 2 && LS <= 6), "light path: whole 1 KB row blocks per wave");
 
   __shared__ __attribute__((aligned(16))) uint8_t s_x[CCR ? 1 : NXB][CCR ? 16 : XBYTES];
+  // the three row buffers of the compiler-read staging (both paths of a tile)
+  __shared__ __attribute__((aligned(16))) uint8_t s_r0[CCR ? XBYTES : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_r1[CCR ? XBYTES : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_r2[CCR ? XBYTES : 16];
+  auto rbuf = [&](auto b) -> uint8_t* {
+    if constexpr (int(b) == 0) return s_r0;
+    else if constexpr (int(b) == 1) return s_r1;
+    else return s_r2;
+  };
   __shared__ int32_t s_pref[257];
   __shared__ int32_t s_off[257];
 
@@ -420,6 +450,95 @@ void expert_gemm_kernel(ExpertArgs a) {
         for (int g = 0; g < NGW; ++g)
           dst[g][s] = buf_ld16((KIND == 0 && g >= NGW / 2) ? wr1 : wr0, wv, ws[g] + (c * CK + s) * wstep);
     };
+    if constexpr (LIGHT) {
+      if (rows <= LBM) {
+        // Same staging and operand layout as the full tile below (rows of a
+        // chunk in the three LDS arrays by direct-to-LDS loads, each wave its
+        // own 1 KB blocks, operands read by the compiler one fragment ahead),
+        // over LBM rows.  Each step stages rows two chunks ahead and then
+        // loads weights LS - 1 chunks ahead; MFMA chains run in the same k
+        // order as the full tile's, so a row's outputs have the same bits.
+        constexpr int LDPW = LBM / 8 / NW;  // 1 KB row blocks per wave and chunk
+        constexpr int NWLL = NGW * CK;      // weight loads per wave and chunk
+        u32x4 ring[LS][NGW][CK];
+        static_for<LS - 1>([&](auto i) { load_w(ring[int(i)], min(int(i), nch - 1)); });
+        f32x4 lacc[LRB][NGW];
+#pragma unroll
+        for (int rb = 0; rb < LRB; ++rb)
+#pragma unroll
+          for (int g = 0; g < NGW; ++g) lacc[rb][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const __amdgpu_buffer_rsrc_t lxs = make_rsrc(a.A, uint32_t(int64_t(a.A_rows) * K * int(sizeof(T))));
+        int ldsrc[LDPW];
+#pragma unroll
+        for (int j = 0; j < LDPW; ++j) {
+          const int blk = j * NW + w;
+          const int r = 8 * blk + (l >> 3);
+          const int seg = (l & 7) ^ (l >> 3) ^ (blk & 1);
+          ldsrc[j] = a.sorted_token[row0 + min(r, rows - 1)] * K * int(sizeof(T)) + seg * 16;
+        }
+        const int lsw = (r16 & 7) ^ (r16 >> 3);
+        const int lrd[2] = {r16 * ROWBC + ((q ^ lsw) << 4), r16 * ROWBC + ((q ^ lsw ^ 4) << 4)};
+        stage_rows<LDPW, NW>(lxs, s_r0 + w * 1024, ldsrc, 0);
+        stage_rows<LDPW, NW>(lxs, s_r1 + w * 1024, ldsrc, min(1, nch - 1) * KC * int(sizeof(T)));
+        wait_vmcnt<LDPW>();
+        lds_barrier();
+        // step c: rows of chunk c + 2 into array (c + 2) % 3, weights of
+        // chunk c + LS - 1 into ring slot (c - 1) % LS (read by step c - 1),
+        // then the MFMAs of chunk c from array c % 3 and ring slot c % LS
+        auto lstep = [&](auto B, auto RI, int c) {
+          stage_rows<LDPW, NW>(lxs, rbuf(std::integral_constant<int, (int(B) + 2) % 3>{}) + w * 1024, ldsrc,
+                               min(c + 2, nch - 1) * KC * int(sizeof(T)));
+          load_w(ring[(int(RI) + LS - 1) % LS], min(c + LS - 1, nch - 1));
+          __builtin_amdgcn_sched_barrier(0);  // the loads go out before the MFMAs
+          const uint8_t* xb = rbuf(B);
+          constexpr int NF = CK * LRB;  // operand fragments of the chunk, k-step major
+          u32x4 af[2];
+          af[0] = lds_rd16(xb + lrd[0]);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          static_for<NF>([&](auto f) {
+            constexpr int s = int(f) / LRB, rb = int(f) % LRB;
+            if constexpr (int(f) + 1 < NF)
+              af[(int(f) + 1) & 1] = lds_rd16(xb + ((int(f) + 1) % LRB) * 16 * ROWBC + lrd[(int(f) + 1) / LRB]);
+#pragma unroll
+            for (int g = 0; g < NGW; ++g) lacc[rb][g] = mma_step<T>(af[int(f) & 1], ring[int(RI)][g][s], lacc[rb][g]);
+            if constexpr (int(f) + 1 < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NGW, 0);
+          });
+          // chunk c + 1's rows have landed once at most the loads issued
+          // after them are outstanding: step c's alone at c = 0 (chunk 1
+          // was staged by the prologue), else also step c - 1's weights
+          if (c == 0)
+            wait_vmcnt<NWLL + LDPW>();
+          else
+            wait_vmcnt<2 * NWLL + LDPW>();
+          lds_barrier();
+        };
+        constexpr int LU = LS % 3 == 0 ? LS : 3 * LS;  // steps until array and ring slot repeat
+        for (int c = 0; c < nch; c += LU)
+          static_for<LU>([&](auto u) {
+            if (c + int(u) < nch)
+              lstep(std::integral_constant<int, int(u) % 3>{}, std::integral_constant<int, int(u) % LS>{}, c + int(u));
+          });
+#pragma unroll
+        for (int rb = 0; rb < LRB; ++rb) {
+          if (rb < nrb) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int r = rb * 16 + 4 * q + j;
+              if (r < rows) {
+                const int64_t p = row0 + r;
+#pragma unroll
+                for (int g = 0; g < NGW / 2; ++g) {
+                  const float v = silu(lacc[rb][g][j]) * lacc[rb][g + NGW / 2][j];
+                  reinterpret_cast<T*>(a.out)[p * N + col0 + 16 * g + r16] = St<T>::from_f32(v);
+                }
+              }
+            }
+          }
+        }
+        continue;
+      }
+    }
     load_w(wA, 0);
     if (STAGES == 3) load_w(wB, min(1, nch - 1));
 
@@ -473,14 +592,7 @@ void expert_gemm_kernel(ExpertArgs a) {
         // before that step, so rows are staged one chunk ahead (chunk c + 2
         // is loaded during step c and waited for at the start of step c + 2,
         // with chunk c + 1's rows landing meanwhile).
-        __shared__ __attribute__((aligned(16))) uint8_t s_r0[XBYTES];
-        __shared__ __attribute__((aligned(16))) uint8_t s_r1[XBYTES];
-        __shared__ __attribute__((aligned(16))) uint8_t s_r2[XBYTES];
-        auto buf = [&](auto b) -> uint8_t* {
-          if constexpr (int(b) == 0) return s_r0;
-          else if constexpr (int(b) == 1) return s_r1;
-          else return s_r2;
-        };
+        auto buf = [&](auto b) -> uint8_t* { return rbuf(b); };
         // step c: weights of chunk c + 1, rows of chunk c + 2 into array
         // (B + 2) % 3, the MFMAs of chunk c from array B = c % 3
         auto step = [&](auto B, u32x4 (&cur)[NGW][CK], u32x4 (&ahead)[NGW][CK], int c) {
