@@ -18,7 +18,7 @@
 //     through LDS and shared by all waves of the tile: through registers
 //     into two LDS buffers, or (128-row tiles) by direct-to-LDS buffer loads
 //     into a ring of three buffers, two chunks ahead of the MFMAs.
-// In the 128-row gate/up tier a tile of at most 32 slot rows (an expert with
+// In the 128-row tier a tile of at most 32 slot rows (an expert with
 // few kept slots, or the ragged last m-tile of a larger one) multiplies only
 // its own row blocks and spends the freed accumulator registers on a deeper
 // weight ring; its outputs have the same bits as in a full tile.
@@ -72,11 +72,18 @@ namespace {
                               // (0: inline-assembly read groups from one ring, as the down projection)
 #endif
 #ifndef ACE_LIGHT_RB
-#define ACE_LIGHT_RB 2        // big gate/up tier: tiles of at most 16*ACE_LIGHT_RB rows take the light
+#define ACE_LIGHT_RB 2        // 128-row tier: tiles of at most 16*ACE_LIGHT_RB rows take the light
                               // path (only their row blocks' MFMAs, a deeper weight ring); 0: off
 #endif
 #ifndef ACE_LIGHT_STAGES
 #define ACE_LIGHT_STAGES 3    // weight register ring depth of the light path (chunks)
+#endif
+#ifndef ACE_LIGHT_STAGES_DOWN
+#define ACE_LIGHT_STAGES_DOWN 3  // the same for the down projection's light path (0: off)
+#endif
+#ifndef ACE_LIGHT_DOWN_SLOTS
+#define ACE_LIGHT_DOWN_SLOTS 1024  // routed slots per expert (on average) below which the 128-row down
+                                   // projection is launched with its light path
 #endif
 #ifndef ACE_BIG_SLOTS
 #define ACE_BIG_SLOTS 256     // routed slots per expert (on average) from which the big tier is used
@@ -316,7 +323,8 @@ __device__ __forceinline__ void lds_read_group(uint32_t addr, u32x4 (&v)[NR]) {
 // WPE: occupancy target (waves per SIMD) given to the register allocator; 0
 // picks it from the tile height.  XB > 0: the slot rows are staged with
 // direct-to-LDS loads into XB buffers instead of through registers.
-template <typename T, int RB, int NW, int KIND, int STAGES, int NGW = 2, int CK = 4, int WPE = 0, int XB = 0>
+template <typename T, int RB, int NW, int KIND, int STAGES, int NGW = 2, int CK = 4, int WPE = 0, int XB = 0,
+          bool LT = true>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : (RB <= 3 ? 4 : (RB >= 16 ? 1 : (RB >= 8 ? 2 : ACE_WAVES_PER_EU))))))
 void expert_gemm_kernel(ExpertArgs a) {
@@ -343,15 +351,15 @@ void expert_gemm_kernel(ExpertArgs a) {
   constexpr int XBYTES = DMA ? BM * ROWBC : BM * PITCH;
   constexpr bool CCR = DMA && ACE_BIG_CCR && KIND == 0;
   static_assert(!CCR || (XB == 3 && STAGES == 2), "compiler-issued reads: three buffers, two weight stages");
-  // Light path of the compiler-read tier: a tile with at most LBM slot rows
+  // Light path of the direct-to-LDS tier: a tile with at most LBM slot rows
   // (an expert with few kept slots, or the last m-tile of a larger one)
   // multiplies only its LRB row blocks, so its time goes to the weight
   // stream; the registers the other row blocks' accumulators would hold
   // carry a deeper weight ring instead (LS chunks, LS - 1 in flight).
   constexpr int LRB = ACE_LIGHT_RB > 0 ? ACE_LIGHT_RB : 1;
-  constexpr bool LIGHT = CCR && ACE_LIGHT_RB > 0 && LRB < RB;
+  constexpr int LS = KIND == 0 ? ACE_LIGHT_STAGES : ACE_LIGHT_STAGES_DOWN;
+  constexpr bool LIGHT = LT && DMA && XB == 3 && (CCR || KIND == 1) && ACE_LIGHT_RB > 0 && LRB < RB && LS >= 2;
   constexpr int LBM = 16 * (LIGHT ? LRB : 1);
-  constexpr int LS = ACE_LIGHT_STAGES;
   static_assert(!LIGHT || (LBM % (8 * NW) == 0 && LS >= 2 && LS <= 6), "light path: whole 1 KB row blocks per wave");
 
   __shared__ __attribute__((aligned(16))) uint8_t s_x[CCR ? 1 : NXB][CCR ? 16 : XBYTES];
@@ -474,36 +482,58 @@ void expert_gemm_kernel(ExpertArgs a) {
           const int blk = j * NW + w;
           const int r = 8 * blk + (l >> 3);
           const int seg = (l & 7) ^ (l >> 3) ^ (blk & 1);
-          ldsrc[j] = a.sorted_token[row0 + min(r, rows - 1)] * K * int(sizeof(T)) + seg * 16;
+          const int rr = min(r, rows - 1);
+          ldsrc[j] = ((KIND == 0) ? a.sorted_token[row0 + rr] : row0 + rr) * K * int(sizeof(T)) + seg * 16;
         }
         const int lsw = (r16 & 7) ^ (r16 >> 3);
         const int lrd[2] = {r16 * ROWBC + ((q ^ lsw) << 4), r16 * ROWBC + ((q ^ lsw ^ 4) << 4)};
-        stage_rows<LDPW, NW>(lxs, s_r0 + w * 1024, ldsrc, 0);
-        stage_rows<LDPW, NW>(lxs, s_r1 + w * 1024, ldsrc, min(1, nch - 1) * KC * int(sizeof(T)));
+        // the three row buffers: gate/up, the separate arrays read by the
+        // compiler; down, the one-array ring read by inline-assembly groups
+        auto lbuf = [&](auto b) -> uint8_t* {
+          if constexpr (KIND == 0) return rbuf(b);
+          else return s_x[int(b)];
+        };
+        const uint32_t lds_ring = uint32_t(uintptr_t((__attribute__((address_space(3))) uint8_t*)(&s_x[0][0])));
+        stage_rows<LDPW, NW>(lxs, lbuf(std::integral_constant<int, 0>{}) + w * 1024, ldsrc, 0);
+        stage_rows<LDPW, NW>(lxs, lbuf(std::integral_constant<int, 1>{}) + w * 1024, ldsrc,
+                             min(1, nch - 1) * KC * int(sizeof(T)));
         wait_vmcnt<LDPW>();
         lds_barrier();
         // step c: rows of chunk c + 2 into array (c + 2) % 3, weights of
         // chunk c + LS - 1 into ring slot (c - 1) % LS (read by step c - 1),
         // then the MFMAs of chunk c from array c % 3 and ring slot c % LS
         auto lstep = [&](auto B, auto RI, int c) {
-          stage_rows<LDPW, NW>(lxs, rbuf(std::integral_constant<int, (int(B) + 2) % 3>{}) + w * 1024, ldsrc,
+          stage_rows<LDPW, NW>(lxs, lbuf(std::integral_constant<int, (int(B) + 2) % 3>{}) + w * 1024, ldsrc,
                                min(c + 2, nch - 1) * KC * int(sizeof(T)));
           load_w(ring[(int(RI) + LS - 1) % LS], min(c + LS - 1, nch - 1));
           __builtin_amdgcn_sched_barrier(0);  // the loads go out before the MFMAs
-          const uint8_t* xb = rbuf(B);
-          constexpr int NF = CK * LRB;  // operand fragments of the chunk, k-step major
-          u32x4 af[2];
-          af[0] = lds_rd16(xb + lrd[0]);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          static_for<NF>([&](auto f) {
-            constexpr int s = int(f) / LRB, rb = int(f) % LRB;
-            if constexpr (int(f) + 1 < NF)
-              af[(int(f) + 1) & 1] = lds_rd16(xb + ((int(f) + 1) % LRB) * 16 * ROWBC + lrd[(int(f) + 1) / LRB]);
+          if constexpr (KIND == 0) {
+            const uint8_t* xb = lbuf(B);
+            constexpr int NF = CK * LRB;  // operand fragments of the chunk, k-step major
+            u32x4 af[2];
+            af[0] = lds_rd16(xb + lrd[0]);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            static_for<NF>([&](auto f) {
+              constexpr int s = int(f) / LRB, rb = int(f) % LRB;
+              if constexpr (int(f) + 1 < NF)
+                af[(int(f) + 1) & 1] = lds_rd16(xb + ((int(f) + 1) % LRB) * 16 * ROWBC + lrd[(int(f) + 1) / LRB]);
 #pragma unroll
-            for (int g = 0; g < NGW; ++g) lacc[rb][g] = mma_step<T>(af[int(f) & 1], ring[int(RI)][g][s], lacc[rb][g]);
-            if constexpr (int(f) + 1 < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, NGW, 0);
-          });
+              for (int g = 0; g < NGW; ++g)
+                lacc[rb][g] = mma_step<T>(af[int(f) & 1], ring[int(RI)][g][s], lacc[rb][g]);
+              if constexpr (int(f) + 1 < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x008, NGW, 0);
+            });
+          } else {
+            const uint32_t xb = lds_ring + uint32_t(int(B)) * XBYTES;
+            static_for<CK>([&](auto s) {
+              u32x4 af[LRB];
+              lds_read_group<LRB, 0, 16 * ROWBC>(xb + uint32_t(lrd[int(s)]), af);
+#pragma unroll
+              for (int f = 0; f < LRB; ++f)
+#pragma unroll
+                for (int g = 0; g < NGW; ++g) lacc[f][g] = mma_step<T>(af[f], ring[int(RI)][g][int(s)], lacc[f][g]);
+            });
+          }
           // chunk c + 1's rows have landed once at most the loads issued
           // after them are outstanding: step c's alone at c = 0 (chunk 1
           // was staged by the prologue), else also step c - 1's weights
@@ -527,10 +557,17 @@ void expert_gemm_kernel(ExpertArgs a) {
               const int r = rb * 16 + 4 * q + j;
               if (r < rows) {
                 const int64_t p = row0 + r;
+                if constexpr (KIND == 0) {
 #pragma unroll
-                for (int g = 0; g < NGW / 2; ++g) {
-                  const float v = silu(lacc[rb][g][j]) * lacc[rb][g + NGW / 2][j];
-                  reinterpret_cast<T*>(a.out)[p * N + col0 + 16 * g + r16] = St<T>::from_f32(v);
+                  for (int g = 0; g < NGW / 2; ++g) {
+                    const float v = silu(lacc[rb][g][j]) * lacc[rb][g + NGW / 2][j];
+                    reinterpret_cast<T*>(a.out)[p * N + col0 + 16 * g + r16] = St<T>::from_f32(v);
+                  }
+                } else {
+                  const float gt = a.sorted_gate[p];
+                  T* o = reinterpret_cast<T*>(a.out) + p * N + col0 + r16;
+#pragma unroll
+                  for (int g = 0; g < NGW; ++g) o[16 * g] = St<T>::from_f32(gt * lacc[rb][g][j]);
                 }
               }
             }
@@ -1193,7 +1230,8 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const T* __restrict__
   st16(dst + u * EPL, ld16(src + row * K + k));
 }
 
-template <typename T, int RB, int NW, int KIND, int STAGES, int NGW = 2, int CK = 4, int WPE = 0, int XB = 0>
+template <typename T, int RB, int NW, int KIND, int STAGES, int NGW = 2, int CK = 4, int WPE = 0, int XB = 0,
+          bool LT = true>
 hipError_t launch_one(const ExpertArgs& a, int ntok, int k, hipStream_t s) {
   constexpr int BM = 16 * RB;
   constexpr int ROWS_PER_WG = (KIND == 0) ? NW * 8 * NGW : NW * 16 * NGW;
@@ -1205,7 +1243,7 @@ hipError_t launch_one(const ExpertArgs& a, int ntok, int k, hipStream_t s) {
   constexpr bool COLS = columns_dealt<RB, KIND>();
   const int64_t per_xcd_bound = COLS ? (nbc + NXCD - 1) / NXCD * mt_bound : (mt_bound * nbc + NXCD - 1) / NXCD;
   const int64_t grid = std::max<int64_t>(NXCD, std::min<int64_t>(per_xcd_bound * NXCD, int64_t(1) << 30));
-  hipLaunchKernelGGL((expert_gemm_kernel<T, RB, NW, KIND, STAGES, NGW, CK, WPE, XB>), dim3(unsigned(grid)),
+  hipLaunchKernelGGL((expert_gemm_kernel<T, RB, NW, KIND, STAGES, NGW, CK, WPE, XB, LT>), dim3(unsigned(grid)),
                      dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
@@ -1262,12 +1300,18 @@ hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs
     if (stream_path)
       return kind == 0 ? launch_splitk<bf16_t, 0>(a, T, k, num_cu, s) : launch_splitk<bf16_t, 1>(a, T, k, num_cu, s);
     constexpr int NG = ACE_GATEUP_NW, ND = ACE_DOWN_NW;
-    if (big_rb)
-      return kind == 0
-                 ? launch_one<bf16_t, ACE_BIG_RB, ACE_BIG_NW, 0, ACE_BIG_STAGES, ACE_BIG_NGW, ACE_BIG_CK, ACE_BIG_WPE,
-                              ACE_BIG_XB>(a, T, k, s)
-                 : launch_one<bf16_t, ACE_BIG_RB, ACE_BIG_NW, 1, ACE_BIG_STAGES, ACE_BIG_NGW, ACE_BIG_CK, ACE_BIG_WPE,
-                              ACE_BIG_XB>(a, T, k, s);
+    if (big_rb) {
+      if (kind == 0)
+        return launch_one<bf16_t, ACE_BIG_RB, ACE_BIG_NW, 0, ACE_BIG_STAGES, ACE_BIG_NGW, ACE_BIG_CK, ACE_BIG_WPE,
+                          ACE_BIG_XB>(a, T, k, s);
+      // the down projection's light path costs its full tiles a few spilled
+      // registers: taken only where light tiles are expected to be common
+      if (int64_t(T) * k < int64_t(ACE_LIGHT_DOWN_SLOTS) * a.E)
+        return launch_one<bf16_t, ACE_BIG_RB, ACE_BIG_NW, 1, ACE_BIG_STAGES, ACE_BIG_NGW, ACE_BIG_CK, ACE_BIG_WPE,
+                          ACE_BIG_XB, true>(a, T, k, s);
+      return launch_one<bf16_t, ACE_BIG_RB, ACE_BIG_NW, 1, ACE_BIG_STAGES, ACE_BIG_NGW, ACE_BIG_CK, ACE_BIG_WPE,
+                        ACE_BIG_XB, false>(a, T, k, s);
+    }
     constexpr int SG = ACE_SMALL_NGW_GATEUP, SGC = ACE_SMALL_CK_GATEUP;
     constexpr int SD = ACE_SMALL_NGW_DOWN, SDC = ACE_SMALL_CK_DOWN;
     if (small_rb && a.N % ((kind == 0 ? 8 * NG * SG : 16 * ND * SD)) == 0)
