@@ -224,6 +224,39 @@ def test_big_tier_light_and_full_tiles(dev, packed):
     check_slot_outputs(L, g, ref, "bf16")
 
 
+@pytest.mark.parametrize("packed", [False, True])
+def test_light_path_same_bits_as_full_tiles(dev, packed):
+    """A token's act and slot rows for an expert do not depend on whether the
+    expert's tile took the light path (at most 32 rows) or a full 128-row
+    tile: the same MFMA chains in the same k order.  Crafted logits route
+    tokens 0..19 to experts (0, 1) in both runs; expert 0 holds those 20 rows
+    in run A and 200 rows in run B (a full first m-tile)."""
+    E, k, T = 4, 2, 520  # T*k >= 256*E: the 128-row tier
+    L, _, _ = _bf16_case(T=T, H=256, E=E, I=256, k=k, rate=0.0, cfg_id=112)
+    rng = np.random.default_rng(3)
+
+    def logits(n0):
+        lg = rng.normal(0.0, 0.1, (T, E)).astype(np.float32)
+        lg[:, 0] = -10.0                 # expert 0 only where forced below
+        lg[:n0, 0] = 5.0
+        lg[:n0, 1] = 4.0
+        return lg
+
+    base = logits(200)
+    la, lb = base.copy(), base.copy()
+    la[20:200] = logits(0)[20:200]       # run A: only tokens 0..19 reach expert 0
+    gl = GpuLayer(L, dev, packed=packed)
+    a = gl.run(0.0, 0.0, logits_in=la)
+    b = gl.run(0.0, 0.0, logits_in=lb)
+    assert np.diff(a["offsets"])[0] == 20 and np.diff(b["offsets"])[0] == 200
+    for t in range(20):
+        i = int(np.flatnonzero(a["topk_idx"][t] == 0)[0])
+        assert b["topk_idx"][t, i] == 0
+        pa, pb = a["slot_pos"][t, i], b["slot_pos"][t, i]
+        for n in ("act", "slot_out"):
+            assert np.array_equal(a[n][pa].view(np.uint16), b[n][pb].view(np.uint16)), (n, t)
+
+
 # ---------------------------------------------------------------- seeded random shapes
 def _random_case(i):
     rng = np.random.default_rng(9000 + i)
