@@ -322,7 +322,8 @@ __device__ __forceinline__ void lds_read_group(uint32_t addr, u32x4 (&v)[NR]) {
 
 // WPE: occupancy target (waves per SIMD) given to the register allocator; 0
 // picks it from the tile height.  XB > 0: the slot rows are staged with
-// direct-to-LDS loads into XB buffers instead of through registers.
+// direct-to-LDS loads into XB buffers instead of through registers.  LT:
+// the light path for tiles of few rows is compiled in (direct-to-LDS tiers).
 template <typename T, int RB, int NW, int KIND, int STAGES, int NGW = 2, int CK = 4, int WPE = 0, int XB = 0,
           bool LT = true>
 __global__ __launch_bounds__(NW * 64)
@@ -460,12 +461,14 @@ void expert_gemm_kernel(ExpertArgs a) {
     };
     if constexpr (LIGHT) {
       if (rows <= LBM) {
-        // Same staging and operand layout as the full tile below (rows of a
-        // chunk in the three LDS arrays by direct-to-LDS loads, each wave its
-        // own 1 KB blocks, operands read by the compiler one fragment ahead),
-        // over LBM rows.  Each step stages rows two chunks ahead and then
-        // loads weights LS - 1 chunks ahead; MFMA chains run in the same k
-        // order as the full tile's, so a row's outputs have the same bits.
+        // Same staging and operand layout as the full tile below, over LBM
+        // rows: a chunk's rows go into three LDS buffers by direct-to-LDS
+        // loads, each wave its own 1 KB blocks; gate/up reads the operands
+        // from its three arrays by compiler-issued loads one fragment ahead,
+        // down from its one-array ring by inline-assembly groups.  Each step
+        // stages rows two chunks ahead and then loads weights LS - 1 chunks
+        // ahead; MFMA chains run in the same k order as the full tile's, so a
+        // row's outputs have the same bits.
         constexpr int LDPW = LBM / 8 / NW;  // 1 KB row blocks per wave and chunk
         constexpr int NWLL = NGW * CK;      // weight loads per wave and chunk
         u32x4 ring[LS][NGW][CK];
