@@ -81,10 +81,6 @@ namespace {
 #ifndef ACE_LIGHT_STAGES_DOWN
 #define ACE_LIGHT_STAGES_DOWN 3  // the same for the down projection's light path (0: off)
 #endif
-#ifndef ACE_LIGHT_DOWN_SLOTS
-#define ACE_LIGHT_DOWN_SLOTS 1024  // routed slots per expert (on average) below which the 128-row down
-                                   // projection is launched with its light path
-#endif
 #ifndef ACE_BIG_SLOTS
 #define ACE_BIG_SLOTS 256     // routed slots per expert (on average) from which the big tier is used
 #endif
@@ -322,10 +318,8 @@ __device__ __forceinline__ void lds_read_group(uint32_t addr, u32x4 (&v)[NR]) {
 
 // WPE: occupancy target (waves per SIMD) given to the register allocator; 0
 // picks it from the tile height.  XB > 0: the slot rows are staged with
-// direct-to-LDS loads into XB buffers instead of through registers.  LT:
-// the light path for tiles of few rows is compiled in (direct-to-LDS tiers).
-template <typename T, int RB, int NW, int KIND, int STAGES, int NGW = 2, int CK = 4, int WPE = 0, int XB = 0,
-          bool LT = true>
+// direct-to-LDS loads into XB buffers instead of through registers.
+template <typename T, int RB, int NW, int KIND, int STAGES, int NGW = 2, int CK = 4, int WPE = 0, int XB = 0>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : (RB <= 3 ? 4 : (RB >= 16 ? 1 : (RB >= 8 ? 2 : ACE_WAVES_PER_EU))))))
 void expert_gemm_kernel(ExpertArgs a) {
@@ -359,7 +353,7 @@ void expert_gemm_kernel(ExpertArgs a) {
   // carry a deeper weight ring instead (LS chunks, LS - 1 in flight).
   constexpr int LRB = ACE_LIGHT_RB > 0 ? ACE_LIGHT_RB : 1;
   constexpr int LS = KIND == 0 ? ACE_LIGHT_STAGES : ACE_LIGHT_STAGES_DOWN;
-  constexpr bool LIGHT = LT && DMA && XB == 3 && (CCR || KIND == 1) && ACE_LIGHT_RB > 0 && LRB < RB && LS >= 2;
+  constexpr bool LIGHT = DMA && XB == 3 && (CCR || KIND == 1) && ACE_LIGHT_RB > 0 && LRB < RB && LS >= 2;
   constexpr int LBM = 16 * (LIGHT ? LRB : 1);
   static_assert(!LIGHT || (LBM % (8 * NW) == 0 && LS >= 2 && LS <= 6), "light path: whole 1 KB row blocks per wave");
 
@@ -552,12 +546,16 @@ void expert_gemm_kernel(ExpertArgs a) {
             if (c + int(u) < nch)
               lstep(std::integral_constant<int, int(u) % 3>{}, std::integral_constant<int, int(u) % LS>{}, c + int(u));
           });
+        // the row offsets are formed here, not hoisted out of the tile loop
+        // (where they would take registers for its whole length)
+        int q4 = 4 * q;
+        asm volatile("" : "+v"(q4));
 #pragma unroll
         for (int rb = 0; rb < LRB; ++rb) {
           if (rb < nrb) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const int r = rb * 16 + 4 * q + j;
+              const int r = rb * 16 + q4 + j;
               if (r < rows) {
                 const int64_t p = row0 + r;
                 if constexpr (KIND == 0) {
@@ -794,13 +792,15 @@ void expert_gemm_kernel(ExpertArgs a) {
       }
     }
 
-    // epilogue
+    // epilogue (row offsets formed here, not hoisted out of the tile loop)
+    int q4 = 4 * q;
+    asm volatile("" : "+v"(q4));
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       if (rb < nrb) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int r = rb * 16 + 4 * q + j;
+          const int r = rb * 16 + q4 + j;
           if (r < rows) {
             const int64_t p = row0 + r;
             if (KIND == 0) {
@@ -1233,8 +1233,7 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const T* __restrict__
   st16(dst + u * EPL, ld16(src + row * K + k));
 }
 
-template <typename T, int RB, int NW, int KIND, int STAGES, int NGW = 2, int CK = 4, int WPE = 0, int XB = 0,
-          bool LT = true>
+template <typename T, int RB, int NW, int KIND, int STAGES, int NGW = 2, int CK = 4, int WPE = 0, int XB = 0>
 hipError_t launch_one(const ExpertArgs& a, int ntok, int k, hipStream_t s) {
   constexpr int BM = 16 * RB;
   constexpr int ROWS_PER_WG = (KIND == 0) ? NW * 8 * NGW : NW * 16 * NGW;
@@ -1246,7 +1245,7 @@ hipError_t launch_one(const ExpertArgs& a, int ntok, int k, hipStream_t s) {
   constexpr bool COLS = columns_dealt<RB, KIND>();
   const int64_t per_xcd_bound = COLS ? (nbc + NXCD - 1) / NXCD * mt_bound : (mt_bound * nbc + NXCD - 1) / NXCD;
   const int64_t grid = std::max<int64_t>(NXCD, std::min<int64_t>(per_xcd_bound * NXCD, int64_t(1) << 30));
-  hipLaunchKernelGGL((expert_gemm_kernel<T, RB, NW, KIND, STAGES, NGW, CK, WPE, XB, LT>), dim3(unsigned(grid)),
+  hipLaunchKernelGGL((expert_gemm_kernel<T, RB, NW, KIND, STAGES, NGW, CK, WPE, XB>), dim3(unsigned(grid)),
                      dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
@@ -1303,18 +1302,12 @@ hipError_t launch_expert(int dtype, int kind, bool stream_path, const ExpertArgs
     if (stream_path)
       return kind == 0 ? launch_splitk<bf16_t, 0>(a, T, k, num_cu, s) : launch_splitk<bf16_t, 1>(a, T, k, num_cu, s);
     constexpr int NG = ACE_GATEUP_NW, ND = ACE_DOWN_NW;
-    if (big_rb) {
-      if (kind == 0)
-        return launch_one<bf16_t, ACE_BIG_RB, ACE_BIG_NW, 0, ACE_BIG_STAGES, ACE_BIG_NGW, ACE_BIG_CK, ACE_BIG_WPE,
-                          ACE_BIG_XB>(a, T, k, s);
-      // the down projection's light path costs its full tiles a few spilled
-      // registers: taken only where light tiles are expected to be common
-      if (int64_t(T) * k < int64_t(ACE_LIGHT_DOWN_SLOTS) * a.E)
-        return launch_one<bf16_t, ACE_BIG_RB, ACE_BIG_NW, 1, ACE_BIG_STAGES, ACE_BIG_NGW, ACE_BIG_CK, ACE_BIG_WPE,
-                          ACE_BIG_XB, true>(a, T, k, s);
-      return launch_one<bf16_t, ACE_BIG_RB, ACE_BIG_NW, 1, ACE_BIG_STAGES, ACE_BIG_NGW, ACE_BIG_CK, ACE_BIG_WPE,
-                        ACE_BIG_XB, false>(a, T, k, s);
-    }
+    if (big_rb)
+      return kind == 0
+                 ? launch_one<bf16_t, ACE_BIG_RB, ACE_BIG_NW, 0, ACE_BIG_STAGES, ACE_BIG_NGW, ACE_BIG_CK, ACE_BIG_WPE,
+                              ACE_BIG_XB>(a, T, k, s)
+                 : launch_one<bf16_t, ACE_BIG_RB, ACE_BIG_NW, 1, ACE_BIG_STAGES, ACE_BIG_NGW, ACE_BIG_CK, ACE_BIG_WPE,
+                              ACE_BIG_XB>(a, T, k, s);
     constexpr int SG = ACE_SMALL_NGW_GATEUP, SGC = ACE_SMALL_CK_GATEUP;
     constexpr int SD = ACE_SMALL_NGW_DOWN, SDC = ACE_SMALL_CK_DOWN;
     if (small_rb && a.N % ((kind == 0 ? 8 * NG * SG : 16 * ND * SD)) == 0)
